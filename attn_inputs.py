@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs for the exact attention forward.
+
+This module is shared by both sides of every parity check (the fp64 CPU oracle
+and the HIP path). It only draws Q, K, V and picks which query rows a check
+samples; it contains none of the attention arithmetic.
+
+Recipe (one workload = B, H, N, d, causal, dtype, seed):
+  g = torch.Generator('cpu').manual_seed(seed)
+  q, k, v = torch.randn((B, H, N, d), generator=g, dtype=float32), in that order
+  k *= k_scale        (3.0 for the peaked-softmax workload, in fp32, before rounding)
+  round to bf16 with round-to-nearest-even (fp32 workloads stay fp32)
+Layout is [B, H, N, d], contiguous, row-major. The default softmax scale is
+1/sqrt(d) rounded to fp32: the standard attention code on the unite.ai page
+("Flash Attention: revolutionizing transformer efficiency", opening code block)
+divides the scores by the square root of the head width.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str          # "bf16" or "f32"
+    seed: int
+    k_scale: float = 1.0
+    sampled_rows: int = 0   # 0: every row is checked; else rows sampled per check
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    @property
+    def flops(self) -> float:
+        """Attention-forward FLOPs as the metric counts them: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def elt_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once; O written once (input dtype); lse written once (fp32)."""
+        n = self.B * self.H * self.N
+        return 4 * n * self.d * self.elt_bytes + 4 * n
+
+
+# The workloads: seed = workload number; C2 has a causal and a non-causal variant.
+WORKLOADS = {
+    "c1_f32_b1h1n128d64": Workload("c1_f32_b1h1n128d64", 1, 1, 128, 64, False, "f32", 1),
+    "c2n_bf16_b4h8n1024d64": Workload("c2n_bf16_b4h8n1024d64", 4, 8, 1024, 64, False, "bf16", 2),
+    "c2c_bf16_b4h8n1024d64_causal": Workload("c2c_bf16_b4h8n1024d64_causal", 4, 8, 1024, 64, True, "bf16", 2),
+    "c3_bf16_b2h16n4096d128": Workload("c3_bf16_b2h16n4096d128", 2, 16, 4096, 128, False, "bf16", 3),
+    "c4_bf16_b1h32n16384d128_causal": Workload("c4_bf16_b1h32n16384d128_causal", 1, 32, 16384, 128, True, "bf16", 4,
+                                               sampled_rows=256),
+    "c5_bf16_b1h8n32768d64_causal_k3": Workload("c5_bf16_b1h8n32768d64_causal_k3", 1, 8, 32768, 64, True, "bf16", 5,
+                                                k_scale=3.0, sampled_rows=256),
+}
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to fp32 (the value handed to both sides)."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def make_qkv(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16", k_scale: float = 1.0):
+    """Draw q, k, v ~ N(0, 1) in fp32 (CPU generator), scale k, round to dtype. Returns CPU tensors."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if k_scale != 1.0:
+        k = k * float(k_scale)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    return q.to(tdt).contiguous(), k.to(tdt).contiguous(), v.to(tdt).contiguous()
+
+
+def make_workload(w: Workload):
+    return make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype, w.k_scale)
+
+
+def sample_rows(B: int, H: int, N: int, n: int, seed: int) -> np.ndarray:
+    """n distinct flat row ids (b*H + h)*N + i, uniform without replacement, seeded with seed+1000."""
+    total = B * H * N
+    n = min(n, total)
+    g = torch.Generator("cpu").manual_seed(int(seed) + 1000)
+    return torch.randperm(total, generator=g)[:n].numpy().astype(np.int64)
+
+
+def edge_rows(N: int, Br: int = 128, Bc: int = 64) -> np.ndarray:
+    """Fixed rows of head 0 at tile edges: first, last, and around one Q block and one KV tile."""
+    cand = [0, 1, Br - 1, Br, N // 2, N - Bc, N - 2, N - 1]
+    return np.array(sorted({i for i in cand if 0 <= i < N}), dtype=np.int64)
+
+
+def check_rows(w: Workload) -> np.ndarray | None:
+    """Rows a parity check compares: None (all rows) or the sampled set plus the edge rows."""
+    if not w.sampled_rows:
+        return None
+    r = np.concatenate([sample_rows(w.B, w.H, w.N, w.sampled_rows, w.seed), edge_rows(w.N)])
+    return np.unique(r)
+
+
+def sha256(*tensors: torch.Tensor) -> str:
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()

@@ -1,0 +1,90 @@
+/*
+ * fa.h -- C ABI of the exact fused attention forward for AMD gfx950 (MI355X).
+ *
+ * Operation. For every batch b, head h and query row i:
+ *     s_ij   = scale * q_i . k_j                  (j visible: all j, or j <= i when causal)
+ *     o_i    = sum_j softmax_j(s_i.) * v_j
+ *     lse_i  = ln sum_j exp(s_ij)                 (natural log, over the visible j)
+ * This is the standard attention of the unite.ai page "Flash Attention:
+ * revolutionizing transformer efficiency" (opening code block; "The Math Behind
+ * Flash Attention", item 1, max-subtracted softmax). It is computed the way the
+ * same page's "Flash Attention Algorithm" and "Implementation Details" describe
+ * it -- tile by tile, with a running row maximum m and running row sum l, so the
+ * N x N score matrix never reaches device memory -- using the three
+ * FlashAttention-2 changes listed on the systems-analysis.info page
+ * "FlashAttention-2 (VI)", section "Kiến trúc kỹ thuật và nguyên lý hoạt động":
+ * fewer non-matmul FLOPs (1/l applied once at the end), parallelism over blocks
+ * of query rows as well as over batch x heads, and per-wave ownership of query
+ * rows inside a workgroup. lse is the log form of the running statistics M and
+ * L of the unite.ai page's blockwise code. Causal visibility (key j <= query i)
+ * is a reading of "causal" in the triton-transformer README's usage example.
+ *
+ * Layout. q, k, v, o are [B, H, N, d] contiguous row-major (element (b,h,i,c)
+ * at ((b*H + h)*N + i)*d + c). lse is [B, H, N] contiguous fp32.
+ *
+ * Ownership. The caller allocates every buffer in device memory and keeps it
+ * alive until the stream has run the work. The library allocates nothing, keeps
+ * no state between calls, and never synchronises: it validates the arguments on
+ * the host, enqueues exactly one kernel on `stream` (0 = null stream) and
+ * returns. Results are valid once the caller synchronises the stream. q, k and v
+ * are only read; o and lse are only written. Calls are thread-safe, and the
+ * same inputs give bitwise-identical outputs on every call (no atomics, no
+ * split over keys).
+ *
+ * Errors. 0 on success; otherwise one of the FA_ERR_* codes below, and nothing
+ * is enqueued. Every check except FA_ERR_HIP runs before any HIP call. Faults
+ * inside the kernel surface at the caller's next synchronisation.
+ * B, H or N equal to 0 is an empty problem: the call returns 0, enqueues
+ * nothing and does not look at the pointers.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_ERR_NULL 1    /* a pointer is NULL (non-empty problem) */
+#define FA_ERR_SHAPE 2   /* B, H or N negative; B*H over 65535; N over 2^30 */
+#define FA_ERR_HEADDIM 3 /* d is not 64 or 128 */
+#define FA_ERR_ALIGN 4   /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+#define FA_ERR_ARG 5     /* scale not finite or not > 0, or causal not 0/1 */
+#define FA_ERR_ALIAS 6   /* o or lse overlaps q, k or v, or o overlaps lse */
+#define FA_ERR_HIP 7     /* the HIP runtime reported an error at launch */
+
+/*
+ * fa_fwd -- bf16 inputs and output, fp32 accumulation and fp32 lse.
+ *   q, k, v : const bf16 [B,H,N,d] (device)       o : bf16 [B,H,N,d] (device, written)
+ *   lse     : float [B,H,N] (device, written), natural-log log-sum-exp of the scaled scores
+ *   B, H, N : batch, heads, sequence length (queries and keys have the same length N)
+ *   d       : head dimension, 64 or 128
+ *   causal  : 1 -> key j visible to query i iff j <= i; 0 -> every key visible
+ *   scale   : softmax scale applied to q.k (e.g. 1/sqrt(d)); finite and > 0
+ *   stream  : HIP stream the kernel is enqueued on
+ * The probabilities are rounded to bf16 (round-to-nearest-even) before the
+ * product with V; o is rounded to bf16 once, after the division by l.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
+           float scale, hipStream_t stream);
+
+/*
+ * fa_fwd_f32 -- the same operation with fp32 q, k, v and o. Products and sums
+ * stay in fp32 throughout (fp32 matrix-core instructions, no bf16 step).
+ * Arguments, layout, ownership and errors as fa_fwd.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
+               int causal, float scale, hipStream_t stream);
+
+/* fa_strerror -- static, NUL-terminated description of an FA_* code. */
+const char* fa_strerror(int code);
+
+/* fa_version -- library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_MI355X_FA_H */

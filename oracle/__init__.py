@@ -1,0 +1,115 @@
+"""fp64 CPU oracle for the exact attention forward.
+
+TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the benchmark's
+CPU-baseline leg may import or call this package; the GPU path never does, and
+this package imports nothing from it.
+
+The arithmetic lives in attn_oracle.c (plain C, fp64, one materialised score
+row per query, sequential sums); this module only builds it with gcc, loads it
+with ctypes and widens the inputs to fp32 (exact for bf16 and fp32 inputs).
+
+Definition followed (unite.ai page "Flash Attention: revolutionizing transformer
+efficiency", opening code block and "The Math Behind Flash Attention" item 1):
+    o_i = softmax_j(scale * q_i . k_j) v_j,   lse_i = ln sum_j exp(scale * q_i . k_j)
+over the visible keys (all j, or j <= i when causal -- a reading of "causal"
+in the triton-transformer README). Parity pins: tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "attn_oracle.c"
+_LIB = _HERE / "liboracle.so"
+_lib = None
+
+
+def build(force: bool = True) -> Path:
+    """Compile attn_oracle.c with gcc into liboracle.so (no -ffast-math: IEEE fp64 semantics)."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp")
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", str(_SRC), "-o", str(tmp), "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not _LIB.exists():
+            build(force=False)
+        lib = ctypes.CDLL(str(_LIB))
+        f = lib.oracle_attn_rows
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_int,
+                      ctypes.c_double,
+                      ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _as_f32(x) -> np.ndarray:
+    """Widen a CPU torch tensor (bf16 or fp32) or array to a contiguous fp32 ndarray, exactly."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu")
+            if x.dtype not in (torch.bfloat16, torch.float32):
+                raise TypeError(f"oracle takes bf16 or fp32 inputs, got {x.dtype}")
+            return np.ascontiguousarray(x.to(torch.float32).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(x)
+    if a.dtype != np.float32:
+        raise TypeError(f"oracle takes fp32 arrays, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def attention_rows(q, k, v, causal: bool, scale: float, rows=None, threads: int | None = None):
+    """Oracle output for the listed flat rows (b*H + h)*Nq + i (None: every row, in order).
+
+    q: [B, H, Nq, d], k and v: [B, H, Nk, d], bf16/fp32 (torch CPU tensors or fp32 arrays).
+    The attention problems have Nq == Nk; key blocks (Nk < Nq) serve the merge pins.
+    scale: the fp32 scale handed to the GPU; the oracle uses exactly that value.
+    Returns (o [n_rows, d] float64, lse [n_rows] float64).
+    """
+    qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
+    if qa.ndim != 4 or ka.shape != va.shape or qa.shape[:2] != ka.shape[:2] or qa.shape[3] != ka.shape[3]:
+        raise ValueError(f"q [B,H,Nq,d] and k, v [B,H,Nk,d] shapes disagree: {qa.shape} {ka.shape} {va.shape}")
+    B, H, N, d = qa.shape
+    Nk = ka.shape[2]
+    sc = float(np.float32(scale))
+    if rows is None:
+        n = B * H * N
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = int(rows_arr.size)
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    if n == 0:
+        return o, lse
+    rc = _load().oracle_attn_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, B, H, N, Nk, d, int(bool(causal)), sc,
+                                  None if rows_arr is None else rows_arr.ctypes.data, n, o.ctypes.data,
+                                  lse.ctypes.data, int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_rows failed with code {rc}")
+    return o, lse
+
+
+def attention(q, k, v, causal: bool, scale: float, threads: int | None = None):
+    """Oracle output for every row: (o [B,H,N,d] float64, lse [B,H,N] float64)."""
+    B, H, N, d = tuple(q.shape)
+    o, lse = attention_rows(q, k, v, causal, scale, None, threads)
+    return o.reshape(B, H, N, d), lse.reshape(B, H, N)

@@ -1,0 +1,292 @@
+"""Pins for the fp64 CPU oracle: facts fixed by the pages and by mathematics, not by the oracle itself.
+
+Definition pinned: the unite.ai page "Flash Attention: revolutionizing transformer
+efficiency" -- standard attention (opening code block), softmax with the row
+maximum subtracted ("The Math Behind Flash Attention", item 1) and the merge of
+two blocks' softmax ("The Math Behind Flash Attention", item 2, read with the
+inner softmax as the unnormalised exp(x - m_x) and the outer operation as the
+division by the merged sum, since the printed formula nests softmax in a way
+that has no meaning). Each pin is chosen so that a plausible slip in the oracle
+(a dropped scale, a sign, a wrong causal side, a transposed operand, a missing
+term in lse) fails at least one of them.
+"""
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import oracle
+
+GOLDEN = Path(__file__).resolve().parent / "golden" / "closed_form_cases.json"
+
+
+def _eval(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, {"e": math.e, "ln": math.log}))
+
+
+def _t(a, shape_bhnd):
+    return torch.tensor(np.asarray(a, dtype=np.float32).reshape(shape_bhnd))
+
+
+# --- golden closed forms ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_golden_closed_forms(causal):
+    cases = json.loads(GOLDEN.read_text())["cases"]
+    for c in cases:
+        q = np.asarray(c["q"], dtype=np.float32)
+        N, d = q.shape
+        q = _t(c["q"], (1, 1, N, d))
+        k = _t(c["k"], (1, 1, N, d))
+        v = _t(c["v"], (1, 1, N, d))
+        o, lse = oracle.attention(q, k, v, causal, c["scale"], threads=2)
+        exp = c["causal" if causal else "noncausal"]
+        o_ref = np.array([[_eval(x) for x in row] for row in exp["o"]])
+        lse_ref = np.array([_eval(x) for x in exp["lse"]])
+        np.testing.assert_allclose(o[0, 0], o_ref, rtol=0, atol=1e-14, err_msg=c["name"])
+        np.testing.assert_allclose(lse[0, 0], lse_ref, rtol=0, atol=1e-14, err_msg=c["name"])
+
+
+# --- brute force in pure Python (exactly rounded sums) -------------------------------------------------------------
+
+def _brute(q, k, v, causal, scale):
+    B, H, N, d = q.shape
+    qd, kd, vd = (x.to(torch.float64).numpy() for x in (q, k, v))
+    o = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                js = range(i + 1) if causal else range(N)
+                s = [scale * math.fsum(float(qd[b, h, i, c]) * float(kd[b, h, j, c]) for c in range(d)) for j in js]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = math.fsum(w)
+                for c in range(d):
+                    o[b, h, i, c] = math.fsum(wj * float(vd[b, h, j, c]) for wj, j in zip(w, js)) / tot
+                lse[b, h, i] = m + math.log(tot)
+    return o, lse
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (2, 1, 5, 3), (1, 2, 9, 5), (2, 2, 7, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(shape, causal):
+    q, k, v = ai.make_qkv(*shape, seed=11, dtype="f32")
+    scale = 0.37
+    o, lse = oracle.attention(q, k, v, causal, scale, threads=3)
+    ob, lb = _brute(q, k, v, causal, float(np.float32(scale)))
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-13)
+
+
+# --- library special case: torch SDPA on the CPU in fp64, scipy logsumexp ----------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d,dtype", [(1, 2, 333, 64, "bf16"), (2, 1, 130, 128, "bf16"), (1, 1, 128, 64, "f32")])
+def test_matches_sdpa_fp64(B, H, N, d, dtype, causal):
+    from scipy.special import logsumexp
+
+    q, k, v = ai.make_qkv(B, H, N, d, seed=101, dtype=dtype)
+    scale = ai.default_scale(d)
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    qd, kd, vd = (x.to(torch.float64) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, is_causal=causal, scale=scale).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    scores = np.einsum("bhic,bhjc->bhij", qd.numpy(), kd.numpy()) * scale
+    if causal:
+        scores = np.where(np.tril(np.ones((N, N), dtype=bool)), scores, -np.inf)
+    np.testing.assert_allclose(lse, logsumexp(scores, axis=-1), rtol=0, atol=1e-12)
+
+
+# --- V = I read-out: the output exposes the probabilities directly ---------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identity_readout_rows_sum_to_one(causal):
+    N, d = 48, 64
+    q, k, _ = ai.make_qkv(1, 1, N, d, seed=7, dtype="bf16")
+    v = torch.zeros((1, 1, N, d), dtype=torch.float32)
+    v[0, 0, :, :N] = torch.eye(N)
+    o, _ = oracle.attention(q, k, v, causal, ai.default_scale(d))
+    p = o[0, 0, :, :N]
+    assert np.all(p >= 0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(o[0, 0, :, N:] == 0)
+    if causal:
+        assert np.all(p[np.triu_indices(N, 1)] == 0.0)  # masked probabilities are exactly zero
+        assert np.all(np.diag(p) > 0)
+    else:
+        assert np.all(p > 0)
+
+
+# --- closed forms: q = 0, identical keys, a single key ---------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_is_mean_of_visible_values(causal):
+    B, H, N, d = 2, 2, 77, 64
+    _, k, v = ai.make_qkv(B, H, N, d, seed=3, dtype="bf16")
+    q = torch.zeros_like(k)
+    o, lse = oracle.attention(q, k, v, causal, ai.default_scale(d))
+    vd = v.to(torch.float64).numpy()
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = np.cumsum(vd, axis=2) / cnt[None, None, :, None] if causal else np.broadcast_to(
+        vd.mean(axis=2, keepdims=True), vd.shape)
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(cnt), lse.shape), rtol=0, atol=1e-13)
+
+
+def test_identical_keys_give_mean_for_any_query():
+    N, d = 50, 128
+    q, k, v = ai.make_qkv(1, 1, N, d, seed=5, dtype="bf16")
+    k = k[:, :, :1].expand(-1, -1, N, -1).contiguous()
+    o, lse = oracle.attention(q, k, v, False, 0.125)
+    vd = v.to(torch.float64).numpy()
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(vd[0, 0].mean(axis=0), (N, d)), rtol=0, atol=1e-13)
+    s = 0.125 * (q.to(torch.float64)[0, 0] @ k.to(torch.float64)[0, 0, 0]).numpy()
+    np.testing.assert_allclose(lse[0, 0], s + math.log(N), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_key(causal):
+    q, k, v = ai.make_qkv(2, 3, 1, 64, seed=9, dtype="bf16")
+    o, lse = oracle.attention(q, k, v, causal, 0.125)
+    np.testing.assert_array_equal(o, v.to(torch.float64).numpy())
+    s = 0.125 * (q.to(torch.float64) * k.to(torch.float64)).sum(-1).numpy()
+    np.testing.assert_allclose(lse, s, rtol=0, atol=1e-13)
+
+
+def test_causal_row0_is_v0_and_last_row_is_noncausal():
+    q, k, v = ai.make_qkv(1, 2, 65, 64, seed=4, dtype="bf16")
+    oc, lc = oracle.attention(q, k, v, True, 0.125)
+    on, ln_ = oracle.attention(q, k, v, False, 0.125)
+    np.testing.assert_array_equal(oc[:, :, 0], v.to(torch.float64).numpy()[:, :, 0])
+    np.testing.assert_allclose(oc[:, :, -1], on[:, :, -1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lc[:, :, -1], ln_[:, :, -1], rtol=0, atol=1e-14)
+
+
+def test_causal_row_is_attention_over_its_prefix():
+    N, d = 40, 64
+    q, k, v = ai.make_qkv(1, 1, N, d, seed=8, dtype="bf16")
+    oc, lc = oracle.attention(q, k, v, True, 0.125)
+    for i in (0, 1, 17, 39):
+        # row i of the causal problem == the non-causal problem of query i over keys 0..i
+        on, ln_ = oracle.attention(q[:, :, i:i + 1].contiguous(), k[:, :, :i + 1].contiguous(),
+                                   v[:, :, :i + 1].contiguous(), False, 0.125)
+        np.testing.assert_allclose(oc[0, 0, i], on[0, 0, 0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lc[0, 0, i], ln_[0, 0, 0], rtol=0, atol=1e-14)
+
+
+# --- the blockwise merge of the Math section, item 2 -------------------------------------------------------------------
+
+def _merge(parts):
+    """Merge per-block (o_b, lse_b): lse = ln sum_b exp(lse_b); o = sum_b exp(lse_b - lse) o_b."""
+    lses = np.stack([p[1] for p in parts])
+    m = lses.max(axis=0)
+    w = np.exp(lses - m)
+    lse = m + np.log(w.sum(axis=0))
+    o = sum(np.exp(p[1] - lse)[..., None] * p[0] for p in parts)
+    return o, lse
+
+
+@pytest.mark.parametrize("split", ["1", "7", "64", "random"])
+def test_blockwise_merge_equals_full_softmax(split):
+    B, H, N, d = 1, 2, 200, 64
+    q, k, v = ai.make_qkv(B, H, N, d, seed=12, dtype="bf16")
+    o_full, lse_full = oracle.attention(q, k, v, False, 0.125)
+    if split == "random":
+        rng = np.random.default_rng(0)
+        cuts = np.sort(rng.choice(np.arange(1, N), size=9, replace=False))
+    else:
+        cuts = np.arange(int(split), N, int(split))
+    bounds = [0, *cuts.tolist(), N]
+    parts = [oracle.attention(q, k[:, :, a:b].contiguous(), v[:, :, a:b].contiguous(), False, 0.125)
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    o, lse = _merge(parts)
+    np.testing.assert_allclose(o, o_full, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_full, rtol=1e-12, atol=1e-13)
+
+
+# --- invariances: shift of the keys, joint permutation, linearity in V ----------------------------------------------------
+
+def _grid(shape, seed, lo, hi, den):
+    """Values on a coarse dyadic grid so that sums of two of them stay exact in fp32."""
+    rng = np.random.default_rng(seed)
+    return torch.tensor(rng.integers(lo, hi, size=shape).astype(np.float32) / den)
+
+
+def test_key_shift_invariance():
+    B, H, N, d = 1, 2, 60, 64
+    q = _grid((B, H, N, d), 1, -8, 9, 8.0)
+    k = _grid((B, H, N, d), 2, -8, 9, 8.0)
+    v = _grid((B, H, N, d), 3, -8, 9, 8.0)
+    u = _grid((1, 1, 1, d), 4, -4, 5, 8.0)
+    scale = 0.125
+    o0, l0 = oracle.attention(q, k, v, False, scale)
+    o1, l1 = oracle.attention(q, k + u, v, False, scale)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12)
+    shift = scale * (q.double() * u.double()).sum(-1).numpy()
+    np.testing.assert_allclose(l1, l0 + shift, rtol=0, atol=1e-12)
+
+
+def test_joint_key_permutation_and_linearity():
+    B, H, N, d = 1, 1, 90, 64
+    q = _grid((B, H, N, d), 5, -8, 9, 8.0)
+    k = _grid((B, H, N, d), 6, -8, 9, 8.0)
+    v1 = _grid((B, H, N, d), 7, -8, 9, 8.0)
+    v2 = _grid((B, H, N, d), 8, -8, 9, 8.0)
+    perm = torch.tensor(np.random.default_rng(3).permutation(N))
+    o, l = oracle.attention(q, k, v1, False, 0.125)
+    op, lp = oracle.attention(q, k[:, :, perm].contiguous(), v1[:, :, perm].contiguous(), False, 0.125)
+    np.testing.assert_allclose(op, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lp, l, rtol=0, atol=1e-12)
+    o2, _ = oracle.attention(q, k, v2, False, 0.125)
+    o12, _ = oracle.attention(q, k, v1 + v2, False, 0.125)
+    np.testing.assert_allclose(o12, o + o2, rtol=0, atol=1e-12)
+    o3, _ = oracle.attention(q, k, 2 * v1, False, 0.125)
+    np.testing.assert_allclose(o3, 2 * o, rtol=0, atol=1e-12)
+
+
+# --- peaked rows: the max-subtracted path equals the unshifted sums when no exp overflows ----------------------------
+
+def test_peaked_rows_match_unshifted_evaluation():
+    w = ai.WORKLOADS["c5_bf16_b1h8n32768d64_causal_k3"]
+    N = 2048
+    q, k, v = ai.make_qkv(1, 2, N, w.d, seed=w.seed, dtype="bf16", k_scale=w.k_scale)
+    rows = np.array([0, 5, 700, 2047, N + 3, 2 * N - 1])
+    o, lse = oracle.attention_rows(q, k, v, True, w.scale, rows=rows)
+    qd, kd, vd = (x.to(torch.float64).numpy() for x in (q, k, v))
+    for r, fr in enumerate(rows):
+        bh, i = divmod(int(fr), N)
+        s = w.scale * (kd[0, bh, :i + 1] @ qd[0, bh, i])
+        assert s.max() < 700  # exp cannot overflow in fp64
+        e = np.exp(s)
+        np.testing.assert_allclose(o[r], (e @ vd[0, bh, :i + 1]) / e.sum(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[r], np.log(e.sum()), rtol=0, atol=1e-12)
+
+
+# --- sampled rows agree with the full evaluation; argument checks ------------------------------------------------------
+
+def test_rows_subset_matches_full():
+    q, k, v = ai.make_qkv(2, 2, 100, 64, seed=21, dtype="bf16")
+    of, lf = oracle.attention(q, k, v, True, 0.125)
+    rows = ai.sample_rows(2, 2, 100, 37, seed=21)
+    o, l = oracle.attention_rows(q, k, v, True, 0.125, rows=rows)
+    np.testing.assert_array_equal(o, of.reshape(-1, 64)[rows])
+    np.testing.assert_array_equal(l, lf.reshape(-1)[rows])
+
+
+def test_threads_do_not_change_bits():
+    q, k, v = ai.make_qkv(1, 3, 150, 64, seed=22, dtype="bf16")
+    a = oracle.attention(q, k, v, True, 0.125, threads=1)
+    b = oracle.attention(q, k, v, True, 0.125, threads=7)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_bad_rows_rejected():
+    q, k, v = ai.make_qkv(1, 1, 8, 64, seed=1, dtype="bf16")
+    with pytest.raises(RuntimeError):
+        oracle.attention_rows(q, k, v, False, 0.125, rows=np.array([8]))
