@@ -1,0 +1,15 @@
+"""Exact fused attention forward for AMD MI355X (gfx950): a C-ABI HIP library and its Python binding.
+
+    from exact_attention_13_amd import forward
+    o, lse = forward(q, k, v, causal=True)
+
+The library (libfa.so, built from csrc/ by `python -m exact_attention_13_amd.build`) exports fa_fwd,
+fa_fwd_f32, fa_strerror and fa_version (include/fa.h). Importing this package fails if it is not built.
+"""
+from .binding import (EXPORTS, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HEADDIM, FA_ERR_HIP, FA_ERR_NULL,
+                      FA_ERR_SHAPE, FA_OK, fa_fwd, fa_fwd_f32, fa_strerror, fa_version, library_path)
+from .attention import forward
+
+__all__ = ["forward", "fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version", "library_path", "EXPORTS", "FA_OK",
+           "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN", "FA_ERR_ARG", "FA_ERR_ALIAS",
+           "FA_ERR_HIP"]

@@ -1,0 +1,68 @@
+"""ctypes binding of libfa.so: the same entry points as include/fa.h, argument marshalling only.
+
+Every step of the attention forward runs in the library's HIP kernel. PyTorch only provides device
+buffers and the current stream. If libfa.so is missing this module raises at import time: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+# PyTorch ships its own HIP runtime (libamdhip64.so, soname libamdhip64.so.7). Importing torch first makes
+# libfa.so's libamdhip64.so.7 dependency resolve to that same copy; loading libfa.so first would map a second
+# HIP runtime into the process, and torch's streams and device pointers would then be handed to the wrong one.
+import torch  # noqa: F401  (load order matters, see above)
+
+_LIB_PATH = Path(__file__).resolve().parent / "libfa.so"
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEADDIM = 3
+FA_ERR_ALIGN = 4
+FA_ERR_ARG = 5
+FA_ERR_ALIAS = 6
+FA_ERR_HIP = 7
+
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version")
+
+if not _LIB_PATH.exists():
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m exact_attention_13_amd.build` "
+                      "(the attention forward has no other implementation)")
+_lib = ctypes.CDLL(str(_LIB_PATH))
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_lib.fa_fwd.restype = _I
+_lib.fa_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_lib.fa_fwd_f32.restype = _I
+_lib.fa_fwd_f32.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_lib.fa_strerror.restype = ctypes.c_char_p
+_lib.fa_strerror.argtypes = [_I]
+_lib.fa_version.restype = _I
+_lib.fa_version.argtypes = []
+
+
+def library_path() -> str:
+    return str(_LIB_PATH)
+
+
+def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int, scale: float,
+           stream: int) -> int:
+    """Raw entry point: device pointers as ints, bf16 q/k/v/o, fp32 lse. Returns the FA_* code."""
+    return _lib.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+
+
+def fa_fwd_f32(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,
+               scale: float, stream: int) -> int:
+    """Raw entry point: device pointers as ints, fp32 q/k/v/o and lse. Returns the FA_* code."""
+    return _lib.fa_fwd_f32(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+
+
+def fa_strerror(code: int) -> str:
+    return _lib.fa_strerror(code).decode()
+
+
+def fa_version() -> int:
+    return _lib.fa_version()

@@ -1,0 +1,95 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/fa.h declares, and rejects bad
+arguments before any HIP call (so these run without a GPU). No call here reaches a kernel launch."""
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import exact_attention_13_amd as fa
+from exact_attention_13_amd import binding
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "fa.h"
+A = 0x10000  # 16-byte aligned fake device addresses, far apart so that nothing overlaps
+B_ = 0x20000000
+
+
+def _declared():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^(?:const\s+)?\w+\s*\**\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for sym in _declared():
+        assert sym in exported, sym
+        assert hasattr(binding._lib, sym)
+
+
+def test_version_and_strerror():
+    assert fa.fa_version() == 10000
+    for code in range(8):
+        assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
+    assert fa.fa_strerror(99) == "unknown error code"
+
+
+def _call(fn=None, q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, B=1, H=2, N=64,
+          d=64, causal=0, scale=0.125):
+    fn = fn or fa.fa_fwd
+    return fn(q, k, v, o, lse, B, H, N, d, causal, scale, 0)
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+def test_error_codes(fn):
+    assert _call(fn, q=0) == fa.FA_ERR_NULL
+    assert _call(fn, lse=0) == fa.FA_ERR_NULL
+    assert _call(fn, N=-1) == fa.FA_ERR_SHAPE
+    assert _call(fn, B=-3) == fa.FA_ERR_SHAPE
+    assert _call(fn, B=300, H=300) == fa.FA_ERR_SHAPE
+    assert _call(fn, N=(1 << 30) + 1) == fa.FA_ERR_SHAPE
+    for d in (0, 32, 96, 256):
+        assert _call(fn, d=d) == fa.FA_ERR_HEADDIM
+    for s in (0.0, -0.125, float("inf"), float("nan")):
+        assert _call(fn, scale=s) == fa.FA_ERR_ARG
+    assert _call(fn, causal=2) == fa.FA_ERR_ARG
+    assert _call(fn, causal=-1) == fa.FA_ERR_ARG
+    assert _call(fn, q=A + 8) == fa.FA_ERR_ALIGN
+    assert _call(fn, o=A + 0x3000000 + 4) == fa.FA_ERR_ALIGN
+    assert _call(fn, lse=A + 0x4000000 + 2) == fa.FA_ERR_ALIGN
+    assert _call(fn, o=A) == fa.FA_ERR_ALIAS                     # o is q
+    assert _call(fn, o=A + 0x2000000 + 64) == fa.FA_ERR_ALIAS     # o starts inside v
+    assert _call(fn, lse=A + 0x1000000 + 16) == fa.FA_ERR_ALIAS  # lse inside k
+    assert _call(fn, lse=A + 0x3000000 + 256) == fa.FA_ERR_ALIAS  # lse inside o
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+def test_empty_problem_is_a_no_op_that_ignores_pointers(fn):
+    assert _call(fn, q=0, k=0, v=0, o=0, lse=0, N=0) == fa.FA_OK
+    assert _call(fn, q=0, k=0, v=0, o=0, lse=0, B=0) == fa.FA_OK
+    assert _call(fn, q=0, k=0, v=0, o=0, lse=0, H=0, d=128, causal=1) == fa.FA_OK
+    # scalar arguments are still checked on an empty problem
+    assert _call(fn, N=0, d=80) == fa.FA_ERR_HEADDIM
+    assert _call(fn, N=0, scale=0.0) == fa.FA_ERR_ARG
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
+
+
+def test_one_hip_runtime_in_the_process():
+    """libfa.so must share torch's HIP runtime: exactly one libamdhip64 mapped after importing the package."""
+    code = ("import exact_attention_13_amd, torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps))\n")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, check=True,
+                         cwd=str(HEADER.parent.parent)).stdout
+    assert out.strip() == "1"
