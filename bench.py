@@ -1,0 +1,390 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload c3_bf16_b2h16n4096d128]
+
+One step = one fa_fwd call (the whole hot path: Q/K/V read, S = QK^T, online softmax, PV, 1/l, o and lse
+written) over the workload's synthetic inputs, already resident in device memory. Prints ONE JSON line:
+value = attention-forward TFLOP/s (4*B*H*N^2*d, halved when causal) over the timed steps; roofline = the
+kernel's MFMA roofline from HIP-event launch durations; cpu_baseline = the fp64 oracle timed on a bounded
+sample of the same workload on this host's cores.
+
+Other modes (used to produce the rocprofv3 summaries under profiles/):
+    --pmc-pass          run a copy kernel of known size, then the workload kernel, a few times each
+    --summarize DIR     print a summary of the rocprofv3 output found under DIR
+    --write-profiles    turn the outputs of PROFILE_COMMANDS (under gpurun_out/) into profiles/ summaries
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk (AMD's published 2.5 PF)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "c3_bf16_b2h16n4096d128"
+KERNEL_SRC = ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_kernel.hip"
+PROFILES = ROOT / "profiles"
+
+
+# The rocprofv3 runs whose outputs --write-profiles summarises ({w} = workload name). Counter runs hold one
+# counter group each; the copy kernel of --pmc-pass calibrates FETCH_SIZE / WRITE_SIZE against known bytes.
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{w}_trace -o run -- "
+             "python bench.py --workload {w} --no-cpu-baseline --no-other-workloads --steps 50 --warmup 10",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_{w}_fetch -o run -- "
+             "python bench.py --workload {w} --pmc-pass",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_{w}_write -o run -- "
+             "python bench.py --workload {w} --pmc-pass",
+    "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA "
+          "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+          "-d gpurun_out/prof_{w}_sq -o run -- python bench.py --workload {w} --pmc-pass",
+}
+
+
+def kernel_src_hash() -> str:
+    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+
+
+def kernel_name(w) -> str:
+    kind = "bf16" if w.dtype == "bf16" else "f32"
+    return f"fa_fwd_{kind}_kernel<{w.d}, {'true' if w.causal else 'false'}>"
+
+
+def _device_inputs(w):
+    import torch
+    import attn_inputs as ai
+
+    q, k, v = ai.make_workload(w)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    return q, k, v, o, lse
+
+
+def _caller(w, q, k, v, o, lse, stream_handle):
+    import exact_attention_13_amd as fa
+
+    fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.d,
+            int(w.causal), w.scale, stream_handle)
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"fa_fwd failed: {fa.fa_strerror(rc)}")
+    return call
+
+
+def time_workload(w, steps: int, warmup: int):
+    """Returns (wall_s for `steps` calls, per-launch durations in ms from HIP events on the launch stream)."""
+    import torch
+
+    q, k, v, o, lse = _device_inputs(w)
+    stream = torch.cuda.current_stream()
+    call = _caller(w, q, k, v, o, lse, stream.cuda_stream)
+    for _ in range(warmup):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    del q, k, v, o, lse
+    return wall, durs
+
+
+def traffic_from_profiles(w):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on the current kernel source."""
+    f = PROFILES / f"{w.name}_hbm_traffic.txt"
+    if not f.exists():
+        return None
+    try:
+        rec = json.loads(f.read_text())
+    except json.JSONDecodeError:
+        return None
+    if rec.get("kernel_src_sha256_16") != kernel_src_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_rows: int):
+    """fp64 oracle on a seeded sample of the workload's query rows; TFLOP/s in the metric's FLOP count."""
+    import numpy as np
+
+    import attn_inputs as ai
+    import oracle
+
+    q, k, v = ai.make_workload(w)
+    rows = ai.sample_rows(w.B, w.H, w.N, n_rows, seed=w.seed + 7)
+    threads = oracle.default_threads()
+    oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows[:threads], threads=threads)  # load + warm
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    i = rows % w.N
+    keys = (i + 1) if w.causal else np.full_like(i, w.N)
+    flops = float(np.sum(4.0 * keys * w.d))  # 2 FLOP per q.k product term + 2 per p.v term, per visible key
+    # the metric counts 4*N*d per row (halved on average when causal); sampled rows use their real key counts
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} seeded random query rows of {w.name} ({len(rows) / (w.B * w.H * w.N):.1%} of "
+                      f"the rows), fp64, {dt:.2f} s wall on {threads} threads; FLOPs counted as 4*d per visible key",
+            "seconds": dt}
+
+
+def pmc_pass(w, reps: int):
+    """Kernels for the rocprofv3 counter runs: a plain copy of known size, then the workload kernel."""
+    import torch
+
+    n = 1 << 28  # 512 MiB of bf16 read + 512 MiB written by torch.neg
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    q, k, v, o, lse = _device_inputs(w)
+    call = _caller(w, q, k, v, o, lse, torch.cuda.current_stream().cuda_stream)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_pass": w.name, "copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "reps": reps,
+                      "kernel_src_sha256_16": kernel_src_hash()}), flush=True)
+
+
+def summarize(d: str):
+    """Summarise rocprofv3 CSV output under d: kernel stats and per-kernel counter means."""
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out.setdefault("kernel_stats", []).append(
+                    {"name": r.get("Name"), "calls": int(r.get("Calls", 0)),
+                     "avg_us": float(r.get("AverageNs", 0)) / 1e3, "min_us": float(r.get("MinNs", 0)) / 1e3,
+                     "max_us": float(r.get("MaxNs", 0)) / 1e3, "pct": float(r.get("Percentage", 0))})
+    counters = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (r.get("Kernel_Name"), r.get("Counter_Name"))
+                counters.setdefault(key, {})
+                did = r.get("Dispatch_Id")
+                counters[key][did] = counters[key].get(did, 0.0) + float(r.get("Counter_Value", 0))
+    if counters:
+        out["counters"] = [{"kernel": k[0], "counter": k[1], "dispatches": len(v),
+                            "mean_per_dispatch": statistics.fmean(v.values())} for k, v in sorted(counters.items())]
+    print(json.dumps(out, indent=1))
+
+
+def _stats(d):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _counters(d):
+    """{(kernel substring match later), counter} -> list of per-dispatch values (summed over dimensions)."""
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = (r["Kernel_Name"], r["Counter_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (kname, cname, _), val in per.items():
+        out.setdefault((kname, cname), []).append(val)
+    return out
+
+
+def _pick(counters, cname, needle):
+    vals = [v for (k, c), v in counters.items() if c == cname and needle in k]
+    if not vals:
+        raise RuntimeError(f"no {cname} values for kernels matching {needle!r}")
+    return statistics.fmean(vals[0])
+
+
+def write_profiles(w):
+    """Summaries of the PROFILE_COMMANDS outputs: profiles/<workload>_rocprof.md and ..._hbm_traffic.txt."""
+    dirs = {k: f"gpurun_out/prof_{w.name}_{k}" for k in PROFILE_COMMANDS}
+    kname = kernel_name(w).split("<")[0]
+    trace = [r for r in _stats(dirs["trace"]) if kname in r["Name"]]
+    if not trace:
+        raise RuntimeError("no kernel statistics for the attention kernel")
+    t = trace[0]
+    avg_us = float(t["AverageNs"]) / 1e3
+    fetch, write = _counters(dirs["fetch"]), _counters(dirs["write"])
+    copy = "neg_kernel"
+    copy_read_kib = _pick(fetch, "FETCH_SIZE", copy)
+    copy_write_kib = _pick(write, "WRITE_SIZE", copy)
+    known_kib = 2 * (1 << 28) / 1024  # bytes read (and written) by the copy, in KiB
+    f_fetch = known_kib / copy_read_kib
+    f_write = known_kib / copy_write_kib
+    k_read = _pick(fetch, "FETCH_SIZE", kname) * f_fetch * 1024
+    k_write = _pick(write, "WRITE_SIZE", kname) * f_write * 1024
+    sq = _counters(dirs["sq"])
+    mfma_busy = _pick(sq, "SQ_VALU_MFMA_BUSY_CYCLES", kname)
+    mops = _pick(sq, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kname)
+    conflict = _pick(sq, "SQ_LDS_BANK_CONFLICT", kname)
+    lds_active = _pick(sq, "SQ_LDS_IDX_ACTIVE", kname)
+    n_simd = 256 * 4
+    util = mfma_busy / n_simd / (avg_us * 1e-6 * 2.4e9)
+    traffic = {"kernel": kernel_name(w), "workload": w.name, "kernel_src_sha256_16": kernel_src_hash(),
+               "hbm_bytes_per_launch": round(k_read + k_write), "read_bytes": round(k_read),
+               "write_bytes": round(k_write), "algorithmic_bytes": w.algorithmic_bytes,
+               "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5)}
+    PROFILES.mkdir(exist_ok=True)
+    (PROFILES / f"{w.name}_hbm_traffic.txt").write_text(json.dumps(traffic, indent=1) + "\n")
+    cmds = "\n".join(f"    {PROFILE_COMMANDS[k].format(w=w.name)}" for k in PROFILE_COMMANDS)
+    md = f"""# rocprofv3 summary: {kernel_name(w)} on {w.name}
+
+Kernel source sha256[:16]: `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip).
+Workload: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} {w.dtype}; {w.flops:.4g} FLOP per launch
+(4*B*H*N^2*d{', halved' if w.causal else ''}), {w.algorithmic_bytes} algorithmic HBM bytes per launch.
+
+Commands (run from the repository root; outputs under gpurun_out/, summarised by `python bench.py --workload {w.name} --write-profiles`):
+
+{cmds}
+
+## Kernel trace (--kernel-trace --stats)
+
+| kernel | calls | avg us | min us | max us |
+|---|---|---|---|---|
+| {t['Name'][:90]} | {t['Calls']} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
+
+Attention TFLOP/s at the traced average: {w.flops / (avg_us * 1e-6) / 1e12:.1f}
+({100 * w.flops / (avg_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
+
+## HBM traffic (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+
+Calibration: the copy kernel (torch.neg over 2^28 bf16) reads and writes {known_kib:.0f} KiB;
+FETCH_SIZE reads {copy_read_kib:.1f} KiB (scale {f_fetch:.4f}), WRITE_SIZE reads {copy_write_kib:.1f} KiB (scale {f_write:.4f}).
+
+| | counter KiB | scaled bytes | algorithmic bytes |
+|---|---|---|---|
+| read | {k_read / f_fetch / 1024:.1f} | {k_read:.0f} | {3 * w.B * w.H * w.N * w.d * w.elt_bytes} (q, k, v) |
+| write | {k_write / f_write / 1024:.1f} | {k_write:.0f} | {w.B * w.H * w.N * (w.d * w.elt_bytes + 4)} (o, lse) |
+
+HBM bandwidth at the traced average: {(k_read + k_write) / (avg_us * 1e-6) / 1e9:.0f} GB/s.
+
+## Matrix cores and LDS (SQ counters, per dispatch)
+
+| counter | value |
+|---|---|
+| SQ_VALU_MFMA_BUSY_CYCLES | {mfma_busy:.4g} |
+| SQ_INSTS_VALU_MFMA_MOPS_BF16 (x512 FLOP) | {mops:.4g} (= {mops * 512:.4g} FLOP) |
+| SQ_INSTS_VALU | {_pick(sq, 'SQ_INSTS_VALU', kname):.4g} |
+| SQ_INSTS_MFMA | {_pick(sq, 'SQ_INSTS_MFMA', kname):.4g} |
+| SQ_LDS_BANK_CONFLICT | {conflict:.4g} |
+| SQ_LDS_IDX_ACTIVE | {lds_active:.4g} |
+| SQ_WAIT_INST_LDS | {_pick(sq, 'SQ_WAIT_INST_LDS', kname):.4g} |
+| SQ_WAVE_CYCLES | {_pick(sq, 'SQ_WAVE_CYCLES', kname):.4g} |
+| GRBM_GUI_ACTIVE | {_pick(sq, 'GRBM_GUI_ACTIVE', kname):.4g} |
+
+MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (traced average x 2.4 GHz) = {100 * util:.1f} %.
+LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active, 1):.1f} %.
+"""
+    (PROFILES / f"{w.name}_rocprof.md").write_text(md)
+    print(md)
+
+
+def main():
+    import attn_inputs as ai
+
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(ai.WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=32768, help="query rows in the oracle's CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--write-profiles", action="store_true")
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return 0
+    if args.write_profiles:
+        write_profiles(ai.WORKLOADS[args.workload])
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); the attention "
+              "forward shards over heads with no communication, so a multi-GPU figure is not measured here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import exact_attention_13_amd  # noqa: F401  (fails loudly if libfa.so is missing)
+
+    w = ai.WORKLOADS[args.workload]
+    if args.pmc_pass:
+        pmc_pass(w, reps=5)
+        return 0
+
+    wall, durs = time_workload(w, args.steps, args.warmup)
+    ms_step = wall / args.steps * 1e3
+    value = w.flops * args.steps / wall / 1e12
+    k_mean = statistics.fmean(durs)
+    k_med = statistics.median(durs)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = w.flops / (k_mean * 1e-3) / 1e12
+    line = {
+        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (B,H,N,d,causal)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q, k, v; no dataset)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "input_dtype": w.dtype, "accumulate": "fp32"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "kernel_ms": {"mean": round(k_mean, 4), "median": round(k_med, 4), "min": round(min(durs), 4),
+                      "p90": round(sorted(durs)[int(0.9 * (len(durs) - 1))], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w),
+                     "kernel": kernel_name(w), "flops_per_launch": w.flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+        "kernel_src_sha256_16": kernel_src_hash(),
+    }
+    if not args.no_other_workloads:
+        others = {}
+        for name, ow in ai.WORKLOADS.items():
+            if name == w.name or ow.dtype != "bf16":
+                continue
+            _, od = time_workload(ow, steps=20, warmup=3)
+            om = statistics.fmean(od)
+            others[name] = {"kernel_ms_mean": round(om, 4), "tflops": round(ow.flops / (om * 1e-3) / 1e12, 2),
+                            "pct_of_peak": round(100 * ow.flops / (om * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        line["other_workloads"] = others
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, args.cpu_rows)
+        cb.pop("seconds")
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

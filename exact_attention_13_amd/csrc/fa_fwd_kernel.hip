@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_launch.h"
 
 namespace fa {
@@ -89,18 +91,33 @@ __device__ __forceinline__ void map_workgroup(int lin, int nq, int bh_count, boo
 // ------------------------------------------------------------------------------------------------------------
 template <int D>
 struct Bf16Cfg {
-  static constexpr int kStrideK = D + 8;   // LDS row stride of K in elements (+16 B: 16-B reads of 16 rows hit
-                                           // distinct banks)
-  static constexpr int kStrideV = D + 16;  // LDS row stride of V (+32 B: the transposing reads of 4 rows x
-                                           // 32 B hit distinct banks)
-  static constexpr int kTileK = kBc * kStrideK;
+  // LDS row strides in elements. K: +16 B, so the 16-byte fragment reads of 16 different rows in one LDS
+  // pass land on distinct banks. V: +64 B, so the transposing reads of 4 consecutive rows x 64 B in one pass
+  // land on distinct banks (with +32 B every second row overlapped and each read took two passes).
+  static constexpr int kStrideK = D + 8;
+  static constexpr int kStrideV = D + 32;
+  static constexpr int kTileK = kBc * kStrideK;                 // elements per K buffer
   static constexpr int kTileV = kBc * kStrideV;
-  static constexpr int kLdsBytes = 2 * (kTileK + kTileV) * 2;
-  static constexpr int kChunksPerRow = D / 8;                         // 16-byte chunks per row
-  static constexpr int kChunks = kBc * kChunksPerRow / kThreads;      // per thread per tensor per tile
-  static constexpr int kDB = D / 16;                                  // K-steps of the first product
-  static constexpr int kCB = D / 32;                                  // 32-column blocks of the output
+  static constexpr int kLdsBytes = 2 * (kTileK + kTileV) * 2;   // two buffers of each
+  static constexpr int kChunksPerRow = D / 8;                   // 16-byte chunks per row
+  static constexpr int kChunks = kBc * kChunksPerRow / kThreads;  // per thread, per tensor, per tile
+  static constexpr int kDB = D / 16;                            // K-steps of the first product
+  static constexpr int kCB = D / 32;                            // 32-column blocks of the output
 };
+
+// A raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zero. gfx9-family
+// descriptor flags word. Only the per-lane offset is range-checked, so a tile's start goes into the base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+template <int V>
+using Int = std::integral_constant<int, V>;
+
+// Lazy rescaling: the exponent reference m_ref only moves when some row's new maximum exceeds it by more
+// than this (log2 units), so unnormalised weights stay <= 2^8 and the O rescale is skipped on most tiles.
+// Any reference gives the same softmax; lse and 1/l use the final reference.
+constexpr float kRescaleLog2 = 8.f;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
@@ -108,9 +125,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale) {
   using C = Bf16Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  lds_char* smem = (lds_char*)smem_raw;
-  lds_char* ks_base = smem;                                 // 2 buffers of K [kBc][kStrideK]
-  lds_char* vs_base = smem + 2 * C::kTileK * 2;             // 2 buffers of V [kBc][kStrideV]
+  lds_char* const smem = (lds_char*)smem_raw;
+  // layout: K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -142,137 +158,155 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // ---- K/V tile staging: each thread moves kChunks 16-byte chunks of K and of V per tile
+  // ---- K/V tile staging through registers: kChunks 16-byte chunks of K and of V per thread per tile.
+  // The per-thread byte offset inside a tile never changes; the tile start is in the descriptor.
+  int goff[C::kChunks];   // byte offset of chunk p inside a tile in device memory
+  int soff_k[C::kChunks]; // byte offset of chunk p inside K buffer 0 in LDS
+  int soff_v[C::kChunks]; // byte offset of chunk p inside V buffer 0 in LDS
+#pragma unroll
+  for (int p = 0; p < C::kChunks; ++p) {
+    const int c = tid + kThreads * p;
+    const int row = c / C::kChunksPerRow, col = (c % C::kChunksPerRow) * 8;
+    goff[p] = (row * D + col) * 2;
+    soff_k[p] = (row * C::kStrideK + col) * 2;
+    soff_v[p] = 2 * C::kTileK * 2 + (row * C::kStrideV + col) * 2;
+  }
   u32x4 kreg[C::kChunks], vreg[C::kChunks];
   auto load_tile = [&](int j) {
+    const int bytes = min(N - j * kBc, kBc) * D * 2;          // rows past N read as zero
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (size_t)j * kBc * D, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (size_t)j * kBc * D, bytes);
 #pragma unroll
     for (int p = 0; p < C::kChunks; ++p) {
-      const int c = tid + kThreads * p;
-      const int row = c / C::kChunksPerRow, col = (c % C::kChunksPerRow) * 8;
-      const int key = j * kBc + row;
-      if (key < N) {
-        kreg[p] = *(const u32x4*)(kh + (size_t)key * D + col);
-        vreg[p] = *(const u32x4*)(vh + (size_t)key * D + col);
-      } else {
-        kreg[p] = (u32x4){0u, 0u, 0u, 0u};
-        vreg[p] = (u32x4){0u, 0u, 0u, 0u};
-      }
+      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(kr, goff[p], 0, 0);
+      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vr, goff[p], 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-    lds_char* ks = ks_base + buf * C::kTileK * 2;
-    lds_char* vs = vs_base + buf * C::kTileV * 2;
+  auto store_tile = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
 #pragma unroll
     for (int p = 0; p < C::kChunks; ++p) {
-      const int c = tid + kThreads * p;
-      const int row = c / C::kChunksPerRow, col = (c % C::kChunksPerRow) * 8;
-      *(__attribute__((address_space(3))) u32x4*)(ks + (row * C::kStrideK + col) * 2) = kreg[p];
-      *(__attribute__((address_space(3))) u32x4*)(vs + (row * C::kStrideV + col) * 2) = vreg[p];
+      *(__attribute__((address_space(3))) u32x4*)(smem + soff_k[p] + BUF * C::kTileK * 2) = kreg[p];
+      *(__attribute__((address_space(3))) u32x4*)(smem + soff_v[p] + BUF * C::kTileV * 2) = vreg[p];
     }
   };
 
   // K row this lane feeds to the first product: bits 2 and 3 of l32 swapped.
   const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-  // Byte offsets (within a buffer) of this lane's K fragment reads and transposing V reads.
-  const int k_off = (krow * C::kStrideK + 8 * h) * 2;
-  const int v_off = ((8 * h + (lane & 15) / 4) * C::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // This lane's K fragment reads and transposing V reads (buffer 0).
+  const lds_char* const k_rd = smem + (krow * C::kStrideK + 8 * h) * 2;
+  const lds_char* const v_rd =
+      smem + 2 * C::kTileK * 2 +
+      ((8 * h + (lane & 15) / 4) * C::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   const float c2 = scale * kLog2e;
-  float m_run = -INFINITY;  // running max of raw scores q.k for row my_q
-  float l_run = 0.f;        // this lane's share of the running sum (keys it holds)
+  float m_ref = -INFINITY;  // exponent reference (raw-score units) for row my_q
+  float l_run = 0.f;        // this lane's share of the running sum (the keys it holds)
   f32x16 oacc[C::kCB];
 #pragma unroll
   for (int cb = 0; cb < C::kCB; ++cb) oacc[cb] = (f32x16){};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const bool more = (j + 1) < n_tiles;
-    if (more) load_tile(j + 1);
-
+  auto compute_tile = [&](int j, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int kv0 = j * kBc;
-    const bool active = (q0w < N) && (!CAUSAL || kv0 <= q0w + kRowsPerWave - 1);
-    if (active) {
-      const lds_char* ks = ks_base + buf * C::kTileK * 2;
-      const lds_char* vs = vs_base + buf * C::kTileV * 2;
+    const lds_char* ks = k_rd + BUF * C::kTileK * 2;
+    const lds_char* vs = v_rd + BUF * C::kTileV * 2;
 
-      // ---- S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks)
-      f32x16 s[2];
+    // ---- S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks)
+    f32x16 s[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        s[b] = (f32x16){};
+    for (int b = 0; b < 2; ++b) {
+      s[b] = (f32x16){};
 #pragma unroll
-        for (int kb = 0; kb < C::kDB; ++kb) {
-          const bf16x8 kf =
-              *(const __attribute__((address_space(3))) bf16x8*)(ks + k_off + (32 * b * C::kStrideK + 16 * kb) * 2);
-          s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s[b], 0, 0, 0);
-        }
+      for (int kb = 0; kb < C::kDB; ++kb) {
+        const bf16x8 kf =
+            *(const __attribute__((address_space(3))) bf16x8*)(ks + (32 * b * C::kStrideK + 16 * kb) * 2);
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s[b], 0, 0, 0);
       }
-      // s[b][r] is the score of query my_q and key kv0 + 32b + 16(r/8) + 8h + r%8.
+    }
+    // s[b][r] is the score of query my_q and key kv0 + 32b + 16(r/8) + 8h + r%8.
 
-      // ---- mask (only tiles that cross the diagonal or the end of the sequence)
-      const bool need_mask = (kv0 + kBc > N) || (CAUSAL && kv0 + kBc - 1 > q0w);
-      if (need_mask) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
-            const bool vis = (key < N) && (!CAUSAL || key <= my_q);
-            s[b][r] = vis ? s[b][r] : -INFINITY;
-          }
-      }
-
-      // ---- online softmax statistics
-      float mx = s[0][0];
+    // ---- mask (only tiles that cross the diagonal or the end of the sequence)
+    const bool need_mask = (kv0 + kBc > N) || (CAUSAL && kv0 + kBc - 1 > q0w);
+    if (need_mask) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-      mx = pair_max32(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // a row with no visible key so far
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      const float nb = -m_use * c2;
-      float rowsum = 0.f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f32x16 p;
-#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c2, nb));
-          rowsum += p[r];
+          const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
+          const bool vis = (key < N) && (!CAUSAL || key <= my_q);
+          s[b][r] = vis ? s[b][r] : -INFINITY;
         }
-        pf[2 * b] = __builtin_convertvector(p.lo, bf16x8);
-        pf[2 * b + 1] = __builtin_convertvector(p.hi, bf16x8);
-      }
-      l_run = l_run * alpha + rowsum;
-      m_run = m_new;
-#pragma unroll
-      for (int cb = 0; cb < C::kCB; ++cb) oacc[cb] *= alpha;
-
-      // ---- O^T += V^T P^T: 4 K-steps of 16 keys; lane slot 8h+e <-> key kv0 + 16m + 8h + e
-#pragma unroll
-      for (int cb = 0; cb < C::kCB; ++cb) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const lds_char* va = vs + v_off + ((16 * m) * C::kStrideV + 32 * cb) * 2;
-          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(va));
-          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(va + 4 * C::kStrideV * 2));
-          const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m], oacc[cb], 0, 0, 0);
-        }
-      }
     }
 
-    if (more) store_tile(buf ^ 1);
+    // ---- online softmax statistics
+    float mx = s[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+    mx = pair_max32(mx);  // row max over this tile's 64 keys
+    const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c2 > kRescaleLog2);
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no visible key yet: any finite reference
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_use) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < C::kCB; ++cb) oacc[cb] *= alpha;
+      m_ref = m_use;
+    }
+    const float nb = -m_ref * c2;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 pf[4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x16 p;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c2, nb));
+        rs[r & 3] += p[r];
+      }
+      pf[2 * b] = __builtin_convertvector(p.lo, bf16x8);
+      pf[2 * b + 1] = __builtin_convertvector(p.hi, bf16x8);
+    }
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+
+    // ---- O^T += V^T P^T: 4 K-steps of 16 keys; lane slot 8h+e <-> key kv0 + 16m + 8h + e
+#pragma unroll
+    for (int cb = 0; cb < C::kCB; ++cb) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const lds_char* va = vs + ((16 * m) * C::kStrideV + 32 * cb) * 2;
+        const bf16x4 v0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(va + 4 * C::kStrideV * 2));
+        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m], oacc[cb], 0, 0, 0);
+      }
+    }
+  };
+
+  // One tile: prefetch tile j+1 into registers, compute tile j from LDS buffer BUF, then write tile j+1 into
+  // the other buffer; one barrier per tile. Waves whose rows lie entirely above tile j (causal) only help
+  // with the copy.
+  auto step = [&](int j, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const bool more = (j + 1) < n_tiles;
+    if (more) load_tile(j + 1);
+    const bool active = (q0w < N) && (!CAUSAL || j * kBc <= q0w + kRowsPerWave - 1);
+    if (active) compute_tile(j, bufc);
+    if (more) store_tile(Int<BUF ^ 1>{});
     __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(Int<0>{});
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, Int<0>{});
+    if (j + 1 < n_tiles) step(j + 1, Int<1>{});
   }
 
   // ---- epilogue: o = acc / l once per row, lse = m*scale + ln l
@@ -290,10 +324,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         *(bf16x4*)(orow + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(x, bf16x4);
       }
     }
-    if (h == 0) {
-      const float m_fin = (m_run == -INFINITY) ? 0.f : m_run;
-      lse[(size_t)bh * N + my_q] = (m_fin * c2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    }
+    if (h == 0) lse[(size_t)bh * N + my_q] = (m_ref * c2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
