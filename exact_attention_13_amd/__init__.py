@@ -3,7 +3,7 @@
     from exact_attention_13_amd import forward
     o, lse = forward(q, k, v, causal=True)
 
-The library (libfa.so, built from csrc/ by `python -m exact_attention_13_amd.build`) exports fa_fwd,
+The library (libfa.so, built from csrc/ by `python exact_attention_13_amd/build.py`) exports fa_fwd,
 fa_fwd_f32, fa_strerror and fa_version (include/fa.h). Importing this package fails if it is not built.
 """
 from .binding import (EXPORTS, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HEADDIM, FA_ERR_HIP, FA_ERR_NULL,

@@ -28,7 +28,7 @@ FA_ERR_HIP = 7
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
-    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m exact_attention_13_amd.build` "
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_attention_13_amd/build.py` "
                       "(the attention forward has no other implementation)")
 _lib = ctypes.CDLL(str(_LIB_PATH))
 

@@ -1,6 +1,8 @@
 """Build libfa.so (the C-ABI library) from csrc/ with hipcc for gfx950, in-tree.
 
-    python -m exact_attention_13_amd.build
+    python exact_attention_13_amd/build.py
+
+Run it as a script (or load it by path): importing the package itself loads libfa.so, which may not exist yet.
 """
 from __future__ import annotations
 

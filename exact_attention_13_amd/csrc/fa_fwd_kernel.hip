@@ -9,24 +9,28 @@
 // of query rows as well as over batch x heads, and inside a workgroup each wave owns its own query rows
 // (no cross-wave reduction, K/V tiles shared read-only through LDS).
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 query rows; one wave = 32 query rows):
+// gfx950 mapping of the bf16 kernel (one workgroup = 8 waves = 256 query rows; one wave = 32 query rows):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (fp32 accumulate). With S transposed, lane l of a wave holds
 //     scores of query row (l % 32) only, so the row max needs one exchange between lanes l and l ^ 32
 //     (v_permlane32_swap) and the row sum needs none until the end.
 //   * The S^T accumulator is, after conversion to bf16, exactly the B operand of O^T = V^T P^T on the same
 //     MFMA shape. The K rows are fed to the first product in an order that swaps bits 2 and 3 of the row
-//     index, which makes the 8 keys a lane holds for the second product contiguous.
+//     index, which makes the 8 keys a lane holds for each 16-key step of the second product contiguous.
 //   * The V^T operand is read from row-major V in LDS with ds_read_b64_tr_b16 (transposing LDS read).
 //   * O^T accumulates per lane for one query row, so the rescale by alpha = exp2(m_old - m_new) is a
-//     per-lane scalar multiply.
+//     per-lane scalar multiply, done only when some row maximum grew by more than 2^8.
 //   * exp2 with log2(e) folded into the scale: p = exp2(s * c - m * c), c = scale * log2(e), one FMA.
-//   * K/V tiles of 64 keys are double-buffered in LDS: the global loads for tile j+1 are issued before the
-//     MFMAs of tile j and written to the other buffer after them; one barrier per tile.
+//   * The second product runs one 16-key step at a time, so the exponentials of step m+1 and the V reads of
+//     step m+1 overlap the MFMAs of step m; K fragment reads are issued about four MFMAs ahead.
+//   * K/V tiles of 64 keys go device memory -> LDS by LDS-DMA (buffer_load ... lds) through a 3-stage ring:
+//     tile j+2 is copied while tile j is computed; one barrier per tile. The LDS layouts are XOR-swizzled so
+//     that the K fragment reads, the transposing V reads and the DMA writes are all free of bank conflicts.
 //   * Causal: a workgroup visits only key tiles that meet its rows, a wave skips tiles entirely above its
 //     rows, and the mask is applied only on tiles that cross the diagonal or the sequence end.
 //   * The linear workgroup id is remapped so that (when B*H is a multiple of 8) every query block of a head
 //     runs on the same XCD (workgroups are dealt to the 8 XCDs round-robin) and shares that XCD's L2, and
 //     causal work starts with the longest query blocks.
+// The fp32 kernel keeps the same decomposition on v_mfma_f32_32x32x2f32 with a simple single-buffered loop.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -89,26 +93,40 @@ __device__ __forceinline__ void map_workgroup(int lin, int nq, int bh_count, boo
 // ------------------------------------------------------------------------------------------------------------
 // bf16 kernel
 // ------------------------------------------------------------------------------------------------------------
+// LDS layouts are unpadded and XOR-swizzled at 16-byte-chunk granularity. A tile is 64 rows x D bf16 (row of
+// RB = 2D bytes, CPR = D/8 chunks); chunk c of row r is stored at chunk position c ^ swz(r). LDS has 64 4-byte
+// banks, i.e. 16 bank groups of 16 bytes, so a bank group is (r % RPG) * CPR + position with RPG = 16 / CPR rows per
+// 256 bytes.
+//  * K is read 16 bytes per lane, 16 lanes per LDS pass, 16 different rows at one chunk:
+//    swz_k(r) = (r / RPG) % CPR puts those 16 reads in 16 different bank groups.
+//  * V is read by ds_read_b64_tr_b16, 32 lanes per pass, 4 consecutive rows x 4 consecutive chunks:
+//    swz_v(r) = 4 * ((r / RPG) % (CPR / 4)) spreads the 4 rows over different groups of 4 chunks.
+//  * Tiles are written by LDS-DMA (buffer_load ... lds): one wave-instruction writes 64 consecutive chunks, lane i
+//    chunk i, so each lane fetches from device memory the chunk whose swizzled position is its own.
 template <int D>
-struct Bf16Cfg {
-  // LDS row strides in elements. K: +16 B, so the 16-byte fragment reads of 16 different rows in one LDS
-  // pass land on distinct banks. V: +64 B, so the transposing reads of 4 consecutive rows x 64 B in one pass
-  // land on distinct banks (with +32 B every second row overlapped and each read took two passes).
-  static constexpr int kStrideK = D + 8;
-  static constexpr int kStrideV = D + 32;
-  static constexpr int kTileK = kBc * kStrideK;                 // elements per K buffer
-  static constexpr int kTileV = kBc * kStrideV;
-  static constexpr int kLdsBytes = 2 * (kTileK + kTileV) * 2;   // two buffers of each
-  static constexpr int kChunksPerRow = D / 8;                   // 16-byte chunks per row
-  static constexpr int kChunks = kBc * kChunksPerRow / kThreads;  // per thread, per tensor, per tile
-  static constexpr int kDB = D / 16;                            // K-steps of the first product
-  static constexpr int kCB = D / 32;                            // 32-column blocks of the output
+struct Tile {
+  static constexpr int RB = 2 * D;        // bytes per row
+  static constexpr int CPR = D / 8;       // 16-byte chunks per row
+  static constexpr int RPG = 16 / CPR;    // rows per 256 bytes
+  static constexpr int kBytes = kBc * RB; // one K or V tile
+  static constexpr int kInsts = kBytes / 1024;  // wave-instructions to copy one tile
+  __device__ static constexpr int swz_k(int r) { return (r / RPG) % CPR; }
+  __device__ static constexpr int swz_v(int r) { return 4 * ((r / RPG) % (CPR / 4)); }
 };
 
-// A raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zero. gfx9-family
-// descriptor flags word. Only the per-lane offset is range-checked, so a tile's start goes into the base.
+// A raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zero (also when the
+// destination is LDS). gfx9-family descriptor flags word. Only the per-lane offset is range-checked, so a tile's
+// start goes into the base.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// One LDS-DMA copy: each lane moves 16 bytes from the descriptor's range at byte offset `off` to
+// lds_base + 16 * lane (lds_base must be the same for the whole wave). Kept in a plain (non-template) function:
+// written directly inside the kernel template, the builtin made the host compilation pass drop the kernel's
+// launch stub without a diagnostic.
+__device__ __forceinline__ void lds_copy16_inline(__amdgpu_buffer_rsrc_t r, lds_char* lds_base, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
 }
 
 template <int V>
@@ -119,17 +137,39 @@ using Int = std::integral_constant<int, V>;
 // Any reference gives the same softmax; lse and 1/l use the final reference.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
+// Wait until at most N vector-memory operations of this wave are outstanding (the LDS-DMA copies), then join
+// the workgroup. The barrier is written as a statement with a memory clobber: the compiler may not move memory
+// accesses across it, and no fence is emitted (a release fence would wait for every copy in flight, including
+// the ones meant to overlap the next tile).
+template <int N>
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0 (LDS reads done)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// bf16 kernel: NW waves x 32 query rows per workgroup, ST-stage K/V pipeline in LDS.
+template <int D, bool CAUSAL, int NW, int ST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale) {
-  using C = Bf16Cfg<D>;
+  using T = Tile<D>;
+  constexpr int kThr = 64 * NW;
+  constexpr int kBrW = NW * kRowsPerWave;        // query rows per workgroup
+  constexpr int kDB = D / 16;                    // K-steps of the first product
+  constexpr int kCB = D / 32;                    // 32-column blocks of the output
+  constexpr int kCopies = T::kInsts / NW;        // copy instructions per wave per tensor per tile
+  static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
+  static_assert(ST == 2 || ST == 3, "pipeline depth");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   lds_char* const smem = (lds_char*)smem_raw;
-  // layout: K buffer 0 | K buffer 1 | V buffer 0 | V buffer 1
+  lds_char* const kst = smem;                    // ST K stages
+  lds_char* const vst = smem + ST * T::kBytes;   // ST V stages
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
 
   const int nq = gridDim.x;
@@ -141,16 +181,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const __bf16* kh = k + head_off;
   const __bf16* vh = v + head_off;
 
-  const int q_lo = qb * kBr;
-  const int q_last = min(q_lo + kBr, N) - 1;                 // last real query row of the workgroup
+  const int q_lo = qb * kBrW;
+  const int q_last = min(q_lo + kBrW, N) - 1;              // last real query row of the workgroup
   const int n_tiles = CAUSAL ? (q_last / kBc + 1) : (N + kBc - 1) / kBc;
-  const int q0w = q_lo + wave * kRowsPerWave;                 // first query row of this wave
-  const int my_q = q0w + l32;                                 // query row of this lane
+  const int q0w = q_lo + wave * kRowsPerWave;               // first query row of this wave
+  const int my_q = q0w + l32;                               // query row of this lane
+  // Tiles j < wave_tiles hold at least one key visible to this wave's rows.
+  const int wave_tiles =
+      (q0w >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kRowsPerWave - 1) / kBc + 1) : n_tiles);
 
   // ---- Q fragments: lane holds q[my_q][16*kb + 8*h .. +7] (B operand of S^T = K Q^T)
-  bf16x8 qf[C::kDB];
+  bf16x8 qf[kDB];
 #pragma unroll
-  for (int kb = 0; kb < C::kDB; ++kb) {
+  for (int kb = 0; kb < kDB; ++kb) {
     if (my_q < N) {
       qf[kb] = *(const bf16x8*)(qh + (size_t)my_q * D + 16 * kb + 8 * h);
     } else {
@@ -158,59 +201,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // ---- K/V tile staging through registers: kChunks 16-byte chunks of K and of V per thread per tile.
-  // The per-thread byte offset inside a tile never changes; the tile start is in the descriptor.
-  int goff[C::kChunks];   // byte offset of chunk p inside a tile in device memory
-  int soff_k[C::kChunks]; // byte offset of chunk p inside K buffer 0 in LDS
-  int soff_v[C::kChunks]; // byte offset of chunk p inside V buffer 0 in LDS
+  // ---- tile copies (LDS-DMA). Copy instruction p of this wave writes chunk positions g*64 .. g*64+63 of the
+  // tile, g = wave + NW*p; this lane writes position g*64 + lane and fetches the chunk stored there.
+  int dma_k[kCopies], dma_v[kCopies];  // byte offsets inside the tile in device memory
 #pragma unroll
-  for (int p = 0; p < C::kChunks; ++p) {
-    const int c = tid + kThreads * p;
-    const int row = c / C::kChunksPerRow, col = (c % C::kChunksPerRow) * 8;
-    goff[p] = (row * D + col) * 2;
-    soff_k[p] = (row * C::kStrideK + col) * 2;
-    soff_v[p] = 2 * C::kTileK * 2 + (row * C::kStrideV + col) * 2;
+  for (int p = 0; p < kCopies; ++p) {
+    const int pos = (wave + NW * p) * 64 + lane;
+    const int row = pos / T::CPR, phys = pos % T::CPR;
+    dma_k[p] = row * T::RB + (phys ^ T::swz_k(row)) * 16;
+    dma_v[p] = row * T::RB + (phys ^ T::swz_v(row)) * 16;
   }
-  u32x4 kreg[C::kChunks], vreg[C::kChunks];
-  auto load_tile = [&](int j) {
-    const int bytes = min(N - j * kBc, kBc) * D * 2;          // rows past N read as zero
+  auto copy_tile = [&](int j, auto stc) __attribute__((always_inline)) {
+    constexpr int S = decltype(stc)::value;
+    const int bytes = min(N - j * kBc, kBc) * T::RB;   // rows past N arrive as zeros
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (size_t)j * kBc * D, bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (size_t)j * kBc * D, bytes);
 #pragma unroll
-    for (int p = 0; p < C::kChunks; ++p) {
-      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(kr, goff[p], 0, 0);
-      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vr, goff[p], 0, 0);
-    }
-  };
-  auto store_tile = [&](auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-#pragma unroll
-    for (int p = 0; p < C::kChunks; ++p) {
-      *(__attribute__((address_space(3))) u32x4*)(smem + soff_k[p] + BUF * C::kTileK * 2) = kreg[p];
-      *(__attribute__((address_space(3))) u32x4*)(smem + soff_v[p] + BUF * C::kTileV * 2) = vreg[p];
+    for (int p = 0; p < kCopies; ++p) {
+      const int dst = (wave + NW * p) * 1024;
+      lds_copy16_inline(kr, kst + S * T::kBytes + dst, dma_k[p]);
+      lds_copy16_inline(vr, vst + S * T::kBytes + dst, dma_v[p]);
     }
   };
 
-  // K row this lane feeds to the first product: bits 2 and 3 of l32 swapped.
+  // ---- this lane's LDS read offsets (stage 0)
+  // K: row 32b + krow (krow = l32 with bits 2 and 3 swapped, see the header), chunk 2kb + h. swz_k depends only
+  // on the row modulo 32 here, so one offset per kb serves both 32-key blocks.
   const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-  // This lane's K fragment reads and transposing V reads (buffer 0).
-  const lds_char* const k_rd = smem + (krow * C::kStrideK + 8 * h) * 2;
-  const lds_char* const v_rd =
-      smem + 2 * C::kTileK * 2 +
-      ((8 * h + (lane & 15) / 4) * C::kStrideV + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  int k_off[kDB];
+#pragma unroll
+  for (int kb = 0; kb < kDB; ++kb) k_off[kb] = krow * T::RB + ((2 * kb + h) ^ T::swz_k(krow)) * 16;
+  // V (transposing read): rows 16m + 8h + 4*half + (lane&15)/4, columns 32cb + 16*((lane>>4)&1) + 4*(lane&3).
+  // swz_v depends on the row only through (lane&15)/4 here, so one offset per cb serves every m and half.
+  const int vrow = 8 * h + (lane & 15) / 4;
+  int v_off[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int col = 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    v_off[cb] = vrow * T::RB + ((col / 8) ^ T::swz_v(vrow)) * 16 + (col % 8) * 2;
+  }
 
   const float c2 = scale * kLog2e;
   float m_ref = -INFINITY;  // exponent reference (raw-score units) for row my_q
   float l_run = 0.f;        // this lane's share of the running sum (the keys it holds)
-  f32x16 oacc[C::kCB];
+  f32x16 oacc[kCB];
 #pragma unroll
-  for (int cb = 0; cb < C::kCB; ++cb) oacc[cb] = (f32x16){};
+  for (int cb = 0; cb < kCB; ++cb) oacc[cb] = (f32x16){};
 
-  auto compute_tile = [&](int j, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
+  auto compute_tile = [&](int j, auto stc) __attribute__((always_inline)) {
+    constexpr int S = decltype(stc)::value;
     const int kv0 = j * kBc;
-    const lds_char* ks = k_rd + BUF * C::kTileK * 2;
-    const lds_char* vs = v_rd + BUF * C::kTileV * 2;
+    const lds_char* ks = kst + S * T::kBytes;
+    const lds_char* vs = vst + S * T::kBytes;
 
     // ---- S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks)
     f32x16 s[2];
@@ -218,12 +260,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int b = 0; b < 2; ++b) {
       s[b] = (f32x16){};
 #pragma unroll
-      for (int kb = 0; kb < C::kDB; ++kb) {
-        const bf16x8 kf =
-            *(const __attribute__((address_space(3))) bf16x8*)(ks + (32 * b * C::kStrideK + 16 * kb) * 2);
+      for (int kb = 0; kb < kDB; ++kb) {
+        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(ks + k_off[kb] + 32 * b * T::RB);
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s[b], 0, 0, 0);
       }
     }
+    // Issue order for the block above (scheduling groups: 0x100 = LDS read, 0x008 = MFMA): 4 fragment reads,
+    // then one MFMA per further read, so each K fragment is read ~4 MFMAs before it is used.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * kDB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // s[b][r] is the score of query my_q and key kv0 + 32b + 16(r/8) + 8h + r%8.
 
     // ---- mask (only tiles that cross the diagonal or the end of the sequence)
@@ -253,60 +303,75 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const float alpha = __builtin_amdgcn_exp2f((m_ref - m_use) * c2);
       l_run *= alpha;
 #pragma unroll
-      for (int cb = 0; cb < C::kCB; ++cb) oacc[cb] *= alpha;
+      for (int cb = 0; cb < kCB; ++cb) oacc[cb] *= alpha;
       m_ref = m_use;
     }
     const float nb = -m_ref * c2;
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 pf[4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x16 p;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c2, nb));
-        rs[r & 3] += p[r];
-      }
-      pf[2 * b] = __builtin_convertvector(p.lo, bf16x8);
-      pf[2 * b + 1] = __builtin_convertvector(p.hi, bf16x8);
-    }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
-    // ---- O^T += V^T P^T: 4 K-steps of 16 keys; lane slot 8h+e <-> key kv0 + 16m + 8h + e
+    // ---- P and O^T += V^T P^T, one 16-key step m at a time: the 8 exponentials of step m+1 can run on the
+    // vector ALU while the MFMAs of step m run, and the V fragments of step m+1 are read during step m.
+    // Lane slot 8h+e of step m <-> key kv0 + 16m + 8h + e.
+    auto read_v = [&](int m, bf16x8(&vf)[kCB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cb = 0; cb < C::kCB; ++cb) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const lds_char* va = vs + ((16 * m) * C::kStrideV + 32 * cb) * 2;
+      for (int cb = 0; cb < kCB; ++cb) {
+        const lds_char* va = vs + v_off[cb] + 16 * m * T::RB;
         const bf16x4 v0 =
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va));
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(va + 4 * C::kStrideV * 2));
-        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[m], oacc[cb], 0, 0, 0);
+            (__attribute__((address_space(3))) bf16x4*)(va + 4 * T::RB));
+        vf[cb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+    };
+    bf16x8 vfa[kCB], vfb[kCB];
+    read_v(0, vfa);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      bf16x8(&vcur)[kCB] = (m & 1) ? vfb : vfa;
+      bf16x8(&vnxt)[kCB] = (m & 1) ? vfa : vfb;
+      f32x8 x = (m & 1) ? s[m >> 1].hi : s[m >> 1].lo;
+      f32x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, nb));
+        rs[e & 3] += p[e];
+      }
+      const bf16x8 pf = __builtin_convertvector(p, bf16x8);
+      if (m < 3) read_v(m + 1, vnxt);
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[cb], pf, oacc[cb], 0, 0, 0);
+    }
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+
+  // One tile: start copying tile j+ST-1 into the stage tile j-1 used (every wave finished it before the last
+  // barrier), compute tile j, wait for this wave's copies of tile j+1, barrier.
+  auto step = [&](int j, auto stc) __attribute__((always_inline)) {
+    constexpr int S = decltype(stc)::value;
+    const bool issue = j + ST - 1 < n_tiles;
+    if (issue) copy_tile(j + ST - 1, Int<(S + ST - 1) % ST>{});
+    if (j < wave_tiles) compute_tile(j, stc);
+    if (ST == 3 && issue) {
+      wait_copies_and_barrier<2 * kCopies>();  // tile j+2's copies may stay in flight
+    } else {
+      wait_copies_and_barrier<0>();
     }
   };
 
-  // One tile: prefetch tile j+1 into registers, compute tile j from LDS buffer BUF, then write tile j+1 into
-  // the other buffer; one barrier per tile. Waves whose rows lie entirely above tile j (causal) only help
-  // with the copy.
-  auto step = [&](int j, auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    const bool more = (j + 1) < n_tiles;
-    if (more) load_tile(j + 1);
-    const bool active = (q0w < N) && (!CAUSAL || j * kBc <= q0w + kRowsPerWave - 1);
-    if (active) compute_tile(j, bufc);
-    if (more) store_tile(Int<BUF ^ 1>{});
-    __syncthreads();
-  };
-
-  load_tile(0);
-  store_tile(Int<0>{});
-  __syncthreads();
-  for (int j = 0; j < n_tiles; j += 2) {
+  // prologue: tiles 0 .. ST-2 into stages 0 .. ST-2
+  copy_tile(0, Int<0>{});
+  if (ST == 3 && n_tiles > 1) {
+    copy_tile(1, Int<1>{});
+    wait_copies_and_barrier<2 * kCopies>();
+  } else {
+    wait_copies_and_barrier<0>();
+  }
+  for (int j = 0; j < n_tiles; j += ST) {
     step(j, Int<0>{});
     if (j + 1 < n_tiles) step(j + 1, Int<1>{});
+    if constexpr (ST == 3) {
+      if (j + 2 < n_tiles) step(j + 2, Int<2>{});
+    }
   }
 
   // ---- epilogue: o = acc / l once per row, lse = m*scale + ln l
@@ -315,7 +380,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float inv = 1.f / l_tot;
     __bf16* orow = o + head_off + (size_t)my_q * D;
 #pragma unroll
-    for (int cb = 0; cb < C::kCB; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // oacc[cb][4g + i] is column 32cb + 8g + 4h + i of row my_q
@@ -476,15 +541,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(const float* __res
 // ------------------------------------------------------------------------------------------------------------
 // launchers (arguments already validated by the C ABI layer)
 // ------------------------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NW, int ST>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                               float scale, hipStream_t stream) {
-  constexpr int lds = Bf16Cfg<D>::kLdsBytes;
-  auto kern = fa_fwd_bf16_kernel<D, CAUSAL>;
+  constexpr int lds = 2 * ST * Tile<D>::kBytes;
+  constexpr int rows = NW * kRowsPerWave;
+  auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((N + kBr - 1) / kBr), (unsigned)BH);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, (const __bf16*)q, (const __bf16*)k,
+  const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)BH);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, (__bf16*)o, lse, N, BH, scale);
   return hipGetLastError();
 }
@@ -503,10 +569,10 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            bool causal, float scale, hipStream_t stream) {
-  if (d == 64) return causal ? launch_bf16<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                             : launch_bf16<64, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_bf16<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_bf16<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+  if (d == 64) return causal ? launch_bf16<64, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
+                             : launch_bf16<64, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? launch_bf16<128, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
+                : launch_bf16<128, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
@@ -516,7 +582,5 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   return causal ? launch_f32<128, true>(q, k, v, o, lse, BH, N, scale, stream)
                 : launch_f32<128, false>(q, k, v, o, lse, BH, N, scale, stream);
 }
-
-int query_rows_per_workgroup() { return kBr; }
 
 }  // namespace fa

@@ -10,7 +10,5 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            bool causal, float scale, hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, hipStream_t stream);
-// Query rows handled by one workgroup (the grid's x extent is ceil(N / this)).
-int query_rows_per_workgroup();
 }  // namespace fa
 #endif
