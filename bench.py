@@ -57,8 +57,12 @@ def kernel_src_hash() -> str:
 
 
 def kernel_name(w) -> str:
-    kind = "bf16" if w.dtype == "bf16" else "f32"
-    return f"fa_fwd_{kind}_kernel<{w.d}, {'true' if w.causal else 'false'}>"
+    """The kernel instance the library launches for workload w (mirrors the launcher's choice)."""
+    c = "true" if w.causal else "false"
+    if w.dtype != "bf16":
+        return f"fa_fwd_f32_kernel<{w.d}, {c}>"
+    wide = ((w.N + 255) // 256) * w.B * w.H >= 512
+    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {8 if wide else 4}, {3 if wide else 2}>"
 
 
 def _device_inputs(w):

@@ -9,7 +9,7 @@
 // of query rows as well as over batch x heads, and inside a workgroup each wave owns its own query rows
 // (no cross-wave reduction, K/V tiles shared read-only through LDS).
 //
-// gfx950 mapping of the bf16 kernel (one workgroup = 8 waves = 256 query rows; one wave = 32 query rows):
+// gfx950 mapping of the bf16 kernel (one workgroup = 8 or 4 waves; one wave = 32 query rows):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (fp32 accumulate). With S transposed, lane l of a wave holds
 //     scores of query row (l % 32) only, so the row max needs one exchange between lanes l and l ^ 32
 //     (v_permlane32_swap) and the row sum needs none until the end.
@@ -20,10 +20,12 @@
 //   * O^T accumulates per lane for one query row, so the rescale by alpha = exp2(m_old - m_new) is a
 //     per-lane scalar multiply, done only when some row maximum grew by more than 2^8.
 //   * exp2 with log2(e) folded into the scale: p = exp2(s * c - m * c), c = scale * log2(e), one FMA.
+//   * The row sum l adds the bf16-rounded weights (the values the MFMA multiplies V by), two per
+//     v_dot2c_f32_bf16, so o is the exact weighted average under those weights.
 //   * The second product runs one 16-key step at a time, so the exponentials of step m+1 and the V reads of
 //     step m+1 overlap the MFMAs of step m; K fragment reads are issued about four MFMAs ahead.
-//   * K/V tiles of 64 keys go device memory -> LDS by LDS-DMA (buffer_load ... lds) through a 3-stage ring:
-//     tile j+2 is copied while tile j is computed; one barrier per tile. The LDS layouts are XOR-swizzled so
+//   * K/V tiles of 64 keys go device memory -> LDS by LDS-DMA (buffer_load ... lds) through a 3-stage ring
+//     (8 waves; 2 stages for 4 waves): tile j+2 is copied while tile j is computed; one barrier per tile. The LDS layouts are XOR-swizzled so
 //     that the K fragment reads, the transposing V reads and the DMA writes are all free of bank conflicts.
 //   * Causal: a workgroup visits only key tiles that meet its rows, a wave skips tiles entirely above its
 //     rows, and the mask is applied only on tiles that cross the diagonal or the sequence end.
@@ -46,6 +48,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kWaves = 4;
@@ -55,6 +58,7 @@ constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBc = 64;                     // keys per K/V tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the lower 32 lanes of its second.
 // Fed x twice, every lane ends up holding {x[l], x[l ^ 32]} across the two results, in an order that depends
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       m_ref = m_use;
     }
     const float nb = -m_ref * c2;
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs[2] = {0.f, 0.f};
 
     // ---- P and O^T += V^T P^T, one 16-key step m at a time: the 8 exponentials of step m+1 can run on the
     // vector ALU while the MFMAs of step m run, and the V fragments of step m+1 are read during step m.
@@ -332,16 +336,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       f32x8 x = (m & 1) ? s[m >> 1].hi : s[m >> 1].lo;
       f32x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, nb));
-        rs[e & 3] += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, nb));
       const bf16x8 pf = __builtin_convertvector(p, bf16x8);
+      // Row sum of the rounded weights (the ones the MFMA multiplies V by), two per v_dot2c_f32_bf16.
+      rs[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), kOnes2, rs[0], false);
+      rs[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), kOnes2, rs[1], false);
+      rs[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, rs[0], false);
+      rs[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, rs[1], false);
       if (m < 3) read_v(m + 1, vnxt);
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[cb], pf, oacc[cb], 0, 0, 0);
     }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    l_run += rs[0] + rs[1];
   };
 
   // One tile: start copying tile j+ST-1 into the stage tile j-1 used (every wave finished it before the last
@@ -567,12 +573,25 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
   return hipGetLastError();
 }
 
+// Workgroup shape: 8 waves (256 rows, one workgroup per CU, 3-stage ring) when the grid has at least two such
+// workgroups per CU of an MI355X (256 CUs); otherwise 4 waves (128 rows, two workgroups per CU, 2-stage ring),
+// which doubles the workgroups of short sequences. Each row's arithmetic is the same in both, so the choice does
+// not change any output bit.
+constexpr long long kWideGridMin = 512;
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            bool causal, float scale, hipStream_t stream) {
-  if (d == 64) return causal ? launch_bf16<64, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
-                             : launch_bf16<64, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_bf16<128, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_bf16<128, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
+  const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
+  if (wide) {
+    if (d == 64) return causal ? launch_bf16<64, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
+                               : launch_bf16<64, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_bf16<128, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
+                  : launch_bf16<128, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
+  }
+  if (d == 64) return causal ? launch_bf16<64, true, 4, 2>(q, k, v, o, lse, BH, N, scale, stream)
+                             : launch_bf16<64, false, 4, 2>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? launch_bf16<128, true, 4, 2>(q, k, v, o, lse, BH, N, scale, stream)
+                : launch_bf16<128, false, 4, 2>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
