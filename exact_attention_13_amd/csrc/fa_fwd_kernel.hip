@@ -153,8 +153,9 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// bf16 kernel: NW waves x 32 query rows per workgroup, ST-stage K/V pipeline in LDS.
-template <int D, bool CAUSAL, int NW, int ST>
+// bf16 kernel: NW waves x 32 query rows per workgroup, K/V tiles of KT x 64 keys (each 64-key part is one
+// swizzled Tile in LDS), ST-stage pipeline in LDS.
+template <int D, bool CAUSAL, int NW, int ST, int KT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale) {
@@ -163,13 +164,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int kBrW = NW * kRowsPerWave;        // query rows per workgroup
   constexpr int kDB = D / 16;                    // K-steps of the first product
   constexpr int kCB = D / 32;                    // 32-column blocks of the output
-  constexpr int kCopies = T::kInsts / NW;        // copy instructions per wave per tensor per tile
+  constexpr int kCopies = T::kInsts / NW;        // copy instructions per wave per tensor per 64-key part
+  constexpr int kBcT = KT * kBc;                 // keys per tile
+  constexpr int kStage = KT * T::kBytes;         // bytes of one tensor's tile in LDS
+  constexpr int kWaitKeep = 2 * KT * kCopies;    // copy instructions per wave per tile (K and V)
   static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
   static_assert(ST == 2 || ST == 3, "pipeline depth");
+  static_assert(KT == 1 || KT == 2, "tile width");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   lds_char* const smem = (lds_char*)smem_raw;
   lds_char* const kst = smem;                    // ST K stages
-  lds_char* const vst = smem + ST * T::kBytes;   // ST V stages
+  lds_char* const vst = smem + ST * kStage;      // ST V stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,12 +192,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int q_lo = qb * kBrW;
   const int q_last = min(q_lo + kBrW, N) - 1;              // last real query row of the workgroup
-  const int n_tiles = CAUSAL ? (q_last / kBc + 1) : (N + kBc - 1) / kBc;
+  const int n_tiles = CAUSAL ? (q_last / kBcT + 1) : (N + kBcT - 1) / kBcT;
   const int q0w = q_lo + wave * kRowsPerWave;               // first query row of this wave
   const int my_q = q0w + l32;                               // query row of this lane
   // Tiles j < wave_tiles hold at least one key visible to this wave's rows.
   const int wave_tiles =
-      (q0w >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kRowsPerWave - 1) / kBc + 1) : n_tiles);
+      (q0w >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kRowsPerWave - 1) / kBcT + 1) : n_tiles);
 
   // ---- Q fragments: lane holds q[my_q][16*kb + 8*h .. +7] (B operand of S^T = K Q^T)
   bf16x8 qf[kDB];
@@ -217,14 +222,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   auto copy_tile = [&](int j, auto stc) __attribute__((always_inline)) {
     constexpr int S = decltype(stc)::value;
-    const int bytes = min(N - j * kBc, kBc) * T::RB;   // rows past N arrive as zeros
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (size_t)j * kBc * D, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (size_t)j * kBc * D, bytes);
 #pragma unroll
-    for (int p = 0; p < kCopies; ++p) {
-      const int dst = (wave + NW * p) * 1024;
-      lds_copy16_inline(kr, kst + S * T::kBytes + dst, dma_k[p]);
-      lds_copy16_inline(vr, vst + S * T::kBytes + dst, dma_v[p]);
+    for (int t = 0; t < KT; ++t) {
+      const int row0 = j * kBcT + t * kBc;
+      const int bytes = max(0, min(N - row0, kBc)) * T::RB;   // rows past N arrive as zeros
+      const size_t base = (size_t)min(row0, N - 1) * D;
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + base, bytes);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + base, bytes);
+#pragma unroll
+      for (int p = 0; p < kCopies; ++p) {
+        const int dst = S * kStage + t * T::kBytes + (wave + NW * p) * 1024;
+        lds_copy16_inline(kr, kst + dst, dma_k[p]);
+        lds_copy16_inline(vr, vst + dst, dma_v[p]);
+      }
     }
   };
 
@@ -254,18 +264,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   auto compute_tile = [&](int j, auto stc) __attribute__((always_inline)) {
     constexpr int S = decltype(stc)::value;
-    const int kv0 = j * kBc;
-    const lds_char* ks = kst + S * T::kBytes;
-    const lds_char* vs = vst + S * T::kBytes;
+    const int kv0 = j * kBcT;
+    const lds_char* ks = kst + S * kStage;
+    const lds_char* vs = vst + S * kStage;
 
-    // ---- S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks)
-    f32x16 s[2];
+    // ---- S^T = K Q^T for keys kv0 .. kv0 + 64KT - 1 (2KT blocks of 32 keys; block b = rows 32(b%2).. of part b/2)
+    f32x16 s[2 * KT];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2 * KT; ++b) {
       s[b] = (f32x16){};
 #pragma unroll
       for (int kb = 0; kb < kDB; ++kb) {
-        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(ks + k_off[kb] + 32 * b * T::RB);
+        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(ks + (b >> 1) * T::kBytes + k_off[kb] +
+                                                                             32 * (b & 1) * T::RB);
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s[b], 0, 0, 0);
       }
     }
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // then one MFMA per further read, so each K fragment is read ~4 MFMAs before it is used.
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * kDB - 4; ++i) {
+    for (int i = 0; i < 2 * KT * kDB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -281,10 +292,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // s[b][r] is the score of query my_q and key kv0 + 32b + 16(r/8) + 8h + r%8.
 
     // ---- mask (only tiles that cross the diagonal or the end of the sequence)
-    const bool need_mask = (kv0 + kBc > N) || (CAUSAL && kv0 + kBc - 1 > q0w);
+    const bool need_mask = (kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w);
     if (need_mask) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2 * KT; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
@@ -296,10 +307,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // ---- online softmax statistics
     float mx = s[0][0];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2 * KT; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-    mx = pair_max32(mx);  // row max over this tile's 64 keys
+    mx = pair_max32(mx);  // row max over this tile's keys
     const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c2 > kRescaleLog2);
     if (__any(grow)) {
       const float m_new = fmaxf(m_ref, mx);
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     auto read_v = [&](int m, bf16x8(&vf)[kCB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const lds_char* va = vs + v_off[cb] + 16 * m * T::RB;
+        const lds_char* va = vs + (m >> 2) * T::kBytes + v_off[cb] + 16 * (m & 3) * T::RB;
         const bf16x4 v0 =
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va));
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bf16x8 vfa[kCB], vfb[kCB];
     read_v(0, vfa);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 4 * KT; ++m) {
       bf16x8(&vcur)[kCB] = (m & 1) ? vfb : vfa;
       bf16x8(&vnxt)[kCB] = (m & 1) ? vfa : vfb;
       f32x8 x = (m & 1) ? s[m >> 1].hi : s[m >> 1].lo;
@@ -343,7 +354,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       rs[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), kOnes2, rs[1], false);
       rs[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, rs[0], false);
       rs[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, rs[1], false);
-      if (m < 3) read_v(m + 1, vnxt);
+      if (m < 4 * KT - 1) read_v(m + 1, vnxt);
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[cb], pf, oacc[cb], 0, 0, 0);
     }
@@ -358,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (issue) copy_tile(j + ST - 1, Int<(S + ST - 1) % ST>{});
     if (j < wave_tiles) compute_tile(j, stc);
     if (ST == 3 && issue) {
-      wait_copies_and_barrier<2 * kCopies>();  // tile j+2's copies may stay in flight
+      wait_copies_and_barrier<kWaitKeep>();  // tile j+2's copies may stay in flight
     } else {
       wait_copies_and_barrier<0>();
     }
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   copy_tile(0, Int<0>{});
   if (ST == 3 && n_tiles > 1) {
     copy_tile(1, Int<1>{});
-    wait_copies_and_barrier<2 * kCopies>();
+    wait_copies_and_barrier<kWaitKeep>();
   } else {
     wait_copies_and_barrier<0>();
   }
@@ -547,12 +558,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(const float* __res
 // ------------------------------------------------------------------------------------------------------------
 // launchers (arguments already validated by the C ABI layer)
 // ------------------------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, int NW, int ST>
+template <int D, bool CAUSAL, int NW, int ST, int KT>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                               float scale, hipStream_t stream) {
-  constexpr int lds = 2 * ST * Tile<D>::kBytes;
+  constexpr int lds = 2 * ST * KT * Tile<D>::kBytes;
   constexpr int rows = NW * kRowsPerWave;
-  auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST>;
+  auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST, KT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)BH);
@@ -573,25 +584,34 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
   return hipGetLastError();
 }
 
-// Workgroup shape: 8 waves (256 rows, one workgroup per CU, 3-stage ring) when the grid has at least two such
-// workgroups per CU of an MI355X (256 CUs); otherwise 4 waves (128 rows, two workgroups per CU, 2-stage ring),
-// which doubles the workgroups of short sequences. Each row's arithmetic is the same in both, so the choice does
-// not change any output bit.
+// Workgroup shape: 8 waves (256 rows, one workgroup per CU, 128-key tiles, 2-stage ring) when the grid has at
+// least two such workgroups per CU of an MI355X (256 CUs); otherwise 4 waves (128 rows, two workgroups per CU,
+// 64-key tiles, 2-stage ring), which doubles the workgroups of short sequences. The two differ in where the
+// exponent reference may move and in the order of the row sums, so their outputs can differ in the last bit;
+// each is deterministic.
 constexpr long long kWideGridMin = 512;
+#ifndef FA_WIDE_ST
+#define FA_WIDE_ST 2
+#define FA_WIDE_KT 2
+#endif
+#define WIDE64T launch_bf16<64, true, 8, FA_WIDE_ST, FA_WIDE_KT>
+#define WIDE64F launch_bf16<64, false, 8, FA_WIDE_ST, FA_WIDE_KT>
+#define WIDE128T launch_bf16<128, true, 8, FA_WIDE_ST, FA_WIDE_KT>
+#define WIDE128F launch_bf16<128, false, 8, FA_WIDE_ST, FA_WIDE_KT>
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            bool causal, float scale, hipStream_t stream) {
   const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
   if (wide) {
-    if (d == 64) return causal ? launch_bf16<64, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
-                               : launch_bf16<64, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
-    return causal ? launch_bf16<128, true, 8, 3>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_bf16<128, false, 8, 3>(q, k, v, o, lse, BH, N, scale, stream);
+    if (d == 64) return causal ? WIDE64T(q, k, v, o, lse, BH, N, scale, stream)
+                               : WIDE64F(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? WIDE128T(q, k, v, o, lse, BH, N, scale, stream)
+                  : WIDE128F(q, k, v, o, lse, BH, N, scale, stream);
   }
-  if (d == 64) return causal ? launch_bf16<64, true, 4, 2>(q, k, v, o, lse, BH, N, scale, stream)
-                             : launch_bf16<64, false, 4, 2>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_bf16<128, true, 4, 2>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_bf16<128, false, 4, 2>(q, k, v, o, lse, BH, N, scale, stream);
+  if (d == 64) return causal ? launch_bf16<64, true, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream)
+                             : launch_bf16<64, false, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? launch_bf16<128, true, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream)
+                : launch_bf16<128, false, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
