@@ -154,7 +154,8 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
 }
 
 // bf16 kernel: NW waves x 32 query rows per workgroup, K/V tiles of KT x 64 keys (each 64-key part is one
-// swizzled Tile in LDS), ST-stage pipeline in LDS.
+// swizzled Tile in LDS), ST-stage ring holding K and V of the same tile; every wave runs S_j, softmax,
+// O += P_j V_j.
 template <int D, bool CAUSAL, int NW, int ST, int KT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -220,23 +221,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     dma_k[p] = row * T::RB + (phys ^ T::swz_k(row)) * 16;
     dma_v[p] = row * T::RB + (phys ^ T::swz_v(row)) * 16;
   }
-  auto copy_tile = [&](int j, auto stc) __attribute__((always_inline)) {
-    constexpr int S = decltype(stc)::value;
+  // Copy tile j of K (or V) into the stage starting `at` bytes into the K (or V) ring.
+  auto copy_part = [&](const __bf16* src, lds_char* ring, int j, int at, const int(&dma)[kCopies])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       const int row0 = j * kBcT + t * kBc;
-      const int bytes = max(0, min(N - row0, kBc)) * T::RB;   // rows past N arrive as zeros
-      const size_t base = (size_t)min(row0, N - 1) * D;
-      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + base, bytes);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + base, bytes);
+      // rows past N arrive as zeros. (The clamp would compile to a vector instruction; readfirstlane keeps the
+      // descriptor in scalar registers, otherwise every copy is wrapped in a loop over distinct descriptors.)
+      const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kBc)) * T::RB);
+      const int row_base = __builtin_amdgcn_readfirstlane(min(row0, N - 1));
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * D, bytes);
 #pragma unroll
-      for (int p = 0; p < kCopies; ++p) {
-        const int dst = S * kStage + t * T::kBytes + (wave + NW * p) * 1024;
-        lds_copy16_inline(kr, kst + dst, dma_k[p]);
-        lds_copy16_inline(vr, vst + dst, dma_v[p]);
-      }
+      for (int p = 0; p < kCopies; ++p)
+        lds_copy16_inline(r, ring + at + t * T::kBytes + (wave + NW * p) * 1024, dma[p]);
     }
   };
+  auto copy_k = [&](int j, int at) __attribute__((always_inline)) { copy_part(kh, kst, j, at, dma_k); };
+  auto copy_v = [&](int j, int at) __attribute__((always_inline)) { copy_part(vh, vst, j, at, dma_v); };
 
   // ---- this lane's LDS read offsets (stage 0)
   // K: row 32b + krow (krow = l32 with bits 2 and 3 swapped, see the header), chunk 2kb + h. swz_k depends only
@@ -262,14 +264,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) oacc[cb] = (f32x16){};
 
-  auto compute_tile = [&](int j, auto stc) __attribute__((always_inline)) {
-    constexpr int S = decltype(stc)::value;
-    const int kv0 = j * kBcT;
-    const lds_char* ks = kst + S * kStage;
-    const lds_char* vs = vst + S * kStage;
-
-    // ---- S^T = K Q^T for keys kv0 .. kv0 + 64KT - 1 (2KT blocks of 32 keys; block b = rows 32(b%2).. of part b/2)
-    f32x16 s[2 * KT];
+  // S^T = K_j Q^T from the K stage at byte `kat` (2KT blocks of 32 keys; block b = rows 32(b%2).. of part b/2).
+  // s[b][r] is the score of query my_q and key j*64KT + 32b + 16(r/8) + 8h + r%8.
+  auto qk = [&](f32x16(&s)[2 * KT], int kat) __attribute__((always_inline)) {
+    const lds_char* ks = kst + kat;
 #pragma unroll
     for (int b = 0; b < 2 * KT; ++b) {
       s[b] = (f32x16){};
@@ -289,11 +287,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    // s[b][r] is the score of query my_q and key kv0 + 32b + 16(r/8) + 8h + r%8.
+  };
 
-    // ---- mask (only tiles that cross the diagonal or the end of the sequence)
-    const bool need_mask = (kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w);
-    if (need_mask) {
+  // Mask (only tiles that cross the diagonal or the end of the sequence), row max and (rarely) the move of the
+  // exponent reference, for tile j held in s.
+  auto stats = [&](f32x16(&s)[2 * KT], int j) __attribute__((always_inline)) {
+    const int kv0 = j * kBcT;
+    if ((kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
 #pragma unroll
       for (int b = 0; b < 2 * KT; ++b)
 #pragma unroll
@@ -303,8 +303,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           s[b][r] = vis ? s[b][r] : -INFINITY;
         }
     }
-
-    // ---- online softmax statistics
     float mx = s[0][0];
 #pragma unroll
     for (int b = 0; b < 2 * KT; ++b)
@@ -321,12 +319,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int cb = 0; cb < kCB; ++cb) oacc[cb] *= alpha;
       m_ref = m_use;
     }
+  };
+
+  // P = exp2(s*c2 - m_ref*c2) and O^T += V^T P^T from the V stage at byte `vat`, one 16-key step m at a time:
+  // the 8 exponentials of step m+1 can run on the vector ALU while the MFMAs of step m run, and the V fragments
+  // of step m+1 are read during step m. Lane slot 8h+e of step m <-> key j*64KT + 16m + 8h + e.
+  auto softmax_pv = [&](f32x16(&s)[2 * KT], int vat) __attribute__((always_inline)) {
+    const lds_char* vs = vst + vat;
     const float nb = -m_ref * c2;
     float rs[2] = {0.f, 0.f};
-
-    // ---- P and O^T += V^T P^T, one 16-key step m at a time: the 8 exponentials of step m+1 can run on the
-    // vector ALU while the MFMAs of step m run, and the V fragments of step m+1 are read during step m.
-    // Lane slot 8h+e of step m <-> key kv0 + 16m + 8h + e.
     auto read_v = [&](int m, bf16x8(&vf)[kCB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
@@ -356,38 +357,50 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       rs[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, rs[1], false);
       if (m < 4 * KT - 1) read_v(m + 1, vnxt);
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[cb], pf, oacc[cb], 0, 0, 0);
+      for (int cb = 0; cb < kCB; ++cb)
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[cb], pf, oacc[cb], 0, 0, 0);
     }
     l_run += rs[0] + rs[1];
   };
 
-  // One tile: start copying tile j+ST-1 into the stage tile j-1 used (every wave finished it before the last
-  // barrier), compute tile j, wait for this wave's copies of tile j+1, barrier.
-  auto step = [&](int j, auto stc) __attribute__((always_inline)) {
-    constexpr int S = decltype(stc)::value;
-    const bool issue = j + ST - 1 < n_tiles;
-    if (issue) copy_tile(j + ST - 1, Int<(S + ST - 1) % ST>{});
-    if (j < wave_tiles) compute_tile(j, stc);
-    if (ST == 3 && issue) {
-      wait_copies_and_barrier<kWaitKeep>();  // tile j+2's copies may stay in flight
+  f32x16 s[2 * KT];
+  {
+    // One tile: start copying tile j+ST-1 into the stage tile j-1 used (every wave finished it before the last
+    // barrier), compute tile j, wait for this wave's copies of tile j+1, barrier.
+    auto step = [&](int j, auto stc) __attribute__((always_inline)) {
+      constexpr int S = decltype(stc)::value;
+      const bool issue = j + ST - 1 < n_tiles;
+      if (issue) {
+        copy_k(j + ST - 1, ((S + ST - 1) % ST) * kStage);
+        copy_v(j + ST - 1, ((S + ST - 1) % ST) * kStage);
+      }
+      if (j < wave_tiles) {
+        qk(s, S * kStage);
+        stats(s, j);
+        softmax_pv(s, S * kStage);
+      }
+      if (ST == 3 && issue) {
+        wait_copies_and_barrier<kWaitKeep>();  // tile j+2's copies may stay in flight
+      } else {
+        wait_copies_and_barrier<0>();
+      }
+    };
+    // prologue: tiles 0 .. ST-2 into stages 0 .. ST-2
+    copy_k(0, 0);
+    copy_v(0, 0);
+    if (ST == 3 && n_tiles > 1) {
+      copy_k(1, kStage);
+      copy_v(1, kStage);
+      wait_copies_and_barrier<kWaitKeep>();
     } else {
       wait_copies_and_barrier<0>();
     }
-  };
-
-  // prologue: tiles 0 .. ST-2 into stages 0 .. ST-2
-  copy_tile(0, Int<0>{});
-  if (ST == 3 && n_tiles > 1) {
-    copy_tile(1, Int<1>{});
-    wait_copies_and_barrier<kWaitKeep>();
-  } else {
-    wait_copies_and_barrier<0>();
-  }
-  for (int j = 0; j < n_tiles; j += ST) {
-    step(j, Int<0>{});
-    if (j + 1 < n_tiles) step(j + 1, Int<1>{});
-    if constexpr (ST == 3) {
-      if (j + 2 < n_tiles) step(j + 2, Int<2>{});
+    for (int j = 0; j < n_tiles; j += ST) {
+      step(j, Int<0>{});
+      if (j + 1 < n_tiles) step(j + 1, Int<1>{});
+      if constexpr (ST == 3) {
+        if (j + 2 < n_tiles) step(j + 2, Int<2>{});
+      }
     }
   }
 
@@ -590,23 +603,15 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
 // exponent reference may move and in the order of the row sums, so their outputs can differ in the last bit;
 // each is deterministic.
 constexpr long long kWideGridMin = 512;
-#ifndef FA_WIDE_ST
-#define FA_WIDE_ST 2
-#define FA_WIDE_KT 2
-#endif
-#define WIDE64T launch_bf16<64, true, 8, FA_WIDE_ST, FA_WIDE_KT>
-#define WIDE64F launch_bf16<64, false, 8, FA_WIDE_ST, FA_WIDE_KT>
-#define WIDE128T launch_bf16<128, true, 8, FA_WIDE_ST, FA_WIDE_KT>
-#define WIDE128F launch_bf16<128, false, 8, FA_WIDE_ST, FA_WIDE_KT>
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                            bool causal, float scale, hipStream_t stream) {
   const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
   if (wide) {
-    if (d == 64) return causal ? WIDE64T(q, k, v, o, lse, BH, N, scale, stream)
-                               : WIDE64F(q, k, v, o, lse, BH, N, scale, stream);
-    return causal ? WIDE128T(q, k, v, o, lse, BH, N, scale, stream)
-                  : WIDE128F(q, k, v, o, lse, BH, N, scale, stream);
+    if (d == 64) return causal ? launch_bf16<64, true, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream)
+                               : launch_bf16<64, false, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_bf16<128, true, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream)
+                  : launch_bf16<128, false, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream);
   }
   if (d == 64) return causal ? launch_bf16<64, true, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream)
                              : launch_bf16<64, false, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream);
