@@ -45,11 +45,11 @@ def _load():
         if not _LIB.exists():
             build(force=False)
         lib = ctypes.CDLL(str(_LIB))
-        f = lib.oracle_attn_rows
+        f = lib.oracle_attn_rows_ex
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                      ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_int,
-                      ctypes.c_double,
+                      ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                      ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
                       ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         _lib = lib
     return _lib
@@ -76,19 +76,28 @@ def _as_f32(x) -> np.ndarray:
     return np.ascontiguousarray(a)
 
 
-def attention_rows(q, k, v, causal: bool, scale: float, rows=None, threads: int | None = None):
+def attention_rows(q, k, v, causal: bool, scale: float, rows=None, threads: int | None = None, kv_len=None):
     """Oracle output for the listed flat rows (b*H + h)*Nq + i (None: every row, in order).
 
-    q: [B, H, Nq, d], k and v: [B, H, Nk, d], bf16/fp32 (torch CPU tensors or fp32 arrays).
+    q: [B, H, Nq, d], k and v: [B, Hkv, Nk, d], bf16/fp32 (torch CPU tensors or fp32 arrays).
+    Hkv divides H; query head h reads key/value head h // (H // Hkv) (grouped/multi-query attention).
     The attention problems have Nq == Nk; key blocks (Nk < Nq) serve the merge pins.
     scale: the fp32 scale handed to the GPU; the oracle uses exactly that value.
-    Returns (o [n_rows, d] float64, lse [n_rows] float64).
+    kv_len: None, or B valid-key counts in [0, Nk] (key-padding mask: keys j >= kv_len[b] are masked).
+    Returns (o [n_rows, d] float64, lse [n_rows] float64); a row with no visible key has o = 0, lse = -inf.
     """
     qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
-    if qa.ndim != 4 or ka.shape != va.shape or qa.shape[:2] != ka.shape[:2] or qa.shape[3] != ka.shape[3]:
-        raise ValueError(f"q [B,H,Nq,d] and k, v [B,H,Nk,d] shapes disagree: {qa.shape} {ka.shape} {va.shape}")
+    if (qa.ndim != 4 or ka.ndim != 4 or ka.shape != va.shape or qa.shape[0] != ka.shape[0]
+            or qa.shape[3] != ka.shape[3] or ka.shape[1] < 1 or qa.shape[1] % ka.shape[1] != 0):
+        raise ValueError(f"q [B,H,Nq,d] and k, v [B,Hkv,Nk,d] shapes disagree: {qa.shape} {ka.shape} {va.shape}")
     B, H, N, d = qa.shape
-    Nk = ka.shape[2]
+    Hkv, Nk = ka.shape[1], ka.shape[2]
+    if kv_len is None:
+        len_arr = None
+    else:
+        len_arr = np.ascontiguousarray(np.asarray(kv_len, dtype=np.int64).reshape(-1))
+        if len_arr.size != B or (len_arr < 0).any() or (len_arr > Nk).any():
+            raise ValueError(f"kv_len must hold {B} counts in [0, {Nk}], got {len_arr}")
     sc = float(np.float32(scale))
     if rows is None:
         n = B * H * N
@@ -100,16 +109,17 @@ def attention_rows(q, k, v, causal: bool, scale: float, rows=None, threads: int 
     lse = np.zeros((n,), dtype=np.float64)
     if n == 0:
         return o, lse
-    rc = _load().oracle_attn_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, B, H, N, Nk, d, int(bool(causal)), sc,
-                                  None if rows_arr is None else rows_arr.ctypes.data, n, o.ctypes.data,
-                                  lse.ctypes.data, int(threads or default_threads()))
+    rc = _load().oracle_attn_rows_ex(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, B, H, Hkv, N, Nk, d,
+                                     int(bool(causal)), sc, None if len_arr is None else len_arr.ctypes.data,
+                                     None if rows_arr is None else rows_arr.ctypes.data, n, o.ctypes.data,
+                                     lse.ctypes.data, int(threads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_rows failed with code {rc}")
     return o, lse
 
 
-def attention(q, k, v, causal: bool, scale: float, threads: int | None = None):
+def attention(q, k, v, causal: bool, scale: float, threads: int | None = None, kv_len=None):
     """Oracle output for every row: (o [B,H,N,d] float64, lse [B,H,N] float64)."""
     B, H, N, d = tuple(q.shape)
-    o, lse = attention_rows(q, k, v, causal, scale, None, threads)
+    o, lse = attention_rows(q, k, v, causal, scale, None, threads, kv_len)
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)

@@ -10,13 +10,29 @@
  * opening code block and in "The Math Behind Flash Attention", item 1 (softmax
  * with the row maximum subtracted): for every batch b, head h and query row i,
  *
- *   s_ij   = scale * sum_c q[b,h,i,c] * k[b,h,j,c]      for j in J_i
- *   J_i    = {0..Nk-1}, or {0..min(i, Nk-1)} when causal (key j visible iff j <= i)
+ *   s_ij   = scale * sum_c q[b,h,i,c] * k[b,g,j,c]      for j in J_i
+ *   J_i    = {j : j < L_b}, and j <= i as well when causal
  *   m_i    = max_{j in J_i} s_ij
  *   l_i    = sum_{j in J_i} exp(s_ij - m_i)
  *   p_ij   = exp(s_ij - m_i) / l_i          (0 for j outside J_i)
- *   o_ic   = sum_j p_ij * v[b,h,j,c]
+ *   o_ic   = sum_j p_ij * v[b,g,j,c]
  *   lse_i  = m_i + ln(l_i)
+ * and, when J_i is empty (only possible with L_b = 0), o_i = 0 and lse_i = -inf
+ * (the log of an empty sum).
+ *
+ * g is the key/value head of query head h. With as many key/value heads as
+ * query heads (Hkv = H) g = h; with fewer (grouped-query attention, Hkv
+ * dividing H; multi-query attention, Hkv = 1) the H/Hkv consecutive query heads
+ * h of a group share head g = h / (H/Hkv). The unite.ai page lists grouped and
+ * multi-query attention among the FlashAttention-2 improvements (section
+ * "FlashAttention-2", item 3) without defining the grouping; consecutive
+ * grouping is a reading.
+ *
+ * L_b is the number of valid keys of batch b (a key-padding mask whose valid
+ * keys are a prefix, as right padding makes): keys j >= L_b are invisible to
+ * every query of that batch. Without lengths L_b = Nk. The mask itself appears
+ * only as a usage example (triton-transformer README, "ex. BERT": a boolean
+ * (batch, seq) mask passed to the model); the prefix form is a reading.
  *
  * The causal rule j <= i is a reading: the pages only say "causal" and
  * "triangular" (triton-transformer README, usage and to-do list). lse is the
@@ -38,9 +54,10 @@
 
 typedef struct {
     const float *q, *k, *v;
-    long B, H, Nq, Nk, d;
+    long B, H, Hkv, Nq, Nk, d;
     int causal;
     double scale;
+    const long *kv_len; /* NULL: every batch has Nk valid keys */
     const long *rows; /* NULL: row r of the output is flat row r */
     long n_rows;
     double *o, *lse;
@@ -52,10 +69,20 @@ typedef struct {
 static int one_row(const job_t *J, long fr, double *s, double *o_out, double *lse_out) {
     const long Nq = J->Nq, Nk = J->Nk, d = J->d;
     const long bh = fr / Nq, i = fr % Nq;
+    const long b = bh / J->H, h = bh % J->H;
+    const long g = h / (J->H / J->Hkv); /* key/value head of query head h */
     const float *qi = J->q + fr * d;
-    const float *kh = J->k + bh * Nk * d;
-    const float *vh = J->v + bh * Nk * d;
-    const long nvis = (J->causal && i + 1 < Nk) ? i + 1 : Nk; /* |J_i| */
+    const float *kh = J->k + (b * J->Hkv + g) * Nk * d;
+    const float *vh = J->v + (b * J->Hkv + g) * Nk * d;
+    /* J_i = {0 .. nvis-1}: keys below L_b, and up to i when causal */
+    long nvis = J->kv_len ? J->kv_len[b] : Nk;
+    if (J->causal && i + 1 < nvis) nvis = i + 1;
+
+    if (nvis == 0) { /* empty softmax */
+        for (long c = 0; c < d; ++c) o_out[c] = 0.0;
+        *lse_out = -INFINITY;
+        return 0;
+    }
 
     /* s_ij for every visible key */
     for (long j = 0; j < nvis; ++j) {
@@ -102,19 +129,26 @@ static void *worker(void *arg) {
 }
 
 /*
- * oracle_attn_rows: attention forward for a list of query rows.
- *   q       : [B, H, Nq, d] fp32, contiguous;  k, v : [B, H, Nk, d] fp32, contiguous
+ * oracle_attn_rows_ex: attention forward for a list of query rows.
+ *   q       : [B, H, Nq, d] fp32, contiguous;  k, v : [B, Hkv, Nk, d] fp32, contiguous
  *             (the attention problems of interest have Nq == Nk; Nq != Nk serves the key-block tests)
+ *   Hkv     : key/value heads, dividing H (query head h reads key/value head h / (H / Hkv))
  *   causal  : key j visible to query i iff j <= i
+ *   kv_len  : B valid-key counts in [0, Nk] (keys j >= kv_len[b] are masked), or NULL (all Nk keys valid)
  *   rows    : n_rows flat row ids (b*H + h)*Nq + i, or NULL for all B*H*Nq rows in order
  *   o       : [n_rows, d] fp64 out;  lse : [n_rows] fp64 out
  *   threads : worker threads (>= 1)
  * Returns 0 on success, 1 on a bad argument, 2 when memory runs out.
  */
-int oracle_attn_rows(const float *q, const float *k, const float *v, long B, long H, long Nq, long Nk, long d,
-                     int causal, double scale, const long *rows, long n_rows, double *o, double *lse, int threads) {
+int oracle_attn_rows_ex(const float *q, const float *k, const float *v, long B, long H, long Hkv, long Nq, long Nk,
+                        long d, int causal, double scale, const long *kv_len, const long *rows, long n_rows,
+                        double *o, double *lse, int threads) {
     if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || n_rows < 0 || threads < 1)
         return 1;
+    if (Hkv < 1 || H % Hkv != 0) return 1;
+    if (kv_len)
+        for (long b = 0; b < B; ++b)
+            if (kv_len[b] < 0 || kv_len[b] > Nk) return 1;
     if (!rows && n_rows != B * H * Nq) return 1;
     if (rows)
         for (long r = 0; r < n_rows; ++r)
@@ -129,7 +163,7 @@ int oracle_attn_rows(const float *q, const float *k, const float *v, long B, lon
         return 2;
     }
     for (int t = 0; t < threads; ++t) {
-        job_t j = {q, k, v, B, H, Nq, Nk, d, causal, scale, rows, n_rows, o, lse, t, threads, 0};
+        job_t j = {q, k, v, B, H, Hkv, Nq, Nk, d, causal, scale, kv_len, rows, n_rows, o, lse, t, threads, 0};
         jobs[t] = j;
     }
     int rc = 0;
@@ -148,4 +182,10 @@ int oracle_attn_rows(const float *q, const float *k, const float *v, long B, lon
     free(jobs);
     free(tids);
     return rc;
+}
+
+/* oracle_attn_rows: oracle_attn_rows_ex with one key/value head per query head and no key-padding mask. */
+int oracle_attn_rows(const float *q, const float *k, const float *v, long B, long H, long Nq, long Nk, long d,
+                     int causal, double scale, const long *rows, long n_rows, double *o, double *lse, int threads) {
+    return oracle_attn_rows_ex(q, k, v, B, H, H, Nq, Nk, d, causal, scale, NULL, rows, n_rows, o, lse, threads);
 }
