@@ -6,7 +6,8 @@ samples; it contains none of the attention arithmetic.
 
 Recipe (one workload = B, H, N, d, causal, dtype, seed):
   g = torch.Generator('cpu').manual_seed(seed)
-  q, k, v = torch.randn((B, H, N, d), generator=g, dtype=float32), in that order
+  q = torch.randn((B, H, N, d), generator=g, dtype=float32), then k and v likewise with shape
+  (B, Hkv, N, d) (Hkv = H unless the workload has grouped key/value heads), in that order
   k *= k_scale        (3.0 for the peaked-softmax workload, in fp32, before rounding)
   round to bf16 with round-to-nearest-even (fp32 workloads stay fp32)
 Layout is [B, H, N, d], contiguous, row-major. The default softmax scale is
@@ -36,26 +37,43 @@ class Workload:
     seed: int
     k_scale: float = 1.0
     sampled_rows: int = 0   # 0: every row is checked; else rows sampled per check
+    Hkv: int = 0            # key/value heads (grouped-query attention); 0: same as H
+    kv_len: tuple = ()      # per-batch valid-key counts (key padding); (): every key valid
+
+    @property
+    def Hk(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
         return default_scale(self.d)
 
+    def _pairs(self, L: int) -> float:
+        """Visible (query, key) pairs of one head with L valid keys, in the metric's convention: N*L, or for
+        causal L^2/2 (the triangle, counted as the metric counts N^2/2) plus (N - L)*L (the rows past it)."""
+        return L * L / 2 + (self.N - L) * L if self.causal else float(self.N * L)
+
     @property
     def flops(self) -> float:
-        """Attention-forward FLOPs as the metric counts them: 4*B*H*N^2*d, halved when causal."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
-        return f / 2 if self.causal else f
+        """Attention-forward FLOPs as the metric counts them: 4*B*H*N^2*d, halved when causal; with key padding
+        4*H*d times the visible pairs of every batch."""
+        lens = self.kv_len or (self.N,) * self.B
+        return 4.0 * self.H * self.d * sum(self._pairs(L) for L in lens)
 
     @property
     def elt_bytes(self) -> int:
         return 2 if self.dtype == "bf16" else 4
 
     @property
+    def kv_rows(self) -> int:
+        """Key/value rows the kernel must read: B*Hkv*N, or only the valid ones with key padding."""
+        return self.Hk * (sum(self.kv_len) if self.kv_len else self.B * self.N)
+
+    @property
     def algorithmic_bytes(self) -> int:
-        """Q, K, V read once; O written once (input dtype); lse written once (fp32)."""
+        """Q read once, valid K and V rows read once, O written once (input dtype); lse written once (fp32)."""
         n = self.B * self.H * self.N
-        return 4 * n * self.d * self.elt_bytes + 4 * n
+        return (2 * n + 2 * self.kv_rows) * self.d * self.elt_bytes + 4 * n
 
 
 # The workloads: seed = workload number; C2 has a causal and a non-causal variant.
@@ -68,6 +86,16 @@ WORKLOADS = {
                                                sampled_rows=256),
     "c5_bf16_b1h8n32768d64_causal_k3": Workload("c5_bf16_b1h8n32768d64_causal_k3", 1, 8, 32768, 64, True, "bf16", 5,
                                                 k_scale=3.0, sampled_rows=256),
+    # Grouped-query attention (8 key/value heads for 32 query heads) at the headline sequence length, and
+    # multi-query attention (1 for 32) at the long causal one.
+    "gqa_bf16_b2h32kv8n4096d128": Workload("gqa_bf16_b2h32kv8n4096d128", 2, 32, 4096, 128, False, "bf16", 6,
+                                           sampled_rows=256, Hkv=8),
+    "mqa_bf16_b1h32kv1n16384d128_causal": Workload("mqa_bf16_b1h32kv1n16384d128_causal", 1, 32, 16384, 128, True,
+                                                   "bf16", 7, sampled_rows=256, Hkv=1),
+    # Key padding: 8 right-padded sequences of mixed lengths in a batch padded to N = 4096 (encoder-style,
+    # non-causal, as in the boolean-mask usage example of the triton-transformer README).
+    "kpad_bf16_b8h16n4096d128": Workload("kpad_bf16_b8h16n4096d128", 8, 16, 4096, 128, False, "bf16", 8,
+                                         sampled_rows=256, kv_len=(4096, 3001, 2500, 4000, 1234, 777, 3333, 2048)),
 }
 
 
@@ -76,13 +104,15 @@ def default_scale(d: int) -> float:
     return float(np.float32(1.0 / math.sqrt(d)))
 
 
-def make_qkv(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16", k_scale: float = 1.0):
-    """Draw q, k, v ~ N(0, 1) in fp32 (CPU generator), scale k, round to dtype. Returns CPU tensors."""
+def make_qkv(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16", k_scale: float = 1.0,
+             Hkv: int | None = None):
+    """Draw q [B,H,N,d] and k, v [B,Hkv,N,d] ~ N(0, 1) in fp32 (CPU generator), scale k, round to dtype.
+    Returns CPU tensors. Hkv defaults to H."""
     g = torch.Generator("cpu").manual_seed(int(seed))
-    shape = (B, H, N, d)
-    q = torch.randn(shape, generator=g, dtype=torch.float32)
-    k = torch.randn(shape, generator=g, dtype=torch.float32)
-    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    kv_shape = (B, Hkv or H, N, d)
+    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn(kv_shape, generator=g, dtype=torch.float32)
+    v = torch.randn(kv_shape, generator=g, dtype=torch.float32)
     if k_scale != 1.0:
         k = k * float(k_scale)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
@@ -90,7 +120,12 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16", k_s
 
 
 def make_workload(w: Workload):
-    return make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype, w.k_scale)
+    return make_qkv(w.B, w.H, w.N, w.d, w.seed, w.dtype, w.k_scale, w.Hkv or None)
+
+
+def kv_len_of(w: Workload):
+    """The workload's per-batch valid-key counts as a list, or None without key padding."""
+    return list(w.kv_len) if w.kv_len else None
 
 
 def sample_rows(B: int, H: int, N: int, n: int, seed: int) -> np.ndarray:

@@ -62,7 +62,7 @@ def kernel_name(w) -> str:
     if w.dtype != "bf16":
         return f"fa_fwd_f32_kernel<{w.d}, {c}>"
     wide = ((w.N + 255) // 256) * w.B * w.H >= 512
-    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {8 if wide else 4}, {3 if wide else 2}>"
+    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {'8, 2, 2' if wide else '4, 2, 1'}>"
 
 
 def _device_inputs(w):
@@ -73,15 +73,23 @@ def _device_inputs(w):
     q, k, v = q.cuda(), k.cuda(), v.cuda()
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-    return q, k, v, o, lse
+    lens = torch.tensor(w.kv_len, dtype=torch.int32, device="cuda") if w.kv_len else None
+    return q, k, v, o, lse, lens
 
 
-def _caller(w, q, k, v, o, lse, stream_handle):
+def _caller(w, q, k, v, o, lse, lens, stream_handle):
+    """One raw C-ABI call for workload w: fa_fwd, fa_fwd_gqa (fewer key/value heads), fa_fwd_kpad (key
+    padding) or fa_fwd_f32."""
     import exact_attention_13_amd as fa
 
-    fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.d,
-            int(w.causal), w.scale, stream_handle)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    tail = (w.N, w.d, int(w.causal), w.scale, stream_handle)
+    if lens is not None:
+        fn, args = fa.fa_fwd_kpad, ptrs + (lens.data_ptr(), w.B, w.H, w.Hk) + tail
+    elif w.Hk != w.H:
+        fn, args = fa.fa_fwd_gqa, ptrs + (w.B, w.H, w.Hk) + tail
+    else:
+        fn, args = (fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32), ptrs + (w.B, w.H) + tail
 
     def call():
         rc = fn(*args)
@@ -94,9 +102,9 @@ def time_workload(w, steps: int, warmup: int):
     """Returns (wall_s for `steps` calls, per-launch durations in ms from HIP events on the launch stream)."""
     import torch
 
-    q, k, v, o, lse = _device_inputs(w)
+    q, k, v, o, lse, lens = _device_inputs(w)
     stream = torch.cuda.current_stream()
-    call = _caller(w, q, k, v, o, lse, stream.cuda_stream)
+    call = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
     for _ in range(warmup):
         call()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -110,7 +118,7 @@ def time_workload(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    del q, k, v, o, lse
+    del q, k, v, o, lse, lens
     return wall, durs
 
 
@@ -136,14 +144,16 @@ def cpu_baseline(w, n_rows: int):
     import oracle
 
     q, k, v = ai.make_workload(w)
+    lens = ai.kv_len_of(w)
     rows = ai.sample_rows(w.B, w.H, w.N, n_rows, seed=w.seed + 7)
     threads = oracle.default_threads()
-    oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows[:threads], threads=threads)  # load + warm
+    oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows[:threads], threads=threads, kv_len=lens)  # warm
     t0 = time.perf_counter()
-    oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows, threads=threads)
+    oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows, threads=threads, kv_len=lens)
     dt = time.perf_counter() - t0
     i = rows % w.N
-    keys = (i + 1) if w.causal else np.full_like(i, w.N)
+    n_valid = np.array(lens)[rows // (w.H * w.N)] if lens else np.full_like(i, w.N)
+    keys = np.minimum(i + 1, n_valid) if w.causal else n_valid
     flops = float(np.sum(4.0 * keys * w.d))  # 2 FLOP per q.k product term + 2 per p.v term, per visible key
     # the metric counts 4*N*d per row (halved on average when causal); sampled rows use their real key counts
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -163,8 +173,8 @@ def pmc_pass(w, reps: int):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    q, k, v, o, lse = _device_inputs(w)
-    call = _caller(w, q, k, v, o, lse, torch.cuda.current_stream().cuda_stream)
+    q, k, v, o, lse, lens = _device_inputs(w)
+    call = _caller(w, q, k, v, o, lse, lens, torch.cuda.current_stream().cuda_stream)
     for _ in range(reps):
         call()
     torch.cuda.synchronize()
@@ -260,8 +270,9 @@ def write_profiles(w):
     md = f"""# rocprofv3 summary: {kernel_name(w)} on {w.name}
 
 Kernel source sha256[:16]: `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip).
-Workload: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} {w.dtype}; {w.flops:.4g} FLOP per launch
-(4*B*H*N^2*d{', halved' if w.causal else ''}), {w.algorithmic_bytes} algorithmic HBM bytes per launch.
+Workload: B={w.B} H={w.H} H_kv={w.Hk} N={w.N} d={w.d} causal={w.causal} {w.dtype}{f' kv_len={list(w.kv_len)}' if w.kv_len else ''};
+{w.flops:.4g} FLOP per launch (4*d*H per visible query-key pair, causal triangles counted as N^2/2),
+{w.algorithmic_bytes} algorithmic HBM bytes per launch.
 
 Commands (run from the repository root; outputs under gpurun_out/, summarised by `python bench.py --workload {w.name} --write-profiles`):
 
@@ -283,7 +294,7 @@ FETCH_SIZE reads {copy_read_kib:.1f} KiB (scale {f_fetch:.4f}), WRITE_SIZE reads
 
 | | counter KiB | scaled bytes | algorithmic bytes |
 |---|---|---|---|
-| read | {k_read / f_fetch / 1024:.1f} | {k_read:.0f} | {3 * w.B * w.H * w.N * w.d * w.elt_bytes} (q, k, v) |
+| read | {k_read / f_fetch / 1024:.1f} | {k_read:.0f} | {(w.B * w.H * w.N + 2 * w.kv_rows) * w.d * w.elt_bytes} (q, k, v) |
 | write | {k_write / f_write / 1024:.1f} | {k_write:.0f} | {w.B * w.H * w.N * (w.d * w.elt_bytes + 4)} (o, lse) |
 
 HBM bandwidth at the traced average: {(k_read + k_write) / (avg_us * 1e-6) / 1e9:.0f} GB/s.
@@ -361,8 +372,9 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q, k, v; no dataset)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "scale": w.scale, "input_dtype": w.dtype, "accumulate": "fp32"},
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hk, "N": w.N, "d": w.d, "causal": w.causal,
+                   "kv_len": list(w.kv_len) or None, "scale": w.scale, "input_dtype": w.dtype,
+                   "accumulate": "fp32"},
         "pct_of_peak": round(100 * value / peak, 2),
         "kernel_ms": {"mean": round(k_mean, 4), "median": round(k_med, 4), "min": round(min(durs), 4),
                       "p90": round(sorted(durs)[int(0.9 * (len(durs) - 1))], 4)},

@@ -1,10 +1,13 @@
-"""Tensor-level call of the attention forward: checks shapes, allocates o and lse with torch, calls fa_fwd.
+"""Tensor-level call of the attention forward: checks shapes, allocates o and lse with torch, calls the C ABI.
 
-    o, lse = forward(q, k, v, causal=False, scale=None)
+    o, lse = forward(q, k, v, causal=False, scale=None, kv_len=None)
 
-q, k, v: [B, H, N, d] contiguous CUDA (ROCm) tensors, all bf16 (-> fa_fwd) or all fp32 (-> fa_fwd_f32),
-d in {64, 128}. scale defaults to 1/sqrt(d). Returns o (same dtype and shape as q) and lse ([B, H, N] fp32,
-natural log). The kernel is enqueued on torch's current stream (or `stream`, a raw hipStream_t int).
+q: [B, H, N, d], k and v: [B, H_kv, N, d] contiguous CUDA (ROCm) tensors, all bf16 or all fp32, d in {64, 128}.
+H_kv < H (grouped/multi-query attention: H_kv divides H, query head h reads key/value head h // (H // H_kv)) and
+kv_len (a device int32 [B] tensor of valid-key counts, key padding) are bf16 only. The entry point is fa_fwd,
+fa_fwd_gqa, fa_fwd_kpad or fa_fwd_f32 accordingly. scale defaults to 1/sqrt(d). Returns o (same dtype and shape
+as q) and lse ([B, H, N] fp32, natural log). The kernel is enqueued on torch's current stream (or `stream`, a raw
+hipStream_t int).
 """
 from __future__ import annotations
 
@@ -25,8 +28,10 @@ def _check(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
             raise ValueError(f"{name} must be contiguous ([B, H, N, d] row-major)")
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:] or k.shape[1] < 1 \
+            or q.shape[1] % k.shape[1] != 0:
+        raise ValueError(f"q [B,H,N,d] and k, v [B,H_kv,N,d] (H_kv dividing H) disagree: {tuple(q.shape)} "
+                         f"{tuple(k.shape)} {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"q, k, v must all be bfloat16 or all float32, got {q.dtype} {k.dtype} {v.dtype}")
     if not (q.device == k.device == v.device):
@@ -34,9 +39,16 @@ def _check(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: float | None = None,
-            out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream: int | None = None):
+            out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream: int | None = None,
+            kv_len: torch.Tensor | None = None):
     _check(q, k, v)
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if (H_kv != H or kv_len is not None) and q.dtype != torch.bfloat16:
+        raise TypeError("grouped key/value heads and kv_len are supported for bfloat16 inputs")
+    if kv_len is not None and (not isinstance(kv_len, torch.Tensor) or kv_len.dtype != torch.int32
+                               or kv_len.shape != (B,) or not kv_len.is_contiguous() or kv_len.device != q.device):
+        raise ValueError("kv_len must be a contiguous int32 [B] tensor on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -50,10 +62,17 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if stream is None:
         with torch.cuda.device(q.device):
             stream = torch.cuda.current_stream().cuda_stream
-    fn = binding.fa_fwd if q.dtype == torch.bfloat16 else binding.fa_fwd_f32
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    c, sc, st = int(bool(causal)), float(scale), int(stream)
     with torch.cuda.device(q.device):
-        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, int(bool(causal)),
-                float(scale), int(stream))
+        if kv_len is not None:
+            rc = binding.fa_fwd_kpad(*ptrs, kv_len.data_ptr(), B, H, H_kv, N, d, c, sc, st)
+        elif H_kv != H:
+            rc = binding.fa_fwd_gqa(*ptrs, B, H, H_kv, N, d, c, sc, st)
+        elif q.dtype == torch.bfloat16:
+            rc = binding.fa_fwd(*ptrs, B, H, N, d, c, sc, st)
+        else:
+            rc = binding.fa_fwd_f32(*ptrs, B, H, N, d, c, sc, st)
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_fwd failed ({rc}): {binding.fa_strerror(rc)}")
     return out, lse

@@ -25,7 +25,7 @@ FA_ERR_ARG = 5
 FA_ERR_ALIAS = 6
 FA_ERR_HIP = 7
 
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_f32", "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_attention_13_amd/build.py` "
@@ -36,6 +36,10 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _lib.fa_fwd.restype = _I
 _lib.fa_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_lib.fa_fwd_gqa.restype = _I
+_lib.fa_fwd_gqa.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_lib.fa_fwd_kpad.restype = _I
+_lib.fa_fwd_kpad.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _lib.fa_fwd_f32.restype = _I
 _lib.fa_fwd_f32.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _lib.fa_strerror.restype = ctypes.c_char_p
@@ -52,6 +56,18 @@ def fa_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: 
            stream: int) -> int:
     """Raw entry point: device pointers as ints, bf16 q/k/v/o, fp32 lse. Returns the FA_* code."""
     return _lib.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+
+
+def fa_fwd_gqa(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, N: int, d: int, causal: int,
+               scale: float, stream: int) -> int:
+    """Raw entry point: bf16 q/o [B,H,N,d], k/v [B,H_kv,N,d]; query head h reads key/value head h // (H // H_kv)."""
+    return _lib.fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream)
+
+
+def fa_fwd_kpad(q: int, k: int, v: int, o: int, lse: int, kv_len: int, B: int, H: int, H_kv: int, N: int, d: int,
+                causal: int, scale: float, stream: int) -> int:
+    """Raw entry point: fa_fwd_gqa plus kv_len, a device int32 [B] array of valid-key counts (key padding)."""
+    return _lib.fa_fwd_kpad(q, k, v, o, lse, kv_len, B, H, H_kv, N, d, causal, scale, stream)
 
 
 def fa_fwd_f32(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,

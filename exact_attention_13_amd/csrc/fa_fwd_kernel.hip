@@ -24,14 +24,21 @@
 //     v_dot2c_f32_bf16, so o is the exact weighted average under those weights.
 //   * The second product runs one 16-key step at a time, so the exponentials of step m+1 and the V reads of
 //     step m+1 overlap the MFMAs of step m; K fragment reads are issued about four MFMAs ahead.
-//   * K/V tiles of 64 keys go device memory -> LDS by LDS-DMA (buffer_load ... lds) through a 3-stage ring
-//     (8 waves; 2 stages for 4 waves): tile j+2 is copied while tile j is computed; one barrier per tile. The LDS layouts are XOR-swizzled so
-//     that the K fragment reads, the transposing V reads and the DMA writes are all free of bank conflicts.
+//   * K/V tiles (128 keys for 8-wave workgroups, 64 for 4-wave ones) go device memory -> LDS by LDS-DMA
+//     (buffer_load ... lds) through a 2-stage ring: tile j+1 is copied while tile j is computed; one barrier per
+//     tile. The LDS layouts are XOR-swizzled so that the K fragment reads, the transposing V reads and the DMA
+//     writes are all free of bank conflicts.
 //   * Causal: a workgroup visits only key tiles that meet its rows, a wave skips tiles entirely above its
 //     rows, and the mask is applied only on tiles that cross the diagonal or the sequence end.
 //   * The linear workgroup id is remapped so that (when B*H is a multiple of 8) every query block of a head
 //     runs on the same XCD (workgroups are dealt to the 8 XCDs round-robin) and shares that XCD's L2, and
-//     causal work starts with the longest query blocks.
+//     causal work starts with the longest query blocks. XCDs take key/value heads round-robin, so the query
+//     heads that share a key/value head (grouped-query attention) also share an L2.
+//   * Grouped/multi-query attention (the unite.ai page, section "FlashAttention-2", item 3): query head bh
+//     reads key/value head bh / group, group = H / Hkv consecutive query heads per key/value head.
+//   * Key padding (a per-batch count Nk of valid keys, triton-transformer README usage example "ex. BERT"):
+//     tiles past Nk are not visited and keys >= Nk are masked like the sequence end; a row with no visible key
+//     gets o = 0 and lse = -inf.
 // The fp32 kernel keeps the same decomposition on v_mfma_f32_32x32x2f32 with a simple single-buffered loop.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -72,17 +79,23 @@ __device__ __forceinline__ float pair_sum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Workgroup -> (head bh, query block qb). Workgroups are dispatched to XCDs round-robin by linear id.
-__device__ __forceinline__ void map_workgroup(int lin, int nq, int bh_count, bool causal, int& bh, int& qb) {
+// Workgroup -> (head bh, query block qb). Workgroups are dispatched to XCDs round-robin by linear id. When B*H
+// is a multiple of 8, XCD x takes the key/value heads x, x+8, x+16, ... (each with its `group` query heads) when
+// their count is a multiple of 8, else the query heads x, x+8, ...: a group's query heads share an L2, and heads
+// of every batch run on every XCD (per-batch work differs under key padding).
+__device__ __forceinline__ void map_workgroup(int lin, int nq, int bh_count, int group, bool causal, int& bh,
+                                              int& qb) {
   if ((bh_count & 7) == 0) {
     const int xcd = lin & 7, t = lin >> 3, per = bh_count >> 3;  // heads per XCD
+    int jh;                                                      // this XCD's jh-th head
     if (causal) {
       qb = nq - 1 - t / per;
-      bh = xcd + 8 * (t % per);
+      jh = t % per;
     } else {
-      bh = xcd + 8 * (t / nq);
+      jh = t / nq;
       qb = t % nq;
     }
+    bh = ((bh_count / group) & 7) == 0 ? (xcd + 8 * (jh / group)) * group + jh % group : xcd + 8 * jh;
   } else {
     if (causal) {
       qb = nq - 1 - lin / bh_count;
@@ -159,7 +172,8 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
 template <int D, bool CAUSAL, int NW, int ST, int KT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale) {
+    __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale, int H, int group,
+    const int* __restrict__ kv_len) {
   using T = Tile<D>;
   constexpr int kThr = 64 * NW;
   constexpr int kBrW = NW * kRowsPerWave;        // query rows per workgroup
@@ -184,16 +198,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int nq = gridDim.x;
   int bh, qb;
-  map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, CAUSAL, bh, qb);
+  map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;  // key/value head of this query head
   const __bf16* qh = q + head_off;
-  const __bf16* kh = k + head_off;
-  const __bf16* vh = v + head_off;
+  const __bf16* kh = k + kv_off;
+  const __bf16* vh = v + kv_off;
+  // valid keys of this batch (key-padding mask), clamped to [0, N]
+  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bh / H], 0), N)) : N;
 
   const int q_lo = qb * kBrW;
   const int q_last = min(q_lo + kBrW, N) - 1;              // last real query row of the workgroup
-  const int n_tiles = CAUSAL ? (q_last / kBcT + 1) : (N + kBcT - 1) / kBcT;
+  const int key_tiles = (Nk + kBcT - 1) / kBcT;             // tiles holding valid keys
+  const int n_tiles = CAUSAL ? min(q_last / kBcT + 1, key_tiles) : key_tiles;
   const int q0w = q_lo + wave * kRowsPerWave;               // first query row of this wave
   const int my_q = q0w + l32;                               // query row of this lane
   // Tiles j < wave_tiles hold at least one key visible to this wave's rows.
@@ -227,10 +245,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       const int row0 = j * kBcT + t * kBc;
-      // rows past N arrive as zeros. (The clamp would compile to a vector instruction; readfirstlane keeps the
+      // rows past Nk arrive as zeros. (The clamp would compile to a vector instruction; readfirstlane keeps the
       // descriptor in scalar registers, otherwise every copy is wrapped in a loop over distinct descriptors.)
-      const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kBc)) * T::RB);
-      const int row_base = __builtin_amdgcn_readfirstlane(min(row0, N - 1));
+      const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(Nk - row0, kBc)) * T::RB);
+      const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Nk - 1));
       const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * D, bytes);
 #pragma unroll
       for (int p = 0; p < kCopies; ++p)
@@ -289,17 +307,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
-  // Mask (only tiles that cross the diagonal or the end of the sequence), row max and (rarely) the move of the
-  // exponent reference, for tile j held in s.
+  // Mask (only tiles that cross the diagonal or the end of the valid keys), row max and (rarely) the move of
+  // the exponent reference, for tile j held in s.
   auto stats = [&](f32x16(&s)[2 * KT], int j) __attribute__((always_inline)) {
     const int kv0 = j * kBcT;
-    if ((kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
+    if ((kv0 + kBcT > Nk) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
 #pragma unroll
       for (int b = 0; b < 2 * KT; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool vis = (key < N) && (!CAUSAL || key <= my_q);
+          const bool vis = (key < Nk) && (!CAUSAL || key <= my_q);
           s[b][r] = vis ? s[b][r] : -INFINITY;
         }
     }
@@ -385,15 +403,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         wait_copies_and_barrier<0>();
       }
     };
-    // prologue: tiles 0 .. ST-2 into stages 0 .. ST-2
-    copy_k(0, 0);
-    copy_v(0, 0);
-    if (ST == 3 && n_tiles > 1) {
-      copy_k(1, kStage);
-      copy_v(1, kStage);
-      wait_copies_and_barrier<kWaitKeep>();
-    } else {
-      wait_copies_and_barrier<0>();
+    // prologue: tiles 0 .. ST-2 into stages 0 .. ST-2 (none when the batch has no valid key; n_tiles is the
+    // same for the whole workgroup)
+    if (n_tiles > 0) {
+      copy_k(0, 0);
+      copy_v(0, 0);
+      if (ST == 3 && n_tiles > 1) {
+        copy_k(1, kStage);
+        copy_v(1, kStage);
+        wait_copies_and_barrier<kWaitKeep>();
+      } else {
+        wait_copies_and_barrier<0>();
+      }
     }
     for (int j = 0; j < n_tiles; j += ST) {
       step(j, Int<0>{});
@@ -404,10 +425,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
 
-  // ---- epilogue: o = acc / l once per row, lse = m*scale + ln l
+  // ---- epilogue: o = acc / l once per row, lse = m*scale + ln l. l >= 1 whenever a key is visible (the weight
+  // of the maximum is >= 1); l == 0 only for a row without visible keys: o = 0, lse = -inf.
   const float l_tot = pair_sum32(l_run);
   if (my_q < N) {
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* orow = o + head_off + (size_t)my_q * D;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
@@ -419,7 +441,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         *(bf16x4*)(orow + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(x, bf16x4);
       }
     }
-    if (h == 0) lse[(size_t)bh * N + my_q] = (m_ref * c2 + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (h == 0)
+      lse[(size_t)bh * N + my_q] = l_tot > 0.f ? (m_ref * c2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -451,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(const float* __res
   const int l32 = lane & 31, h = lane >> 5;
   const int nq = gridDim.x;
   int bh, qb;
-  map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, CAUSAL, bh, qb);
+  map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, 1, CAUSAL, bh, qb);
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
   const int q_lo = qb * kBr;
@@ -573,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(const float* __res
 // ------------------------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, int NW, int ST, int KT>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                              float scale, hipStream_t stream) {
+                              float scale, int H, int group, const int* kv_len, hipStream_t stream) {
   constexpr int lds = 2 * ST * KT * Tile<D>::kBytes;
   constexpr int rows = NW * kRowsPerWave;
   auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST, KT>;
@@ -581,7 +604,7 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)BH);
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (__bf16*)o, lse, N, BH, scale);
+                     (const __bf16*)v, (__bf16*)o, lse, N, BH, scale, H, group, kv_len);
   return hipGetLastError();
 }
 
@@ -604,19 +627,18 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
 // each is deterministic.
 constexpr long long kWideGridMin = 512;
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
-                           bool causal, float scale, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                           int N, int d, bool causal, float scale, const int* kv_len, hipStream_t stream) {
+  const int BH = B * H, group = H / Hkv;
   const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
+#define FA_LAUNCH(D, C, NW, KT) launch_bf16<D, C, NW, 2, KT>(q, k, v, o, lse, BH, N, scale, H, group, kv_len, stream)
   if (wide) {
-    if (d == 64) return causal ? launch_bf16<64, true, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream)
-                               : launch_bf16<64, false, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream);
-    return causal ? launch_bf16<128, true, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_bf16<128, false, 8, 2, 2>(q, k, v, o, lse, BH, N, scale, stream);
+    if (d == 64) return causal ? FA_LAUNCH(64, true, 8, 2) : FA_LAUNCH(64, false, 8, 2);
+    return causal ? FA_LAUNCH(128, true, 8, 2) : FA_LAUNCH(128, false, 8, 2);
   }
-  if (d == 64) return causal ? launch_bf16<64, true, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream)
-                             : launch_bf16<64, false, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_bf16<128, true, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_bf16<128, false, 4, 2, 1>(q, k, v, o, lse, BH, N, scale, stream);
+  if (d == 64) return causal ? FA_LAUNCH(64, true, 4, 1) : FA_LAUNCH(64, false, 4, 1);
+  return causal ? FA_LAUNCH(128, true, 4, 1) : FA_LAUNCH(128, false, 4, 1);
+#undef FA_LAUNCH
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,

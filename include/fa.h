@@ -48,11 +48,11 @@ extern "C" {
 
 #define FA_OK 0
 #define FA_ERR_NULL 1    /* a pointer is NULL (non-empty problem) */
-#define FA_ERR_SHAPE 2   /* B, H or N negative; B*H over 65535; N over 2^30 */
+#define FA_ERR_SHAPE 2   /* B, H, N or H_kv negative; B*H over 65535; N over 2^30; H_kv not dividing H */
 #define FA_ERR_HEADDIM 3 /* d is not 64 or 128 */
-#define FA_ERR_ALIGN 4   /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+#define FA_ERR_ALIGN 4   /* q, k, v or o not 16-byte aligned, or lse / kv_len not 4-byte aligned */
 #define FA_ERR_ARG 5     /* scale not finite or not > 0, or causal not 0/1 */
-#define FA_ERR_ALIAS 6   /* o or lse overlaps q, k or v, or o overlaps lse */
+#define FA_ERR_ALIAS 6   /* o or lse overlaps q, k, v or kv_len, or o overlaps lse */
 #define FA_ERR_HIP 7     /* the HIP runtime reported an error at launch */
 
 /*
@@ -69,6 +69,38 @@ extern "C" {
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
            float scale, hipStream_t stream);
+
+/*
+ * fa_fwd_gqa -- fa_fwd with fewer key/value heads than query heads
+ * (grouped-query attention; H_kv = 1 is multi-query attention), listed among
+ * the FlashAttention-2 improvements on the unite.ai page (section
+ * "FlashAttention-2", item 3).
+ *   k, v    : const bf16 [B,H_kv,N,d] (device)
+ *   H_kv    : key/value heads, >= 1 and dividing H. Query head h reads
+ *             key/value head h / (H / H_kv): each key/value head serves
+ *             H / H_kv consecutive query heads.
+ * Everything else (q, o, lse, layout, ownership, errors) as fa_fwd; H_kv < 1
+ * or not dividing H is FA_ERR_SHAPE. fa_fwd_gqa with H_kv = H is fa_fwd.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N, int d,
+               int causal, float scale, hipStream_t stream);
+
+/*
+ * fa_fwd_kpad -- fa_fwd_gqa with a key-padding mask given as per-batch
+ * lengths (the boolean (batch, seq) mask of the triton-transformer README's
+ * usage example, "ex. BERT", for right-padded sequences: the valid keys of a
+ * batch are a prefix).
+ *   kv_len  : const int32 [B] (device): batch b has kv_len[b] valid keys; key
+ *             j is visible to the queries of batch b only if j < kv_len[b]
+ *             (and j <= i when causal). Values are clamped to [0, N] on the
+ *             device. All N query rows are computed; a row with no visible key
+ *             (kv_len[b] = 0) gets o = 0 and lse = -inf.
+ * Work skips the key tiles past kv_len[b]. kv_len must be 4-byte aligned
+ * (FA_ERR_ALIGN), non-NULL (FA_ERR_NULL) and must not overlap o or lse
+ * (FA_ERR_ALIAS); it is only read, by the kernel. The rest as fa_fwd_gqa.
+ */
+int fa_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse, const int* kv_len, int B, int H,
+                int H_kv, int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
  * fa_fwd_f32 -- the same operation with fp32 q, k, v and o. Products and sums

@@ -33,10 +33,24 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 10000
+    assert fa.fa_version() == 10100
     for code in range(8):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
+
+
+LEN = A + 0x5000000  # fake device address of kv_len
+
+
+def _gqa_same_heads(q, k, v, o, lse, B, H, N, d, causal, scale, stream):
+    return fa.fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream)
+
+
+def _kpad_same_heads(q, k, v, o, lse, B, H, N, d, causal, scale, stream):
+    return fa.fa_fwd_kpad(q, k, v, o, lse, LEN, B, H, H, N, d, causal, scale, stream)
+
+
+ENTRIES = [fa.fa_fwd, fa.fa_fwd_f32, _gqa_same_heads, _kpad_same_heads]
 
 
 def _call(fn=None, q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, B=1, H=2, N=64,
@@ -45,7 +59,7 @@ def _call(fn=None, q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A
     return fn(q, k, v, o, lse, B, H, N, d, causal, scale, 0)
 
 
-@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+@pytest.mark.parametrize("fn", ENTRIES)
 def test_error_codes(fn):
     assert _call(fn, q=0) == fa.FA_ERR_NULL
     assert _call(fn, lse=0) == fa.FA_ERR_NULL
@@ -68,7 +82,30 @@ def test_error_codes(fn):
     assert _call(fn, lse=A + 0x3000000 + 256) == fa.FA_ERR_ALIAS  # lse inside o
 
 
-@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+def test_grouped_heads_error_codes():
+    def gqa(H=4, H_kv=2, o=A + 0x3000000, N=64, B=1):
+        return fa.fa_fwd_gqa(A, A + 0x1000000, A + 0x2000000, o, A + 0x4000000, B, H, H_kv, N, 64, 0, 0.125, 0)
+    assert gqa(H_kv=0) == fa.FA_ERR_SHAPE
+    assert gqa(H_kv=-1) == fa.FA_ERR_SHAPE
+    assert gqa(H_kv=3) == fa.FA_ERR_SHAPE     # 3 does not divide 4
+    assert gqa(H_kv=8) == fa.FA_ERR_SHAPE     # more key/value heads than query heads
+    # k holds H_kv = 1 head of 64 x 64 bf16 = 8192 bytes: o starting 8000 bytes into k overlaps it
+    assert gqa(H_kv=1, o=A + 0x1000000 + 8000) == fa.FA_ERR_ALIAS
+    assert gqa(H_kv=0, N=0) == fa.FA_OK       # empty problem: nothing to check the grouping against
+    assert gqa(H_kv=-1, N=0) == fa.FA_ERR_SHAPE
+
+
+def test_key_padding_error_codes():
+    def kpad(kv_len=LEN, o=A + 0x3000000, lse=A + 0x4000000, N=64):
+        return fa.fa_fwd_kpad(A, A + 0x1000000, A + 0x2000000, o, lse, kv_len, 2, 4, 2, N, 64, 1, 0.125, 0)
+    assert kpad(kv_len=0) == fa.FA_ERR_NULL
+    assert kpad(kv_len=LEN + 2) == fa.FA_ERR_ALIGN
+    assert kpad(o=LEN - 64) == fa.FA_ERR_ALIAS       # o's last bytes cover kv_len
+    assert kpad(lse=LEN + 4 - 4 * 2 * 4 * 64) == fa.FA_ERR_ALIAS  # lse ends on kv_len's first element
+    assert kpad(kv_len=0, N=0) == fa.FA_OK           # empty problem ignores the pointers
+
+
+@pytest.mark.parametrize("fn", ENTRIES)
 def test_empty_problem_is_a_no_op_that_ignores_pointers(fn):
     assert _call(fn, q=0, k=0, v=0, o=0, lse=0, N=0) == fa.FA_OK
     assert _call(fn, q=0, k=0, v=0, o=0, lse=0, B=0) == fa.FA_OK

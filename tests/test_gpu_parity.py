@@ -28,16 +28,17 @@ def fa():
     return fa_mod
 
 
-def _run(fa, q, k, v, causal, scale):
+def _run(fa, q, k, v, causal, scale, kv_len=None):
     qd, kd, vd = (t.to("cuda:0") for t in (q, k, v))
-    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    lens = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device="cuda:0")
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, kv_len=lens)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def _compare(o_gpu, lse_gpu, q, k, v, causal, scale, dtype, rows=None, label=""):
+def _compare(o_gpu, lse_gpu, q, k, v, causal, scale, dtype, rows=None, label="", kv_len=None):
     B, H, N, d = q.shape
-    o_ref, lse_ref = oracle.attention_rows(q, k, v, causal, scale, rows=rows)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, causal, scale, rows=rows, kv_len=kv_len)
     og = o_gpu.reshape(-1, d)
     lg = lse_gpu.reshape(-1)
     if rows is not None:
@@ -58,11 +59,14 @@ def test_workload_parity(fa, name):
     w = ai.WORKLOADS[name]
     print(f"[case] {name}", flush=True)
     q, k, v = ai.make_workload(w)
-    o, lse = _run(fa, q, k, v, w.causal, w.scale)
+    lens = ai.kv_len_of(w)
+    o, lse = _run(fa, q, k, v, w.causal, w.scale, lens)
     rows = ai.check_rows(w)
     if rows is None and w.B * w.H * w.N * w.N * w.d > 4e10:  # the 4096-row case: sampled + edges
         rows = np.unique(np.concatenate([ai.sample_rows(w.B, w.H, w.N, 512, w.seed), ai.edge_rows(w.N)]))
-    _compare(o, lse, q, k, v, w.causal, w.scale, w.dtype, rows=rows, label=name)
+    if rows is not None:  # and the tile edges of the last head
+        rows = np.unique(np.concatenate([rows, (w.B * w.H - 1) * w.N + ai.edge_rows(w.N, 256, 128)]))
+    _compare(o, lse, q, k, v, w.causal, w.scale, w.dtype, rows=rows, label=name, kv_len=lens)
 
 
 # --- ragged sizes: several tiles and a tail, every row checked ----------------------------------------------------------

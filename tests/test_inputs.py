@@ -48,3 +48,30 @@ def test_workload_flops_and_bytes():
     wc = ai.WORKLOADS["c4_bf16_b1h32n16384d128_causal"]
     assert wc.flops == 2 * 32 * 16384 ** 2 * 128
     assert ai.default_scale(128) == float(np.float32(1 / np.sqrt(128)))
+
+
+def test_grouped_heads_draw_fewer_key_value_heads_in_the_same_order():
+    q, k, v = ai.make_qkv(2, 8, 16, 64, seed=9, dtype="f32", Hkv=2)
+    assert q.shape == (2, 8, 16, 64) and k.shape == v.shape == (2, 2, 16, 64)
+    g = torch.Generator("cpu").manual_seed(9)
+    q_ref = torch.randn((2, 8, 16, 64), generator=g)
+    k_ref = torch.randn((2, 2, 16, 64), generator=g)
+    assert torch.equal(q, q_ref) and torch.equal(k, k_ref)
+    # Hkv = H draws exactly what the plain recipe draws
+    assert ai.sha256(*ai.make_qkv(1, 4, 8, 64, seed=9, Hkv=4)) == ai.sha256(*ai.make_qkv(1, 4, 8, 64, seed=9))
+
+
+def test_grouped_and_padded_workload_accounting():
+    w = ai.WORKLOADS["gqa_bf16_b2h32kv8n4096d128"]
+    assert w.Hk == 8 and w.flops == 4 * 2 * 32 * 4096 ** 2 * 128
+    assert w.algorithmic_bytes == (2 * 2 * 32 + 2 * 2 * 8) * 4096 * 128 * 2 + 4 * 2 * 32 * 4096
+    m = ai.WORKLOADS["mqa_bf16_b1h32kv1n16384d128_causal"]
+    assert m.Hk == 1 and m.flops == 2 * 32 * 16384 ** 2 * 128
+    p = ai.WORKLOADS["kpad_bf16_b8h16n4096d128"]
+    assert len(p.kv_len) == p.B and all(0 < L <= p.N for L in p.kv_len)
+    assert p.flops == 4 * 16 * 128 * 4096 * sum(p.kv_len)   # non-causal: every query sees L keys
+    assert p.algorithmic_bytes == (2 * 8 * 16 * 4096 + 2 * 16 * sum(p.kv_len)) * 128 * 2 + 4 * 8 * 16 * 4096
+    assert ai.kv_len_of(p) == list(p.kv_len) and ai.kv_len_of(w) is None
+    # causal with padding: the triangle of the valid keys plus the rows past it
+    wc = ai.Workload("x", 1, 1, 10, 64, True, "bf16", 1, kv_len=(4,))
+    assert wc.flops == 4 * 64 * (4 * 4 / 2 + 6 * 4)
