@@ -1,12 +1,13 @@
-"""fp64 CPU oracle for the exact attention forward.
+"""fp64 CPU oracle for the exact attention forward and its gradients.
 
 TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the benchmark's
 CPU-baseline leg may import or call this package; the GPU path never does, and
 this package imports nothing from it.
 
-The arithmetic lives in attn_oracle.c (plain C, fp64, one materialised score
-row per query, sequential sums); this module only builds it with gcc, loads it
-with ctypes and widens the inputs to fp32 (exact for bf16 and fp32 inputs).
+The arithmetic lives in attn_oracle.c (forward) and attn_bwd_oracle.c
+(gradients): plain C, fp64, one materialised score row per query, sequential
+sums. This module only builds them with gcc, loads them with ctypes and widens
+the inputs to fp32 (exact for bf16 and fp32 inputs).
 
 Definition followed (unite.ai page "Flash Attention: revolutionizing transformer
 efficiency", opening code block and "The Math Behind Flash Attention" item 1):
@@ -24,16 +25,16 @@ from pathlib import Path
 import numpy as np
 
 _HERE = Path(__file__).resolve().parent
-_SRC = _HERE / "attn_oracle.c"
+_SRCS = (_HERE / "attn_oracle.c", _HERE / "attn_bwd_oracle.c")
 _LIB = _HERE / "liboracle.so"
 _lib = None
 
 
 def build(force: bool = True) -> Path:
-    """Compile attn_oracle.c with gcc into liboracle.so (no -ffast-math: IEEE fp64 semantics)."""
-    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+    """Compile the oracle sources with gcc into liboracle.so (no -ffast-math: IEEE fp64 semantics)."""
+    if force or not _LIB.exists() or any(_LIB.stat().st_mtime < f.stat().st_mtime for f in _SRCS):
         tmp = _LIB.with_suffix(".so.tmp")
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", str(_SRC), "-o", str(tmp), "-lm"]
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", *map(str, _SRCS), "-o", str(tmp), "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -51,6 +52,13 @@ def _load():
                       ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
                       ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
                       ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        g = lib.oracle_attn_bwd_rows
+        g.restype = ctypes.c_int
+        g.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_long] * 5 + [ctypes.c_int, ctypes.c_double,
+                                                                     ctypes.c_void_p, ctypes.c_long,
+                                                                     ctypes.c_void_p, ctypes.c_long,
+                                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                                     ctypes.c_void_p, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -123,3 +131,51 @@ def attention(q, k, v, causal: bool, scale: float, threads: int | None = None, k
     B, H, N, d = tuple(q.shape)
     o, lse = attention_rows(q, k, v, causal, scale, None, threads, kv_len)
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, q_rows=None, kv_rows=None,
+                       threads: int | None = None):
+    """Gradients of the attention forward for an upstream gradient dout of o (none for lse).
+
+    q, dout: [B, H, N, d]; k, v: [B, Hkv, N, d] (Hkv divides H); bf16/fp32 CPU tensors or fp32 arrays.
+    q_rows: flat query rows (b*H + h)*N + i for dq, or None for every row; kv_rows: flat key rows
+    (b*Hkv + g)*N + j for dk and dv, or None for every row (an empty list skips that part).
+    Returns (dq [n_q, d], dk [n_kv, d], dv [n_kv, d]) as float64 arrays.
+    """
+    qa, ka, va, da = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    if (qa.ndim != 4 or da.shape != qa.shape or ka.shape != va.shape or ka.ndim != 4 or ka.shape[0] != qa.shape[0]
+            or ka.shape[2:] != qa.shape[2:] or qa.shape[1] % ka.shape[1] != 0):
+        raise ValueError(f"shapes disagree: q {qa.shape} k {ka.shape} v {va.shape} dout {da.shape}")
+    B, H, N, d = qa.shape
+    Hkv = ka.shape[1]
+
+    def rows_arg(rows, total):
+        if rows is None:
+            return None, total
+        arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+        return arr, int(arr.size)
+
+    qr, n_q = rows_arg(q_rows, B * H * N)
+    kr, n_kv = rows_arg(kv_rows, B * Hkv * N)
+    dq = np.zeros((n_q, d), dtype=np.float64)
+    dk = np.zeros((n_kv, d), dtype=np.float64)
+    dv = np.zeros((n_kv, d), dtype=np.float64)
+    if n_q == 0 and n_kv == 0:
+        return dq, dk, dv
+    rc = _load().oracle_attn_bwd_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, B, H, Hkv, N, d,
+                                      int(bool(causal)), float(np.float32(scale)),
+                                      None if qr is None else qr.ctypes.data, n_q,
+                                      None if kr is None else kr.ctypes.data, n_kv,
+                                      dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                      int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_bwd_rows failed with code {rc}")
+    return dq, dk, dv
+
+
+def attention_bwd(q, k, v, dout, causal: bool, scale: float, threads: int | None = None):
+    """Every gradient row: (dq [B,H,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) as float64 arrays."""
+    B, H, N, d = tuple(q.shape)
+    Hkv = tuple(k.shape)[1]
+    dq, dk, dv = attention_bwd_rows(q, k, v, dout, causal, scale, None, None, threads)
+    return dq.reshape(B, H, N, d), dk.reshape(B, Hkv, N, d), dv.reshape(B, Hkv, N, d)
