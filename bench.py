@@ -1,4 +1,4 @@
-"""Benchmark of the exact attention forward on one MI355X.
+"""Benchmark of the exact attention forward (and its gradients) on one MI355X.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload c3_bf16_b2h16n4096d128]
 
@@ -7,6 +7,12 @@ written) over the workload's synthetic inputs, already resident in device memory
 value = attention-forward TFLOP/s (4*B*H*N^2*d, halved when causal) over the timed steps; roofline = the
 kernel's MFMA roofline from HIP-event launch durations; cpu_baseline = the fp64 oracle timed on a bounded
 sample of the same workload on this host's cores.
+
+The line also carries `backward`: the gradient call fa_bwd (dq, then dk and dv) on the headline workload and on
+the long causal one, timed the same way, in the usual FLOP convention 2.5 x the forward's (five matrix products:
+the recomputed QK^T, dO V^T, dV, dQ, dK).
+
+    --bwd-only          time only the gradient call of --workload (one JSON line; for profiling)
 
 Other modes (used to produce the rocprofv3 summaries under profiles/):
     --pmc-pass          run a copy kernel of known size, then the workload kernel, a few times each
@@ -34,6 +40,10 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "c3_bf16_b2h16n4096d128"
 KERNEL_SRC = ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_kernel.hip"
+KERNEL_SRCS = (KERNEL_SRC, ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
+BWD_SRCS = (ROOT / "exact_attention_13_amd" / "csrc" / "fa_bwd_kernel.hip",
+            ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
+BWD_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal")
 PROFILES = ROOT / "profiles"
 
 
@@ -41,7 +51,8 @@ PROFILES = ROOT / "profiles"
 # counter group each; the copy kernel of --pmc-pass calibrates FETCH_SIZE / WRITE_SIZE against known bytes.
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{w}_trace -o run -- "
-             "python bench.py --workload {w} --no-cpu-baseline --no-other-workloads --steps 50 --warmup 10",
+             "python bench.py --workload {w} --no-cpu-baseline --no-other-workloads --no-backward --steps 50 "
+             "--warmup 10",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_{w}_fetch -o run -- "
              "python bench.py --workload {w} --pmc-pass",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_{w}_write -o run -- "
@@ -52,8 +63,11 @@ PROFILE_COMMANDS = {
 }
 
 
-def kernel_src_hash() -> str:
-    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+def kernel_src_hash(srcs=KERNEL_SRCS) -> str:
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
 
 
 def kernel_name(w) -> str:
@@ -120,6 +134,63 @@ def time_workload(w, steps: int, warmup: int):
     durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     del q, k, v, o, lse, lens
     return wall, durs
+
+
+def time_backward(w, steps: int, warmup: int):
+    """Gradient call of workload w (bf16): (wall_s for `steps` calls, per-call durations in ms from HIP events).
+    The forward runs once first to provide o and lse; dout is seeded N(0, 1)."""
+    import torch
+
+    import exact_attention_13_amd as fa
+
+    q, k, v, o, lse, lens = _device_inputs(w)
+    if lens is not None:
+        raise ValueError("the gradient call has no key padding")
+    g = torch.Generator("cpu").manual_seed(w.seed + 500)
+    dout = torch.randn(tuple(q.shape), generator=g).to(torch.bfloat16).cuda()
+    stream = torch.cuda.current_stream()
+    fwd = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
+    fwd()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(w.B, w.H, w.N),), dtype=torch.uint8, device="cuda")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), w.B, w.H, w.Hk, w.N, w.d, int(w.causal), w.scale,
+            stream.cuda_stream)
+
+    def call():
+        rc = fa.fa_bwd(*args)
+        if rc != 0:
+            raise RuntimeError(f"fa_bwd failed: {fa.fa_strerror(rc)}")
+    for _ in range(warmup):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    del q, k, v, o, lse, dout, dq, dk, dv, ws
+    return wall, durs
+
+
+def backward_record(w, steps: int, warmup: int):
+    wall, durs = time_backward(w, steps, warmup)
+    flops = 2.5 * w.flops
+    mean = statistics.fmean(durs)
+    return {"workload": w.name, "tflops": round(flops * steps / wall / 1e12, 2),
+            "pct_of_peak": round(100 * flops * steps / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
+                          "min": round(min(durs), 4)},
+            "roofline": {"bound": "mfma", "achieved": round(flops / (mean * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "flops_per_call": flops, "kernels": ["fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"],
+            "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}
 
 
 def traffic_from_profiles(w):
@@ -269,7 +340,7 @@ def write_profiles(w):
     cmds = "\n".join(f"    {PROFILE_COMMANDS[k].format(w=w.name)}" for k in PROFILE_COMMANDS)
     md = f"""# rocprofv3 summary: {kernel_name(w)} on {w.name}
 
-Kernel source sha256[:16]: `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip).
+Kernel source sha256[:16]: `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip and fa_gfx950.h).
 Workload: B={w.B} H={w.H} H_kv={w.Hk} N={w.N} d={w.d} causal={w.causal} {w.dtype}{f' kv_len={list(w.kv_len)}' if w.kv_len else ''};
 {w.flops:.4g} FLOP per launch (4*d*H per visible query-key pair, causal triangles counted as N^2/2),
 {w.algorithmic_bytes} algorithmic HBM bytes per launch.
@@ -334,6 +405,8 @@ def main():
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--write-profiles", action="store_true")
+    ap.add_argument("--bwd-only", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     args = ap.parse_args()
 
     if args.summarize:
@@ -358,6 +431,9 @@ def main():
     w = ai.WORKLOADS[args.workload]
     if args.pmc_pass:
         pmc_pass(w, reps=5)
+        return 0
+    if args.bwd_only:
+        print(json.dumps(backward_record(w, args.steps, args.warmup)), flush=True)
         return 0
 
     wall, durs = time_workload(w, args.steps, args.warmup)
@@ -394,6 +470,8 @@ def main():
             others[name] = {"kernel_ms_mean": round(om, 4), "tflops": round(ow.flops / (om * 1e-3) / 1e12, 2),
                             "pct_of_peak": round(100 * ow.flops / (om * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
         line["other_workloads"] = others
+    if not args.no_backward:
+        line["backward"] = [backward_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in BWD_WORKLOADS]
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_rows)
         cb.pop("seconds")

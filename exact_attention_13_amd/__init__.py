@@ -1,17 +1,19 @@
-"""Exact fused attention forward for AMD MI355X (gfx950): a C-ABI HIP library and its Python binding.
+"""Exact fused attention for AMD MI355X (gfx950): a C-ABI HIP library and its Python binding.
 
-    from exact_attention_13_amd import forward
+    from exact_attention_13_amd import backward, forward
     o, lse = forward(q, k, v, causal=True)
+    dq, dk, dv = backward(q, k, v, o, lse, dout, causal=True)
 
 The library (libfa.so, built from csrc/ by `python exact_attention_13_amd/build.py`) exports fa_fwd,
-fa_fwd_gqa, fa_fwd_kpad, fa_fwd_f32, fa_strerror and fa_version (include/fa.h). Importing this package
-fails if it is not built.
+fa_fwd_gqa, fa_fwd_kpad, fa_bwd, fa_bwd_workspace_bytes, fa_fwd_f32, fa_strerror and fa_version
+(include/fa.h). Importing this package fails if it is not built.
 """
 from .binding import (EXPORTS, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HEADDIM, FA_ERR_HIP, FA_ERR_NULL,
-                      FA_ERR_SHAPE, FA_OK, fa_fwd, fa_fwd_f32, fa_fwd_gqa, fa_fwd_kpad, fa_strerror, fa_version,
-                      library_path)
-from .attention import forward
+                      FA_ERR_SHAPE, FA_OK, fa_bwd, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_f32, fa_fwd_gqa, fa_fwd_kpad,
+                      fa_strerror, fa_version, library_path)
+from .attention import backward, forward
 
-__all__ = ["forward", "fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_f32", "fa_strerror", "fa_version", "library_path", "EXPORTS", "FA_OK",
+__all__ = ["forward", "backward", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad",
+           "fa_fwd_f32", "fa_strerror", "fa_version", "library_path", "EXPORTS", "FA_OK",
            "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN", "FA_ERR_ARG", "FA_ERR_ALIAS",
            "FA_ERR_HIP"]

@@ -76,3 +76,38 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_fwd failed ({rc}): {binding.fa_strerror(rc)}")
     return out, lse
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, causal: bool = False, scale: float | None = None, stream: int | None = None):
+    """Gradients (dq, dk, dv) of forward(q, k, v, causal, scale) -> (o, lse) for an upstream gradient dout of o.
+
+    bf16 tensors: q, o, dout [B, H, N, d]; k, v [B, H_kv, N, d]; lse [B, H, N] fp32 from the same forward call.
+    Allocates dq, dk, dv and the workspace with torch and calls fa_bwd on torch's current stream (or `stream`).
+    """
+    _check(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the backward pass takes bfloat16 tensors")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    for name, t in (("o", o), ("dout", dout)):
+        if (not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous tensor of q's shape, dtype and device")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = torch.empty((max(binding.fa_bwd_workspace_bytes(B, H, N), 16),), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        rc = binding.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, H_kv, N, d,
+                            int(bool(causal)), float(scale), int(stream))
+    if rc != binding.FA_OK:
+        raise RuntimeError(f"fa_bwd failed ({rc}): {binding.fa_strerror(rc)}")
+    return dq, dk, dv

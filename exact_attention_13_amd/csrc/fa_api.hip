@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kVersion = 10200;  // 1.2.0
 constexpr long long kMaxHeads = 65535;   // B*H is the grid's y extent
 constexpr long long kMaxN = 1LL << 30;
 
@@ -62,6 +62,33 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, c
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Checks of the gradient call: the forward's shape rules, then the nine tensors and the workspace.
+int validate_bwd(const void* const* in, int n_in, void* const* out, int n_out, const float* lse, const float* ws,
+                 int B, int H, int Hkv, int N, int d, int causal, float scale, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0 || Hkv < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (Hkv == 0 || H % Hkv != 0) return FA_ERR_SHAPE;
+  if ((long long)B * H > kMaxHeads || N > kMaxN) return FA_ERR_SHAPE;
+  for (int i = 0; i < n_in; ++i)
+    if (!in[i]) return FA_ERR_NULL;
+  for (int i = 0; i < n_out; ++i)
+    if (!out[i]) return FA_ERR_NULL;
+  if (!lse || !ws) return FA_ERR_NULL;
+  for (int i = 0; i < n_in; ++i)
+    if ((uintptr_t)in[i] & 15) return FA_ERR_ALIGN;
+  for (int i = 0; i < n_out; ++i)
+    if ((uintptr_t)out[i] & 15) return FA_ERR_ALIGN;
+  if (((uintptr_t)lse & 3) || ((uintptr_t)ws & 15)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +108,37 @@ int fa_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse
   return run_bf16(q, k, v, o, lse, kv_len, true, B, H, H_kv, N, d, causal, scale, stream);
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* workspace, int B, int H, int H_kv, int N, int d, int causal, float scale,
+           hipStream_t stream) {
+  const void* in[] = {q, k, v, o, dout};
+  void* out[] = {dq, dk, dv};
+  bool empty = false;
+  int rc = validate_bwd(in, 5, out, 3, lse, workspace, B, H, H_kv, N, d, causal, scale, &empty);
+  if (rc != FA_OK || empty) return rc;
+  // byte ranges: q, o, dout, dq are [B,H,N,d]; k, v, dk, dv are [B,H_kv,N,d]; lse [B,H,N]; the workspace
+  const size_t tq = (size_t)B * H * N * d * 2, tk = (size_t)B * H_kv * N * d * 2, tl = (size_t)B * H * N * 4;
+  const size_t tw = fa::bwd_workspace_bytes(B, H, N);
+  const void* rin[] = {q, k, v, o, dout, lse};
+  const size_t nin[] = {tq, tk, tk, tq, tq, tl};
+  void* rout[] = {dq, dk, dv, workspace};
+  const size_t nout[] = {tq, tk, tk, tw};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(rout[i], nout[i], rin[j], nin[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(rout[i], nout[i], rout[j], nout[j])) return FA_ERR_ALIAS;
+  }
+  const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H_kv, N, d,
+                                           causal != 0, scale, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return fa::bwd_workspace_bytes(B, H, N);
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
                int causal, float scale, hipStream_t stream) {
   bool empty = false;
@@ -93,12 +151,13 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "success";
-    case FA_ERR_NULL: return "a q/k/v/o/lse/kv_len pointer is NULL";
+    case FA_ERR_NULL: return "a tensor, lse, kv_len or workspace pointer is NULL";
     case FA_ERR_SHAPE: return "bad shape: B, H, N must be >= 0, B*H <= 65535, N <= 2^30, H_kv >= 1 dividing H";
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
-    case FA_ERR_ALIGN: return "misaligned pointer: q, k, v, o need 16-byte alignment, lse and kv_len 4-byte";
+    case FA_ERR_ALIGN:
+      return "misaligned pointer: tensors and the workspace need 16-byte alignment, lse and kv_len 4-byte";
     case FA_ERR_ARG: return "bad argument: scale must be finite and > 0, causal must be 0 or 1";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input (q, k, v, kv_len), or o overlaps lse";
+    case FA_ERR_ALIAS: return "an output (o, lse, dq, dk, dv, workspace) overlaps an input or another output";
     case FA_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";
     default: return "unknown error code";
   }

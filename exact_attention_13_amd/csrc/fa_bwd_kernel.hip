@@ -1,0 +1,485 @@
+// fa_bwd_kernel.hip -- gradients of the exact attention forward for gfx950 (MI355X, CDNA4).
+//
+// The pages name a faster backward pass and the recomputation of the attention matrix from stored statistics
+// instead of storing it (unite.ai page "Flash Attention: revolutionizing transformer efficiency": the key ideas
+// after "Enter Flash Attention", item 2; "FlashAttention-2", item 2). With the forward's lse and an upstream
+// gradient dO of o, per query row i and visible key j:
+//     p_ij = exp(scale q_i.k_j - lse_i),  D_i = dO_i . o_i,  dS_ij = p_ij (dO_i . v_j - D_i)
+//     dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i p_ij dO_i
+// (dk, dv summed over the query heads of a key/value group). Two kernels, neither with atomics, so every call
+// gives the same bits:
+//   * fa_bwd_dq_kernel: one workgroup per block of 128 query rows (4 waves x 32 rows), K/V tiles of 64 keys
+//     streamed through LDS exactly like the forward. S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16
+//     put one query row in each lane, so p = exp2(s*c - lse*log2e) and dS^T = p (dP^T - D) need only the lane's
+//     own lse and D; dQ^T += K^T dS^T takes dS^T from registers as the B operand and K^T by transposing LDS reads
+//     (ds_read_b64_tr_b16). It also computes D_i from the o and dO rows it loads anyway and writes (D_i,
+//     lse_i*log2e) to the workspace.
+//   * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys (4 waves x 32 keys) of one key/value head; query
+//     tiles of 64 rows (q, dO and the workspace pairs) of every query head of the group stream through LDS.
+//     S = Q K^T and dP = dO V^T put one key in each lane (K and V rows stay in registers as the B operands);
+//     dV^T += dO^T P and dK^T += Q^T dS take P and dS from registers as B operands and dO^T, Q^T by transposing
+//     LDS reads.
+// The workspace holds the pairs (D_i, lse_i*log2e) as [B*H][Npad] float2, Npad = N rounded up to 64; rows
+// N .. Npad-1 hold (0, +inf), which makes p (and dS) of those rows exactly 0 in the dk/dv kernel.
+// S and dP are computed in both kernels (7 matrix products instead of the 5 of a single pass with atomic dq
+// updates): the price of determinism.
+//
+// LDS tiles (64 rows) are read both row-wise (16 bytes per lane, A operands) and transposed (8 bytes per lane, 4
+// rows x 64 bytes per 32 lanes). One XOR swizzle of the 16-byte chunks serves both without bank conflicts:
+// chunk c of row r is stored at c ^ (4 (t % (CPR/4)) + (t / (CPR/4)) % 4), t = r / RPG (CPR = d/8 chunks per row,
+// RPG = 16/CPR rows per 256 bytes).
+#include "fa_gfx950.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32;                   // rows per wave: query rows (dq) or keys (dk, dv)
+constexpr int kBwdBlock = kBwdWaves * kBwdRows;  // rows per workgroup
+constexpr int kBwdTile = 64;                   // rows per LDS tile: keys (dq) or query rows (dk, dv)
+constexpr int kWsTileBytes = 1024;             // LDS for one tile of workspace pairs (64 x 8 bytes, padded)
+
+__host__ __device__ constexpr int ws_rows(int N) { return (N + kBwdTile - 1) / kBwdTile * kBwdTile; }
+
+template <int D>
+struct BwdTile {
+  static constexpr int RB = 2 * D;      // bytes per row
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int RPG = 16 / CPR;  // rows per 256 bytes
+  static constexpr int Q4 = CPR / 4;
+  static constexpr int kBytes = kBwdTile * RB;
+  static constexpr int kInsts = kBytes / 1024;  // wave-instructions to copy one tile
+  __device__ static constexpr int swz(int r) { return 4 * ((r / RPG) % Q4) + ((r / RPG) / Q4) % 4; }
+  // byte offset of bf16 element (r, col) of the tile
+  __device__ static constexpr int at(int r, int col) { return r * RB + ((col / 8) ^ swz(r)) * 16 + (col % 8) * 2; }
+};
+
+__device__ __forceinline__ int swap_bits23(int l) { return (l & ~12) | ((l & 4) << 1) | ((l & 8) >> 1); }
+
+// 8 consecutive rows (8h .. 8h+7 of a 16-row step) of one 32-column block, transposed: two ds_read_b64_tr_b16.
+__device__ __forceinline__ bf16x8 read_tr8(const lds_char* p0, const lds_char* p1) {
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p0));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p1));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)a[e], (float)b[e], s);
+  return s;
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// dq (and the workspace pairs D_i, lse_i*log2e)
+// ------------------------------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ o, const float* __restrict__ lse, const __bf16* __restrict__ dout,
+    __bf16* __restrict__ dq, float* __restrict__ ws, int N, int BH, float scale, int group) {
+  using T = BwdTile<D>;
+  constexpr int NW = kBwdWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
+  static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  lds_char* const kst = (lds_char*)smem_raw;  // 2 K stages
+  lds_char* const vst = kst + 2 * T::kBytes;  // 2 V stages
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nq = gridDim.x;
+  int bh, qb;
+  map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
+  const size_t head_off = (size_t)bh * (size_t)N * D;
+  const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;
+  const __bf16* kh = k + kv_off;
+  const __bf16* vh = v + kv_off;
+
+  const int q_lo = qb * kBwdBlock;
+  const int q_last = min(q_lo + kBwdBlock, N) - 1;
+  const int n_tiles = CAUSAL ? (q_last / kBwdTile + 1) : (N + kBwdTile - 1) / kBwdTile;
+  const int q0w = q_lo + wave * kBwdRows;
+  const int my_q = q0w + l32;
+  const int wave_tiles =
+      (q0w >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kBwdRows - 1) / kBwdTile + 1) : n_tiles);
+
+  // This lane's query row: q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T), and D_i = dO_i . o_i
+  bf16x8 qf[kDB], df[kDB];
+  float dpart = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < kDB; ++kb) {
+    if (my_q < N) {
+      const size_t e = head_off + (size_t)my_q * D + 16 * kb + 8 * h;
+      qf[kb] = *(const bf16x8*)(q + e);
+      df[kb] = *(const bf16x8*)(dout + e);
+      dpart += dot8(df[kb], *(const bf16x8*)(o + e));
+    } else {
+      qf[kb] = (bf16x8){};
+      df[kb] = (bf16x8){};
+    }
+  }
+  const float Di = pair_sum32(dpart);
+  // rows past N: lse2 = +inf makes every p of the row exactly 0 (D is 0 there: dO was not loaded)
+  const float lse2 = (my_q < N) ? lse[(size_t)bh * N + my_q] * kLog2e : INFINITY;
+  const int npad = ws_rows(N);
+  if (my_q < npad && h == 0) {
+    float2* w = (float2*)ws + (size_t)bh * npad + my_q;
+    *w = make_float2(Di, lse2);
+  }
+
+  // LDS-DMA: copy instruction p of this wave writes chunk positions (wave + NW p)*64 + lane of the tile
+  int dma[kCopies];
+#pragma unroll
+  for (int p = 0; p < kCopies; ++p) {
+    const int pos = (wave + NW * p) * 64 + lane;
+    const int row = pos / T::CPR, phys = pos % T::CPR;
+    dma[p] = row * T::RB + (phys ^ T::swz(row)) * 16;
+  }
+  auto copy_tile = [&](const __bf16* src, lds_char* dst, int j) __attribute__((always_inline)) {
+    const int row0 = j * kBwdTile;
+    // rows past N arrive as zeros; scalar byte count and base keep the descriptor in scalar registers
+    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kBwdTile)) * T::RB);
+    const int row_base = __builtin_amdgcn_readfirstlane(min(row0, N - 1));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * D, bytes);
+#pragma unroll
+    for (int p = 0; p < kCopies; ++p) lds_copy16_inline(r, dst + (wave + NW * p) * 1024, dma[p]);
+  };
+
+  // Row reads of K and V (A operands): row 32b + swap_bits23(l32), columns 16kb + 8h .. +7. The swizzle depends
+  // on the row only modulo 16 here, so one offset per kb serves both 32-key blocks.
+  const int krow = swap_bits23(l32);
+  int row_off[kDB];
+#pragma unroll
+  for (int kb = 0; kb < kDB; ++kb) row_off[kb] = T::at(krow, 16 * kb + 8 * h);
+  // Transposing reads of K (A operand of dQ^T = K^T dS^T): rows 16m + 8h + 4 half + (lane&15)/4, columns
+  // 32cb + 16((lane>>4)&1) + 4(lane&3); the swizzle does not depend on m.
+  int tr_off[kCB][2];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      tr_off[cb][half] =
+          T::at(8 * h + 4 * half + (lane & 15) / 4, 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+  const float c2 = scale * kLog2e;
+  f32x16 acc[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) acc[cb] = (f32x16){};
+
+  // One 64-key tile from the stage at byte `at`. Value r of block b is key j*64 + 32b + 16(r/8) + 8h + r%8.
+  auto compute = [&](int j, int at) __attribute__((always_inline)) {
+    const lds_char* ks = kst + at;
+    const lds_char* vs = vst + at;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = (f32x16){};
+      dp[b] = (f32x16){};
+#pragma unroll
+      for (int kb = 0; kb < kDB; ++kb) {
+        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(ks + 32 * b * T::RB + row_off[kb]);
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s[b], 0, 0, 0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < kDB; ++kb) {
+        const bf16x8 vf = *(const __attribute__((address_space(3))) bf16x8*)(vs + 32 * b * T::RB + row_off[kb]);
+        dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kb], dp[b], 0, 0, 0);
+      }
+    }
+    const int kv0 = j * kBwdTile;
+    if ((kv0 + kBwdTile > N) || (CAUSAL && kv0 + kBwdTile - 1 > q0w)) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
+          const bool vis = (key < N) && (!CAUSAL || key <= my_q);
+          s[b][r] = vis ? s[b][r] : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x8 x = (m & 1) ? s[m >> 1].hi : s[m >> 1].lo;
+      const f32x8 y = (m & 1) ? dp[m >> 1].hi : dp[m >> 1].lo;
+      f32x8 ds;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -lse2));
+        ds[e] = p * (y[e] - Di);
+      }
+      const bf16x8 dsb = __builtin_convertvector(ds, bf16x8);
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        const bf16x8 kt = read_tr8(ks + 16 * m * T::RB + tr_off[cb][0], ks + 16 * m * T::RB + tr_off[cb][1]);
+        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb, acc[cb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Two-stage ring: copy tile j+1 while tile j is computed; one barrier per tile.
+  auto step = [&](int j, int S) __attribute__((always_inline)) {
+    if (j + 1 < n_tiles) {
+      copy_tile(kh, kst + (S ^ 1) * T::kBytes, j + 1);
+      copy_tile(vh, vst + (S ^ 1) * T::kBytes, j + 1);
+    }
+    if (j < wave_tiles) compute(j, S * T::kBytes);
+    wait_copies_and_barrier<0>();
+  };
+  if (n_tiles > 0) {
+    copy_tile(kh, kst, 0);
+    copy_tile(vh, vst, 0);
+    wait_copies_and_barrier<0>();
+  }
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, 0);
+    if (j + 1 < n_tiles) step(j + 1, 1);
+  }
+
+  // dq_i = scale * acc; acc[cb][4g + i] is column 32cb + 8g + 4h + i of row my_q
+  if (my_q < N) {
+    __bf16* row = dq + head_off + (size_t)my_q * D;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = {acc[cb][4 * g] * scale, acc[cb][4 * g + 1] * scale, acc[cb][4 * g + 2] * scale,
+                         acc[cb][4 * g + 3] * scale};
+        *(bf16x4*)(row + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(x, bf16x4);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// dk, dv
+// ------------------------------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ ws, __bf16* __restrict__ dk,
+    __bf16* __restrict__ dv, int N, int BHkv, float scale, int group) {
+  using T = BwdTile<D>;
+  constexpr int NW = kBwdWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  lds_char* const qst = (lds_char*)smem_raw;     // 2 q stages
+  lds_char* const dst = qst + 2 * T::kBytes;      // 2 dO stages
+  lds_char* const wst = dst + 2 * T::kBytes;      // 2 workspace stages
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nk = gridDim.x;
+  int bkv, t;
+  map_workgroup(blockIdx.x + nk * blockIdx.y, nk, BHkv, 1, CAUSAL, bkv, t);
+  // causal: the first key blocks see the most query rows; map_workgroup hands out the last index first
+  const int kblk = CAUSAL ? nk - 1 - t : t;
+  const size_t kv_off = (size_t)bkv * (size_t)N * D;
+  const int bh0 = bkv * group;  // first query head of this key/value head's group
+
+  const int k0 = kblk * kBwdBlock;
+  const int kw0 = k0 + wave * kBwdRows;
+  const int my_k = kw0 + l32;
+
+  // This lane's key: k and v fragments (B operands of S = Q K^T and dP = dO V^T)
+  bf16x8 kf[kDB], vf[kDB];
+#pragma unroll
+  for (int kb = 0; kb < kDB; ++kb) {
+    if (my_k < N) {
+      const size_t e = kv_off + (size_t)my_k * D + 16 * kb + 8 * h;
+      kf[kb] = *(const bf16x8*)(k + e);
+      vf[kb] = *(const bf16x8*)(v + e);
+    } else {
+      kf[kb] = (bf16x8){};
+      vf[kb] = (bf16x8){};
+    }
+  }
+
+  int dma[kCopies];
+#pragma unroll
+  for (int p = 0; p < kCopies; ++p) {
+    const int pos = (wave + NW * p) * 64 + lane;
+    const int row = pos / T::CPR, phys = pos % T::CPR;
+    dma[p] = row * T::RB + (phys ^ T::swz(row)) * 16;
+  }
+  // query tiles: t0 .. nqt-1 of each of the group's query heads (causal: none entirely before this block's keys)
+  const int nqt = (N + kBwdTile - 1) / kBwdTile;
+  const int t0 = CAUSAL ? k0 / kBwdTile : 0;
+  const int per_head = nqt - t0;
+  const int n_iter = (k0 < N) ? group * per_head : 0;
+  const int npad = ws_rows(N);
+  auto copy_iter = [&](int it, int S) __attribute__((always_inline)) {
+    const int hq = bh0 + it / per_head;
+    const int row0 = (t0 + it % per_head) * kBwdTile;
+    const size_t base = (size_t)hq * N;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kBwdTile)));
+    const int row_base = __builtin_amdgcn_readfirstlane(min(row0, N - 1));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (base + row_base) * D, rows * T::RB);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + (base + row_base) * D, rows * T::RB);
+#pragma unroll
+    for (int p = 0; p < kCopies; ++p) {
+      lds_copy16_inline(rq, qst + S * T::kBytes + (wave + NW * p) * 1024, dma[p]);
+      lds_copy16_inline(rd, dst + S * T::kBytes + (wave + NW * p) * 1024, dma[p]);
+    }
+    if (wave == 0) {  // the tile's 64 pairs (512 bytes, always inside the padded workspace); lanes 32..63 fall
+                      // outside the descriptor and write zeros to the unused upper half of the LDS slot
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + 2 * ((size_t)hq * npad + row0), kBwdTile * 8);
+      lds_copy16_inline(rw, wst + S * kWsTileBytes, lane * 16);
+    }
+  };
+
+  // Row reads of q and dO (A operands): row 32sb + swap_bits23(l32), columns 16kb + 8h .. +7
+  const int qrow = swap_bits23(l32);
+  int row_off[kDB];
+#pragma unroll
+  for (int kb = 0; kb < kDB; ++kb) row_off[kb] = T::at(qrow, 16 * kb + 8 * h);
+  // Transposing reads of dO and q (A operands of dV^T = dO^T P and dK^T = Q^T dS)
+  int tr_off[kCB][2];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      tr_off[cb][half] =
+          T::at(8 * h + 4 * half + (lane & 15) / 4, 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
+  const float c2 = scale * kLog2e;
+  f32x16 dk_acc[kCB], dv_acc[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    dk_acc[cb] = (f32x16){};
+    dv_acc[cb] = (f32x16){};
+  }
+
+  // One 64-row query tile (two 32-row sub-blocks) from stage S. In S and dP, lane = key my_k and value r of a
+  // sub-block is query row 16(r/8) + 8h + r%8 of that sub-block (q and dO rows fed in swap_bits23 order).
+  auto compute = [&](int it, int S) __attribute__((always_inline)) {
+    const lds_char* qs = qst + S * T::kBytes;
+    const lds_char* ds_ = dst + S * T::kBytes;
+    const lds_char* wsl = wst + S * kWsTileBytes;
+    const int tile_row0 = (t0 + it % per_head) * kBwdTile;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int qlo = tile_row0 + 32 * sb;
+      if (qlo >= N || (CAUSAL && qlo + kBwdRows - 1 < kw0)) continue;  // no visible pair for this wave
+      f32x16 x = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int kb = 0; kb < kDB; ++kb) {
+        const bf16x8 qa =
+            *(const __attribute__((address_space(3))) bf16x8*)(qs + 32 * sb * T::RB + row_off[kb]);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb], x, 0, 0, 0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < kDB; ++kb) {
+        const bf16x8 da =
+            *(const __attribute__((address_space(3))) bf16x8*)(ds_ + 32 * sb * T::RB + row_off[kb]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kb], dp, 0, 0, 0);
+      }
+      if ((qlo + kBwdRows > N) || (CAUSAL && qlo < kw0 + kBwdRows - 1)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qlo + 16 * (r >> 3) + 8 * h + (r & 7);
+          const bool vis = (qi < N) && (!CAUSAL || my_k <= qi);
+          x[r] = vis ? x[r] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        // (D, lse2) of query rows 32sb + 16m + 8h .. +7 of the tile: 64 bytes, read by every lane of the half
+        const __attribute__((address_space(3))) f32x4* wp =
+            (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 16 * m + 8 * h) * 8);
+        f32x4 w4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w4[u] = wp[u];
+        const f32x8 xs = m ? x.hi : x.lo;
+        const f32x8 ys = m ? dp.hi : dp.lo;
+        f32x8 pv, dsv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float Dq = w4[e >> 1][2 * (e & 1)];
+          const float l2 = w4[e >> 1][2 * (e & 1) + 1];
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[e], c2, -l2));
+          dsv[e] = pv[e] * (ys[e] - Dq);
+        }
+        const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+        const bf16x8 dsb = __builtin_convertvector(dsv, bf16x8);
+        const int rbase = (32 * sb + 16 * m) * T::RB;
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) {
+          const bf16x8 dot_ = read_tr8(ds_ + rbase + tr_off[cb][0], ds_ + rbase + tr_off[cb][1]);
+          dv_acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot_, pb, dv_acc[cb], 0, 0, 0);
+          const bf16x8 qt = read_tr8(qs + rbase + tr_off[cb][0], qs + rbase + tr_off[cb][1]);
+          dk_acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsb, dk_acc[cb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto step = [&](int it, int S) __attribute__((always_inline)) {
+    if (it + 1 < n_iter) copy_iter(it + 1, S ^ 1);
+    compute(it, S);
+    wait_copies_and_barrier<0>();
+  };
+  if (n_iter > 0) {
+    copy_iter(0, 0);
+    wait_copies_and_barrier<0>();
+  }
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, 0);
+    if (it + 1 < n_iter) step(it + 1, 1);
+  }
+
+  // dk_j = scale * dk_acc, dv_j = dv_acc; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k
+  if (my_k < N) {
+    __bf16* rk = dk + kv_off + (size_t)my_k * D;
+    __bf16* rv = dv + kv_off + (size_t)my_k * D;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 a = {dk_acc[cb][4 * g] * scale, dk_acc[cb][4 * g + 1] * scale, dk_acc[cb][4 * g + 2] * scale,
+                         dk_acc[cb][4 * g + 3] * scale};
+        const f32x4 b = {dv_acc[cb][4 * g], dv_acc[cb][4 * g + 1], dv_acc[cb][4 * g + 2], dv_acc[cb][4 * g + 3]};
+        *(bf16x4*)(rk + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(a, bf16x4);
+        *(bf16x4*)(rv + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(b, bf16x4);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------------------
+// launcher (arguments already validated by the C ABI layer)
+// ------------------------------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv,
+                             int N, float scale, hipStream_t stream) {
+  using T = BwdTile<D>;
+  const int group = H / Hkv;
+  constexpr int lds_a = 4 * T::kBytes;
+  constexpr int lds_b = 4 * T::kBytes + 2 * kWsTileBytes;
+  auto ka = fa_bwd_dq_kernel<D, CAUSAL>;
+  auto kb = fa_bwd_dkdv_kernel<D, CAUSAL>;
+  hipError_t e = hipFuncSetAttribute((const void*)ka, hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)kb, hipFuncAttributeMaxDynamicSharedMemorySize, lds_b);
+  if (e != hipSuccess) return e;
+  const unsigned nblk = (unsigned)((N + kBwdBlock - 1) / kBwdBlock);
+  hipLaunchKernelGGL(ka, dim3(nblk, (unsigned)(B * H)), dim3(kBwdThreads), lds_a, stream, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse, (const __bf16*)dout, (__bf16*)dq, ws,
+                     N, B * H, scale, group);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv)), dim3(kBwdThreads), lds_b, stream, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const float*)ws, (__bf16*)dk,
+                     (__bf16*)dv, N, B * Hkv, scale, group);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv, int N,
+                           int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream)
+                  : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream);
+  return causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream)
+                : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,96 @@
+// fa_gfx950.h -- device helpers shared by the attention kernels for gfx950 (MI355X, CDNA4): vector types,
+// lane-pair reductions, raw buffer descriptors, LDS-DMA tile copies and the copy-wait barrier.
+#ifndef FA_MI355X_FA_GFX950_H
+#define FA_MI355X_FA_GFX950_H
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with the lower 32 lanes of its second.
+// Fed x twice, every lane ends up holding {x[l], x[l ^ 32]} across the two results, in an order that depends
+// on the half; max and sum of the two are therefore the pair reductions for every lane.
+__device__ __forceinline__ float pair_max32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zero (also when the
+// destination is LDS). gfx9-family descriptor flags word. Only the per-lane offset is range-checked, so a tile's
+// start goes into the base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// One LDS-DMA copy: each lane moves 16 bytes from the descriptor's range at byte offset `off` to
+// lds_base + 16 * lane (lds_base must be the same for the whole wave). Kept in a plain (non-template) function:
+// written directly inside the kernel template, the builtin made the host compilation pass drop the kernel's
+// launch stub without a diagnostic.
+__device__ __forceinline__ void lds_copy16_inline(__amdgpu_buffer_rsrc_t r, lds_char* lds_base, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+
+// Workgroup -> (head bh, query block qb). Workgroups are dispatched to XCDs round-robin by linear id. When B*H
+// is a multiple of 8, XCD x takes the key/value heads x, x+8, x+16, ... (each with its `group` query heads) when
+// their count is a multiple of 8, else the query heads x, x+8, ...: a group's query heads share an L2, and heads
+// of every batch run on every XCD (per-batch work differs under key padding).
+__device__ __forceinline__ void map_workgroup(int lin, int nq, int bh_count, int group, bool causal, int& bh,
+                                              int& qb) {
+  if ((bh_count & 7) == 0) {
+    const int xcd = lin & 7, t = lin >> 3, per = bh_count >> 3;  // heads per XCD
+    int jh;                                                      // this XCD's jh-th head
+    if (causal) {
+      qb = nq - 1 - t / per;
+      jh = t % per;
+    } else {
+      jh = t / nq;
+      qb = t % nq;
+    }
+    bh = ((bh_count / group) & 7) == 0 ? (xcd + 8 * (jh / group)) * group + jh % group : xcd + 8 * jh;
+  } else {
+    if (causal) {
+      qb = nq - 1 - lin / bh_count;
+      bh = lin % bh_count;
+    } else {
+      bh = lin / nq;
+      qb = lin % nq;
+    }
+  }
+}
+
+template <int V>
+using Int = std::integral_constant<int, V>;
+
+// Wait until at most N vector-memory operations of this wave are outstanding (the LDS-DMA copies), then join
+// the workgroup. The barrier is written as a statement with a memory clobber: the compiler may not move memory
+// accesses across it, and no fence is emitted (a release fence would wait for every copy in flight, including
+// the ones meant to overlap the next tile).
+template <int N>
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0 (LDS reads done)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+}  // namespace fa
+#endif

@@ -1,5 +1,5 @@
 /*
- * fa.h -- C ABI of the exact fused attention forward for AMD gfx950 (MI355X).
+ * fa.h -- C ABI of the exact fused attention forward (and its gradients) for AMD gfx950 (MI355X).
  *
  * Operation. For every batch b, head h and query row i:
  *     s_ij   = scale * q_i . k_j                  (j visible: all j, or j <= i when causal)
@@ -22,13 +22,14 @@
  * Layout. q, k, v, o are [B, H, N, d] contiguous row-major (element (b,h,i,c)
  * at ((b*H + h)*N + i)*d + c). lse is [B, H, N] contiguous fp32.
  *
- * Ownership. The caller allocates every buffer in device memory and keeps it
- * alive until the stream has run the work. The library allocates nothing, keeps
- * no state between calls, and never synchronises: it validates the arguments on
- * the host, enqueues exactly one kernel on `stream` (0 = null stream) and
- * returns. Results are valid once the caller synchronises the stream. q, k and v
- * are only read; o and lse are only written. Calls are thread-safe, and the
- * same inputs give bitwise-identical outputs on every call (no atomics, no
+ * Ownership. The caller allocates every buffer in device memory (including
+ * fa_bwd's workspace) and keeps it alive until the stream has run the work.
+ * The library allocates nothing, keeps no state between calls, and never
+ * synchronises: it validates the arguments on the host, enqueues its kernels
+ * on `stream` (0 = null stream; one kernel for a forward call, two for fa_bwd)
+ * and returns. Results are valid once the caller synchronises the stream.
+ * Inputs are only read; outputs are only written. Calls are thread-safe, and
+ * the same inputs give bitwise-identical outputs on every call (no atomics, no
  * split over keys).
  *
  * Errors. 0 on success; otherwise one of the FA_ERR_* codes below, and nothing
@@ -41,6 +42,7 @@
 #define FA_MI355X_FA_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -50,9 +52,9 @@ extern "C" {
 #define FA_ERR_NULL 1    /* a pointer is NULL (non-empty problem) */
 #define FA_ERR_SHAPE 2   /* B, H, N or H_kv negative; B*H over 65535; N over 2^30; H_kv not dividing H */
 #define FA_ERR_HEADDIM 3 /* d is not 64 or 128 */
-#define FA_ERR_ALIGN 4   /* q, k, v or o not 16-byte aligned, or lse / kv_len not 4-byte aligned */
+#define FA_ERR_ALIGN 4   /* a tensor or the workspace not 16-byte aligned, or lse / kv_len not 4-byte aligned */
 #define FA_ERR_ARG 5     /* scale not finite or not > 0, or causal not 0/1 */
-#define FA_ERR_ALIAS 6   /* o or lse overlaps q, k, v or kv_len, or o overlaps lse */
+#define FA_ERR_ALIAS 6   /* an output overlaps an input or another output */
 #define FA_ERR_HIP 7     /* the HIP runtime reported an error at launch */
 
 /*
@@ -101,6 +103,41 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse, const int* kv_len, int B, int H,
                 int H_kv, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * fa_bwd -- gradients of fa_fwd / fa_fwd_gqa (bf16 tensors, fp32 arithmetic).
+ * The pages name a faster backward pass that recomputes attention from stored
+ * statistics instead of storing the attention matrix (unite.ai page, the key
+ * ideas after "Enter Flash Attention", item 2; section "FlashAttention-2",
+ * item 2); no formula is printed. With lse and o from the forward and an
+ * upstream gradient dout of o (none for lse), per visible (i, j):
+ *     p_ij = exp(scale q_i.k_j - lse_i)      D_i = dout_i . o_i
+ *     dS_ij = p_ij (dout_i . v_j - D_i)
+ *     dq_i = scale sum_j dS_ij k_j   dk_j = scale sum_i dS_ij q_i   dv_j = sum_i p_ij dout_i
+ * dk and dv of a key/value head sum over the H / H_kv query heads that read it.
+ *   q, o, dout : const bf16 [B,H,N,d] (device); o is fa_fwd's output for q, k, v
+ *   k, v       : const bf16 [B,H_kv,N,d] (device)
+ *   lse        : const float [B,H,N] (device), fa_fwd's lse for the same call
+ *   dq         : bf16 [B,H,N,d] (device, written)
+ *   dk, dv     : bf16 [B,H_kv,N,d] (device, written)
+ *   workspace  : device memory of fa_bwd_workspace_bytes(B, H, N) bytes,
+ *                16-byte aligned, overwritten (no contents needed on entry
+ *                or kept on return); calls that share a workspace must be
+ *                ordered on one stream
+ *   B, H, H_kv, N, d, causal, scale : as fa_fwd_gqa (same values as the forward call)
+ * Enqueues two kernels on `stream` (dq, then dk and dv); no atomics, so the
+ * same inputs give bitwise-identical gradients. p and dS are rounded to bf16
+ * before their matrix products, the gradients once at the end. Errors as
+ * fa_fwd, with every tensor and the workspace checked (NULL, 16-byte
+ * alignment) and no output (dq, dk, dv, workspace) allowed to overlap an
+ * input or another output (FA_ERR_ALIAS).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* workspace, int B, int H, int H_kv, int N, int d, int causal, float scale,
+           hipStream_t stream);
+
+/* fa_bwd_workspace_bytes -- bytes of the fa_bwd workspace (0 for an empty problem). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*
  * fa_fwd_f32 -- the same operation with fp32 q, k, v and o. Products and sums

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 10100
+    assert fa.fa_version() == 10200
     for code in range(8):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
@@ -113,6 +113,44 @@ def test_empty_problem_is_a_no_op_that_ignores_pointers(fn):
     # scalar arguments are still checked on an empty problem
     assert _call(fn, N=0, d=80) == fa.FA_ERR_HEADDIM
     assert _call(fn, N=0, scale=0.0) == fa.FA_ERR_ARG
+
+
+BWD = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, dout=A + 0x5000000,
+           dq=A + 0x6000000, dk=A + 0x7000000, dv=A + 0x8000000, ws=A + 0x9000000)
+
+
+def _bwd(B=1, H=2, H_kv=2, N=64, d=64, causal=0, scale=0.125, **ptrs):
+    p = dict(BWD, **ptrs)
+    return fa.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"], p["dv"], p["ws"], B, H,
+                     H_kv, N, d, causal, scale, 0)
+
+
+def test_backward_error_codes():
+    for name in BWD:
+        assert _bwd(**{name: 0}) == fa.FA_ERR_NULL, name
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv", "ws"):
+        assert _bwd(**{name: BWD[name] + 8}) == fa.FA_ERR_ALIGN, name
+    assert _bwd(lse=BWD["lse"] + 2) == fa.FA_ERR_ALIGN
+    assert _bwd(d=96) == fa.FA_ERR_HEADDIM
+    assert _bwd(H_kv=3) == fa.FA_ERR_SHAPE
+    assert _bwd(N=-1) == fa.FA_ERR_SHAPE
+    assert _bwd(scale=0.0) == fa.FA_ERR_ARG
+    assert _bwd(causal=3) == fa.FA_ERR_ARG
+    assert _bwd(dq=BWD["q"]) == fa.FA_ERR_ALIAS                  # dq is q
+    assert _bwd(dk=BWD["dv"] + 4096) == fa.FA_ERR_ALIAS           # dk overlaps dv (16 KiB each)
+    assert _bwd(ws=BWD["o"] + 1024) == fa.FA_ERR_ALIAS            # workspace inside o
+    assert _bwd(dv=BWD["lse"] - 16) == fa.FA_ERR_ALIAS            # dv runs into lse
+    assert _bwd(ws=BWD["dq"] - 16) == fa.FA_ERR_ALIAS             # workspace runs into dq
+    # empty problem: success, pointers ignored
+    assert _bwd(N=0, **{name: 0 for name in BWD}) == fa.FA_OK
+
+
+def test_backward_workspace_bytes():
+    # (D, lse*log2e) float pairs per query row, rows rounded up to 64 per head
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 128 * 8
+    assert fa.fa_bwd_workspace_bytes(1, 1, 64) == 64 * 8
+    assert fa.fa_bwd_workspace_bytes(1, 32, 16384) == 32 * 16384 * 8
+    assert fa.fa_bwd_workspace_bytes(0, 3, 100) == 0 and fa.fa_bwd_workspace_bytes(1, 1, -5) == 0
 
 
 def test_python_wrapper_rejects_cpu_tensors():

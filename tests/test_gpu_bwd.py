@@ -1,0 +1,176 @@
+"""Parity of the gradient kernels (fa_bwd, through the C ABI) with the fp64 gradient oracle, on the GPU.
+
+Tolerance: for each of dq, dk, dv, max |g_gpu - g_oracle| <= 2e-2 * max |g_oracle| + 1e-5 (the forward's 2e-2
+bound, taken at the scale of each gradient tensor: unlike o, gradients grow with N and with dO; the absolute
+1e-5 covers gradients that vanish exactly, e.g. dq and dk with a single key, where dS = p (dO.v - dO.o) is a
+difference of two fp32 dot products of size ~|dO||v| that cancel to rounding noise). The arithmetic behind the
+relative part: p and dS are rounded to bf16 (relative 2^-9) before their products and each gradient once at
+the end (2^-9), with fp32 accumulation; the observed error is reported by every case. The forward that feeds the
+backward is the library's own (o, lse); the oracle recomputes everything from q, k, v, dO.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 2e-2
+ATOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_13_amd as fa_mod
+    return fa_mod
+
+
+def _dout(B, H, N, d, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _inputs(B, H, Hkv, N, d, seed):
+    q, k, v = ai.make_qkv(B, H, N, d, seed, "bf16", Hkv=Hkv)
+    return q, k, v, _dout(B, H, N, d, seed + 500)
+
+
+def _run(fa, q, k, v, dout, causal, scale):
+    qd, kd, vd, dd = (t.to("cuda:0") for t in (q, k, v, dout))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check(label, got, ref):
+    g = got.float().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    assert np.all(np.isfinite(g)), label
+    err = float(np.abs(g - ref).max())
+    mag = float(np.abs(ref).max())
+    rms = float(np.sqrt(np.mean((g - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-300))
+    print(f"[parity] {label} max|err|={err:.3e} max|ref|={mag:.3e} rel={err / max(mag, 1e-300):.3e} "
+          f"rel_rms={rms:.3e}", flush=True)
+    assert err <= RTOL * mag + ATOL, f"{label}: error {err} above {RTOL} x {mag} + {ATOL}"
+
+
+def _full(fa, B, H, Hkv, N, d, causal, seed, label):
+    q, k, v, dout = _inputs(B, H, Hkv, N, d, seed)
+    scale = ai.default_scale(d)
+    dq, dk, dv = _run(fa, q, k, v, dout, causal, scale)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, dout, causal, scale)
+    _check(f"{label} dq", dq, rq)
+    _check(f"{label} dk", dk, rk)
+    _check(f"{label} dv", dv, rv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 7, 63, 64, 65, 130, 333, 1000])
+def test_backward_ragged(fa, N, d, causal):
+    label = f"bwd B2 H2 N{N} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    _full(fa, 2, 2, 2, N, d, causal, 400 + N, label)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hkv", [4, 1])
+def test_backward_grouped_heads(fa, Hkv, d, causal):
+    label = f"bwd B2 H8 Hkv{Hkv} N333 d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    _full(fa, 2, 8, Hkv, 333, d, causal, 450 + Hkv, label)
+
+
+@pytest.mark.parametrize("H,Hkv,causal", [(16, 16, False), (16, 16, True), (16, 4, True)])
+def test_backward_large_sampled_rows(fa, H, Hkv, causal):
+    """B2 N2048 d128: 192 dq rows and 192 dk/dv rows of four heads, plus the first and last rows."""
+    B, N, d = 2, 2048, 128
+    label = f"bwd B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v, dout = _inputs(B, H, Hkv, N, d, 470)
+    scale = ai.default_scale(d)
+    dq, dk, dv = _run(fa, q, k, v, dout, causal, scale)
+    g = torch.Generator("cpu").manual_seed(471)
+    qh = [0, 5, H + 3, 2 * H - 1]
+    kh = [0, 1, Hkv + Hkv // 2, 2 * Hkv - 1]
+    qr = np.unique(np.concatenate([np.array(qh)[:, None] * N + np.array([[0, 1, 127, 128, N - 1]]),
+                                   (np.array(qh)[torch.randint(0, 4, (192,), generator=g).numpy()] * N
+                                    + torch.randint(0, N, (192,), generator=g).numpy())[:, None]], axis=None))
+    kr = np.unique(np.concatenate([np.array(kh)[:, None] * N + np.array([[0, 1, 127, 128, N - 1]]),
+                                   (np.array(kh)[torch.randint(0, 4, (192,), generator=g).numpy()] * N
+                                    + torch.randint(0, N, (192,), generator=g).numpy())[:, None]], axis=None))
+    rq, rk, rv = oracle.attention_bwd_rows(q, k, v, dout, causal, scale, q_rows=qr, kv_rows=kr)
+    _check(f"{label} dq", dq.reshape(-1, d)[torch.from_numpy(qr).to(dq.device)], rq)
+    _check(f"{label} dk", dk.reshape(-1, d)[torch.from_numpy(kr).to(dk.device)], rk)
+    _check(f"{label} dv", dv.reshape(-1, d)[torch.from_numpy(kr).to(dv.device)], rv)
+
+
+def test_backward_is_deterministic(fa):
+    q, k, v, dout = _inputs(2, 8, 2, 1000, 128, 480)
+    a = _run(fa, q, k, v, dout, True, ai.default_scale(128))
+    b = _run(fa, q, k, v, dout, True, ai.default_scale(128))
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_zero_query_closed_forms(fa, causal):
+    """q = 0: dk = scale * sum_i dS_ij q_i is exactly 0; dv_j = sum of dO_i / |J_i| over the queries that see j."""
+    B, H, N, d = 1, 2, 200, 64
+    _, k, v, dout = _inputs(B, H, H, N, d, 485)
+    q = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    dq, dk, dv = _run(fa, q, k, v, dout, causal, ai.default_scale(d))
+    assert torch.count_nonzero(dk) == 0
+    do = dout.to(torch.float64).numpy()
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    w = do / cnt[None, None, :, None]
+    ref = np.flip(np.cumsum(np.flip(w, axis=2), axis=2), axis=2) if causal else np.broadcast_to(
+        w.sum(axis=2, keepdims=True), w.shape)
+    _check(f"bwd q=0 causal={causal} dv", dv, ref)
+
+
+def test_backward_raw_entry_point_and_errors(fa):
+    B, H, Hkv, N, d = 1, 4, 2, 100, 64
+    q, k, v, dout = (t.to("cuda:0") for t in _inputs(B, H, Hkv, N, d, 490))
+    o, lse = fa.forward(q, k, v, causal=True)
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, N),), dtype=torch.uint8, device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    sc = ai.default_scale(d)
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, Hkv, N, d, 1, sc, stream)
+    assert rc == fa.FA_OK
+    ref = fa.backward(q, k, v, o, lse, dout, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+    assert fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                     q.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, Hkv, N, d, 1, sc,
+                     stream) == fa.FA_ERR_ALIAS
+
+
+def test_backward_writes_nothing_outside_its_outputs(fa):
+    """Outputs carved from one buffer between canary bands: every canary byte survives."""
+    B, H, N, d = 1, 2, 130, 64
+    q, k, v, dout = (t.to("cuda:0") for t in _inputs(B, H, H, N, d, 495))
+    o, lse = fa.forward(q, k, v, causal=False)
+    n = B * H * N * d
+    pad = 4096
+    buf = torch.full((3 * n + 4 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda:0")
+    views = [buf[pad + i * (n + pad): pad + i * (n + pad) + n].view(B, H, N, d) for i in range(3)]
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, N),), dtype=torch.uint8, device="cuda:0")
+    rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                   views[0].data_ptr(), views[1].data_ptr(), views[2].data_ptr(), ws.data_ptr(), B, H, H, N, d, 0,
+                   ai.default_scale(d), torch.cuda.current_stream().cuda_stream)
+    assert rc == fa.FA_OK
+    torch.cuda.synchronize()
+    mask = torch.ones_like(buf, dtype=torch.bool)
+    for i in range(3):
+        mask[pad + i * (n + pad): pad + i * (n + pad) + n] = False
+    assert torch.all(buf[mask] == 1234.0)
+    ref = fa.backward(q, k, v, o, lse, dout)
+    torch.cuda.synchronize()
+    assert all(torch.equal(views[i], ref[i]) for i in range(3))
