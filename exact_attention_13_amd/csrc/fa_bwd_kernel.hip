@@ -14,12 +14,14 @@
 //     own lse and D; dQ^T += K^T dS^T takes dS^T from registers as the B operand and K^T by transposing LDS reads
 //     (ds_read_b64_tr_b16). It also computes D_i from the o and dO rows it loads anyway and writes (D_i,
 //     lse_i*log2e) to the workspace.
-//   * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys (4 waves x 32 keys) of one key/value head; query
-//     tiles of 64 rows (q, dO and the workspace pairs) of every query head of the group stream through LDS.
-//     S = Q K^T and dP = dO V^T put one key in each lane (K and V rows stay in registers as the B operands);
-//     dV^T += dO^T P and dK^T += Q^T dS take P and dS from registers as B operands and dO^T, Q^T by transposing
-//     LDS reads.
-// The workspace holds the pairs (D_i, lse_i*log2e) as [B*H][Npad] float2, Npad = N rounded up to 64; rows
+//   * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys of one key/value head, 8 waves: each block of 32
+//     keys belongs to a pair of waves on one SIMD, one accumulating dV (from S and p), the other dK (from dP and
+//     dS), so each holds half the accumulators and two waves share every SIMD. Query tiles of 128 rows (q, dO
+//     and the workspace pairs) of every query head of the group stream through LDS. S = Q K^T and dP = dO V^T
+//     put one key in each lane (K or V rows stay in registers as the B operand); dV^T += dO^T P and
+//     dK^T += Q^T dS take P and dS from registers as B operands and dO^T, Q^T by transposing LDS reads; p
+//     passes from the first wave of the pair to the second through LDS.
+// The workspace holds the pairs (D_i, lse_i*log2e) as [B*H][Npad] float2, Npad = N rounded up to 128; rows
 // N .. Npad-1 hold (0, +inf), which makes p (and dS) of those rows exactly 0 in the dk/dv kernel.
 // S and dP are computed in both kernels (7 matrix products instead of the 5 of a single pass with atomic dq
 // updates): the price of determinism.
@@ -37,18 +39,20 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32;                   // rows per wave: query rows (dq) or keys (dk, dv)
 constexpr int kBwdBlock = kBwdWaves * kBwdRows;  // rows per workgroup
-constexpr int kBwdTile = 64;                   // rows per LDS tile: keys (dq) or query rows (dk, dv)
-constexpr int kWsTileBytes = 1024;             // LDS for one tile of workspace pairs (64 x 8 bytes, padded)
+constexpr int kBwdTile = 64;                   // keys per LDS tile (dq)
+constexpr int kWsTileBytes = 1024;             // LDS slot for one tile of workspace pairs (one copy: 64 x 16 B)
 
-__host__ __device__ constexpr int ws_rows(int N) { return (N + kBwdTile - 1) / kBwdTile * kBwdTile; }
+// Workspace rows per head: N rounded up to the dq workgroup's 128 rows (its grid writes exactly these rows),
+// which is also a whole number of the dk/dv kernel's 64-row query tiles.
+__host__ __device__ constexpr int ws_rows(int N) { return (N + kBwdBlock - 1) / kBwdBlock * kBwdBlock; }
 
-template <int D>
+template <int D, int ROWS = kBwdTile>
 struct BwdTile {
   static constexpr int RB = 2 * D;      // bytes per row
   static constexpr int CPR = D / 8;     // 16-byte chunks per row
   static constexpr int RPG = 16 / CPR;  // rows per 256 bytes
   static constexpr int Q4 = CPR / 4;
-  static constexpr int kBytes = kBwdTile * RB;
+  static constexpr int kBytes = ROWS * RB;
   static constexpr int kInsts = kBytes / 1024;  // wave-instructions to copy one tile
   __device__ static constexpr int swz(int r) { return 4 * ((r / RPG) % Q4) + ((r / RPG) / Q4) % 4; }
   // byte offset of bf16 element (r, col) of the tile
@@ -62,6 +66,19 @@ __device__ __forceinline__ bf16x8 read_tr8(const lds_char* p0, const lds_char* p
   const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p0));
   const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p1));
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Issue order for a block of n LDS-read-fed MFMAs (scheduling groups: 0x100 = LDS read, 0x008 = MFMA): 4 reads,
+// then one MFMA per further read, so each operand is read about four MFMAs before it is used.
+template <int n>
+__device__ __forceinline__ void schedule_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < n - 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
@@ -176,17 +193,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int b = 0; b < 2; ++b) {
       s[b] = (f32x16){};
       dp[b] = (f32x16){};
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int kb = 0; kb < kDB; ++kb) {
         const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(ks + 32 * b * T::RB + row_off[kb]);
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s[b], 0, 0, 0);
-      }
-#pragma unroll
-      for (int kb = 0; kb < kDB; ++kb) {
         const bf16x8 vf = *(const __attribute__((address_space(3))) bf16x8*)(vs + 32 * b * T::RB + row_off[kb]);
         dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[kb], dp[b], 0, 0, 0);
       }
-    }
+    schedule_reads_ahead<4 * kDB>();
     const int kv0 = j * kBwdTile;
     if ((kv0 + kBwdTile > N) || (CAUSAL && kv0 + kBwdTile - 1 > q0w)) {
 #pragma unroll
@@ -198,8 +215,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
           s[b][r] = vis ? s[b][r] : -INFINITY;
         }
     }
+    // dQ^T += K^T dS^T one 16-key step at a time; the K^T fragments of step m+1 are read during step m
+    auto read_kt = [&](int m, bf16x8(&kt)[kCB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+        kt[cb] = read_tr8(ks + 16 * m * T::RB + tr_off[cb][0], ks + 16 * m * T::RB + tr_off[cb][1]);
+    };
+    bf16x8 kta[kCB], ktb[kCB];
+    read_kt(0, kta);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      bf16x8(&cur)[kCB] = (m & 1) ? ktb : kta;
+      bf16x8(&nxt)[kCB] = (m & 1) ? kta : ktb;
       const f32x8 x = (m & 1) ? s[m >> 1].hi : s[m >> 1].lo;
       const f32x8 y = (m & 1) ? dp[m >> 1].hi : dp[m >> 1].lo;
       f32x8 ds;
@@ -209,11 +236,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
         ds[e] = p * (y[e] - Di);
       }
       const bf16x8 dsb = __builtin_convertvector(ds, bf16x8);
+      if (m < 3) read_kt(m + 1, nxt);
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) {
-        const bf16x8 kt = read_tr8(ks + 16 * m * T::RB + tr_off[cb][0], ks + 16 * m * T::RB + tr_off[cb][1]);
-        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb, acc[cb], 0, 0, 0);
-      }
+      for (int cb = 0; cb < kCB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[cb], dsb, acc[cb], 0, 0, 0);
     }
   };
 
@@ -253,20 +278,38 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 // ------------------------------------------------------------------------------------------------------------
 // dk, dv
 // ------------------------------------------------------------------------------------------------------------
+// Join the workgroup once this wave's LDS accesses are done (vector-memory copies may stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0), vmcnt and expcnt no wait
+  asm volatile("s_barrier" ::: "memory");
+}
+
+constexpr int kDkdvWaves = 8;   // 4 pairs of waves; the two waves of a pair share a SIMD and a block of 32 keys
+constexpr int kDkdvTile = 128;  // query rows per LDS tile: four 32-row sub-blocks
+constexpr int kPSlotBytes = 2 * 64 * 16;  // p of one 32 x 32 sub-block, bf16, as the two 16-row steps of 64 lanes
+
+// Waves w and w+4 run on the same SIMD and own the same 32 keys: the p wave (w < 4) computes S = Q K^T, p and
+// dV^T += dO^T P; the dS wave computes dP = dO V^T, then (after the sub-block's barrier) dS = p (dP - D) from the
+// p the other wave left in LDS, and dK^T += Q^T dS. Each holds half the accumulators, so two waves share a SIMD.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ ws, __bf16* __restrict__ dk,
     __bf16* __restrict__ dv, int N, int BHkv, float scale, int group) {
-  using T = BwdTile<D>;
-  constexpr int NW = kBwdWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
+  using T = BwdTile<D, kDkdvTile>;
+  constexpr int NW = kDkdvWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
+  constexpr int kSub = kDkdvTile / kBwdRows;  // 32-row sub-blocks per query tile
+  static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  lds_char* const qst = (lds_char*)smem_raw;     // 2 q stages
-  lds_char* const dst = qst + 2 * T::kBytes;      // 2 dO stages
-  lds_char* const wst = dst + 2 * T::kBytes;      // 2 workspace stages
+  lds_char* const qst = (lds_char*)smem_raw;       // 2 q stages
+  lds_char* const dst = qst + 2 * T::kBytes;       // 2 dO stages
+  lds_char* const wst = dst + 2 * T::kBytes;       // 2 workspace stages
+  lds_char* const pst = wst + 2 * kWsTileBytes;    // 2 p slots per pair
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pw = wave < 4;
+  const int pair = wave & 3;
   const int nk = gridDim.x;
   int bkv, t;
   map_workgroup(blockIdx.x + nk * blockIdx.y, nk, BHkv, 1, CAUSAL, bkv, t);
@@ -276,22 +319,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const int bh0 = bkv * group;  // first query head of this key/value head's group
 
   const int k0 = kblk * kBwdBlock;
-  const int kw0 = k0 + wave * kBwdRows;
+  const int kw0 = k0 + pair * kBwdRows;
   const int my_k = kw0 + l32;
 
-  // This lane's key: k and v fragments (B operands of S = Q K^T and dP = dO V^T)
-  bf16x8 kf[kDB], vf[kDB];
+  // This lane's key: k fragments (p wave, B operand of S = Q K^T) or v fragments (dS wave, of dP = dO V^T)
+  bf16x8 kvf[kDB];
+  const __bf16* kvsrc = pw ? k : v;
 #pragma unroll
-  for (int kb = 0; kb < kDB; ++kb) {
-    if (my_k < N) {
-      const size_t e = kv_off + (size_t)my_k * D + 16 * kb + 8 * h;
-      kf[kb] = *(const bf16x8*)(k + e);
-      vf[kb] = *(const bf16x8*)(v + e);
-    } else {
-      kf[kb] = (bf16x8){};
-      vf[kb] = (bf16x8){};
-    }
-  }
+  for (int kb = 0; kb < kDB; ++kb)
+    kvf[kb] = (my_k < N) ? *(const bf16x8*)(kvsrc + kv_off + (size_t)my_k * D + 16 * kb + 8 * h) : (bf16x8){};
 
   int dma[kCopies];
 #pragma unroll
@@ -300,17 +336,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int row = pos / T::CPR, phys = pos % T::CPR;
     dma[p] = row * T::RB + (phys ^ T::swz(row)) * 16;
   }
-  // query tiles: t0 .. nqt-1 of each of the group's query heads (causal: none entirely before this block's keys)
-  const int nqt = (N + kBwdTile - 1) / kBwdTile;
-  const int t0 = CAUSAL ? k0 / kBwdTile : 0;
+  // Query tiles t0 .. nqt-1 of each of the group's query heads. Key blocks and query tiles are both 128 rows,
+  // so under causal masking the first tile (t0 = this key block) is the only one that crosses the diagonal.
+  const int nqt = (N + kDkdvTile - 1) / kDkdvTile;
+  const int t0 = CAUSAL ? kblk : 0;
   const int per_head = nqt - t0;
   const int n_iter = (k0 < N) ? group * per_head : 0;
   const int npad = ws_rows(N);
   auto copy_iter = [&](int it, int S) __attribute__((always_inline)) {
     const int hq = bh0 + it / per_head;
-    const int row0 = (t0 + it % per_head) * kBwdTile;
+    const int row0 = (t0 + it % per_head) * kDkdvTile;
     const size_t base = (size_t)hq * N;
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kBwdTile)));
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kDkdvTile)));
     const int row_base = __builtin_amdgcn_readfirstlane(min(row0, N - 1));
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (base + row_base) * D, rows * T::RB);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + (base + row_base) * D, rows * T::RB);
@@ -319,19 +356,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
       lds_copy16_inline(rq, qst + S * T::kBytes + (wave + NW * p) * 1024, dma[p]);
       lds_copy16_inline(rd, dst + S * T::kBytes + (wave + NW * p) * 1024, dma[p]);
     }
-    if (wave == 0) {  // the tile's 64 pairs (512 bytes, always inside the padded workspace); lanes 32..63 fall
-                      // outside the descriptor and write zeros to the unused upper half of the LDS slot
-      const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + 2 * ((size_t)hq * npad + row0), kBwdTile * 8);
+    if (wave == 0) {  // the tile's 128 pairs (1 KiB, always inside the padded workspace)
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + 2 * ((size_t)hq * npad + row0), kWsTileBytes);
       lds_copy16_inline(rw, wst + S * kWsTileBytes, lane * 16);
     }
   };
 
-  // Row reads of q and dO (A operands): row 32sb + swap_bits23(l32), columns 16kb + 8h .. +7
+  // Row reads (A operands of S = Q K^T and dP = dO V^T): row 32sb + swap_bits23(l32), columns 16kb + 8h .. +7
   const int qrow = swap_bits23(l32);
   int row_off[kDB];
 #pragma unroll
   for (int kb = 0; kb < kDB; ++kb) row_off[kb] = T::at(qrow, 16 * kb + 8 * h);
-  // Transposing reads of dO and q (A operands of dV^T = dO^T P and dK^T = Q^T dS)
+  // Transposing reads (A operands of dV^T = dO^T P and dK^T = Q^T dS)
   int tr_off[kCB][2];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb)
@@ -341,37 +377,30 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
           T::at(8 * h + 4 * half + (lane & 15) / 4, 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   const float c2 = scale * kLog2e;
-  f32x16 dk_acc[kCB], dv_acc[kCB];
+  f32x16 acc[kCB];  // dV^T (p wave) or dK^T (dS wave) of this pair's keys
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    dk_acc[cb] = (f32x16){};
-    dv_acc[cb] = (f32x16){};
-  }
+  for (int cb = 0; cb < kCB; ++cb) acc[cb] = (f32x16){};
 
-  // One 64-row query tile (two 32-row sub-blocks) from stage S. In S and dP, lane = key my_k and value r of a
-  // sub-block is query row 16(r/8) + 8h + r%8 of that sub-block (q and dO rows fed in swap_bits23 order).
-  auto compute = [&](int it, int S) __attribute__((always_inline)) {
+  // Sub-block sb of the query tile in stage S. In S and dP, lane = key my_k and value r is query row
+  // 16(r/8) + 8h + r%8 of the sub-block (q and dO rows fed in swap_bits23 order); p travels from the p wave to
+  // the dS wave through the pair's LDS slot (sb % 2) in exactly that register layout.
+  auto sub_block = [&](int it, int S, int sb) __attribute__((always_inline)) {
     const lds_char* qs = qst + S * T::kBytes;
-    const lds_char* ds_ = dst + S * T::kBytes;
+    const lds_char* os = dst + S * T::kBytes;
     const lds_char* wsl = wst + S * kWsTileBytes;
-    const int tile_row0 = (t0 + it % per_head) * kBwdTile;
+    lds_char* ps = pst + ((sb & 1) * 4 + pair) * kPSlotBytes;
+    const int row0 = (t0 + it % per_head) * kDkdvTile;
+    const lds_char* rows_src = pw ? qs : os;  // q rows for S, dO rows for dP
+    f32x16 x = (f32x16){};
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int qlo = tile_row0 + 32 * sb;
-      if (qlo >= N || (CAUSAL && qlo + kBwdRows - 1 < kw0)) continue;  // no visible pair for this wave
-      f32x16 x = (f32x16){}, dp = (f32x16){};
-#pragma unroll
-      for (int kb = 0; kb < kDB; ++kb) {
-        const bf16x8 qa =
-            *(const __attribute__((address_space(3))) bf16x8*)(qs + 32 * sb * T::RB + row_off[kb]);
-        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kb], x, 0, 0, 0);
-      }
-#pragma unroll
-      for (int kb = 0; kb < kDB; ++kb) {
-        const bf16x8 da =
-            *(const __attribute__((address_space(3))) bf16x8*)(ds_ + 32 * sb * T::RB + row_off[kb]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kb], dp, 0, 0, 0);
-      }
+    for (int kb = 0; kb < kDB; ++kb) {
+      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(rows_src + 32 * sb * T::RB + row_off[kb]);
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kvf[kb], x, 0, 0, 0);
+    }
+    schedule_reads_ahead<kDB>();
+    const lds_char* tr_src = pw ? os : qs;    // dO^T for dV^T, q^T for dK^T
+    if (pw) {
+      const int qlo = row0 + 32 * sb;
       if ((qlo + kBwdRows > N) || (CAUSAL && qlo < kw0 + kBwdRows - 1)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -382,63 +411,78 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        // (D, lse2) of query rows 32sb + 16m + 8h .. +7 of the tile: 64 bytes, read by every lane of the half
+        // lse2 of query rows 32sb + 16m + 8h .. +7 of the tile (the odd floats of 64 bytes of pairs)
         const __attribute__((address_space(3))) f32x4* wp =
             (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 16 * m + 8 * h) * 8);
-        f32x4 w4[4];
+        f32x8 pv;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w4[u] = wp[u];
-        const f32x8 xs = m ? x.hi : x.lo;
-        const f32x8 ys = m ? dp.hi : dp.lo;
-        f32x8 pv, dsv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float Dq = w4[e >> 1][2 * (e & 1)];
-          const float l2 = w4[e >> 1][2 * (e & 1) + 1];
-          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[e], c2, -l2));
-          dsv[e] = pv[e] * (ys[e] - Dq);
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 w = wp[u];
+          pv[2 * u] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * m + 2 * u], c2, -w[1]));
+          pv[2 * u + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * m + 2 * u + 1], c2, -w[3]));
         }
         const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+        *(__attribute__((address_space(3))) bf16x8*)(ps + (m * 64 + lane) * 16) = pb;
+        const int rbase = (32 * sb + 16 * m) * T::RB;
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) {
+          const bf16x8 at_ = read_tr8(tr_src + rbase + tr_off[cb][0], tr_src + rbase + tr_off[cb][1]);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at_, pb, acc[cb], 0, 0, 0);
+        }
+      }
+      lds_barrier();  // p of this sub-block is in the slot
+    } else {
+      lds_barrier();  // wait for p of this sub-block
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 pb = *(const __attribute__((address_space(3))) bf16x8*)(ps + (m * 64 + lane) * 16);
+        const __attribute__((address_space(3))) f32x4* wp =
+            (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 16 * m + 8 * h) * 8);
+        f32x8 dsv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 w = wp[u];
+          dsv[2 * u] = (float)pb[2 * u] * (x[8 * m + 2 * u] - w[0]);
+          dsv[2 * u + 1] = (float)pb[2 * u + 1] * (x[8 * m + 2 * u + 1] - w[2]);
+        }
         const bf16x8 dsb = __builtin_convertvector(dsv, bf16x8);
         const int rbase = (32 * sb + 16 * m) * T::RB;
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) {
-          const bf16x8 dot_ = read_tr8(ds_ + rbase + tr_off[cb][0], ds_ + rbase + tr_off[cb][1]);
-          dv_acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot_, pb, dv_acc[cb], 0, 0, 0);
-          const bf16x8 qt = read_tr8(qs + rbase + tr_off[cb][0], qs + rbase + tr_off[cb][1]);
-          dk_acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsb, dk_acc[cb], 0, 0, 0);
+          const bf16x8 at_ = read_tr8(tr_src + rbase + tr_off[cb][0], tr_src + rbase + tr_off[cb][1]);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at_, dsb, acc[cb], 0, 0, 0);
         }
       }
     }
   };
 
-  auto step = [&](int it, int S) __attribute__((always_inline)) {
-    if (it + 1 < n_iter) copy_iter(it + 1, S ^ 1);
-    compute(it, S);
-    wait_copies_and_barrier<0>();
-  };
+  // Stage ring: the copy of tile it+1 goes into the other stage after the first sub-block of tile it; every wave
+  // finished reading that stage (tile it-1) before the barrier that ended tile it-1, and the barrier that ends
+  // tile it also waits for the copies.
   if (n_iter > 0) {
     copy_iter(0, 0);
     wait_copies_and_barrier<0>();
   }
-  for (int it = 0; it < n_iter; it += 2) {
-    step(it, 0);
-    if (it + 1 < n_iter) step(it + 1, 1);
+  for (int it = 0; it < n_iter; ++it) {
+    const int S = it & 1;
+#pragma unroll
+    for (int sb = 0; sb < kSub; ++sb) {
+      sub_block(it, S, sb);
+      if (sb == 0 && it + 1 < n_iter) copy_iter(it + 1, S ^ 1);
+    }
+    wait_copies_and_barrier<0>();
   }
 
-  // dk_j = scale * dk_acc, dv_j = dv_acc; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k
+  // dk_j = scale * dK^T, dv_j = dV^T; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k
   if (my_k < N) {
-    __bf16* rk = dk + kv_off + (size_t)my_k * D;
-    __bf16* rv = dv + kv_off + (size_t)my_k * D;
+    __bf16* row = (pw ? dv : dk) + kv_off + (size_t)my_k * D;
+    const float f = pw ? 1.f : scale;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 a = {dk_acc[cb][4 * g] * scale, dk_acc[cb][4 * g + 1] * scale, dk_acc[cb][4 * g + 2] * scale,
-                         dk_acc[cb][4 * g + 3] * scale};
-        const f32x4 b = {dv_acc[cb][4 * g], dv_acc[cb][4 * g + 1], dv_acc[cb][4 * g + 2], dv_acc[cb][4 * g + 3]};
-        *(bf16x4*)(rk + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(a, bf16x4);
-        *(bf16x4*)(rv + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(b, bf16x4);
+        const f32x4 a = {acc[cb][4 * g] * f, acc[cb][4 * g + 1] * f, acc[cb][4 * g + 2] * f, acc[cb][4 * g + 3] * f};
+        *(bf16x4*)(row + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(a, bf16x4);
       }
   }
 }
@@ -450,10 +494,9 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv,
                              int N, float scale, hipStream_t stream) {
-  using T = BwdTile<D>;
   const int group = H / Hkv;
-  constexpr int lds_a = 4 * T::kBytes;
-  constexpr int lds_b = 4 * T::kBytes + 2 * kWsTileBytes;
+  constexpr int lds_a = 4 * BwdTile<D>::kBytes;
+  constexpr int lds_b = 2 * (2 * BwdTile<D, kDkdvTile>::kBytes + kWsTileBytes) + 8 * kPSlotBytes;
   auto ka = fa_bwd_dq_kernel<D, CAUSAL>;
   auto kb = fa_bwd_dkdv_kernel<D, CAUSAL>;
   hipError_t e = hipFuncSetAttribute((const void*)ka, hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
@@ -466,7 +509,7 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
                      N, B * H, scale, group);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv)), dim3(kBwdThreads), lds_b, stream, (const __bf16*)q,
+  hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv)), dim3(64 * kDkdvWaves), lds_b, stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const float*)ws, (__bf16*)dk,
                      (__bf16*)dv, N, B * Hkv, scale, group);
   return hipGetLastError();

@@ -146,9 +146,9 @@ def test_backward_error_codes():
 
 
 def test_backward_workspace_bytes():
-    # (D, lse*log2e) float pairs per query row, rows rounded up to 64 per head
+    # (D, lse*log2e) float pairs per query row, rows rounded up to 128 per head
     assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 128 * 8
-    assert fa.fa_bwd_workspace_bytes(1, 1, 64) == 64 * 8
+    assert fa.fa_bwd_workspace_bytes(1, 1, 64) == 128 * 8
     assert fa.fa_bwd_workspace_bytes(1, 32, 16384) == 32 * 16384 * 8
     assert fa.fa_bwd_workspace_bytes(0, 3, 100) == 0 and fa.fa_bwd_workspace_bytes(1, 1, -5) == 0
 
