@@ -18,6 +18,8 @@ Other modes (used to produce the rocprofv3 summaries under profiles/):
     --pmc-pass          run a copy kernel of known size, then the workload kernel, a few times each
     --summarize DIR     print a summary of the rocprofv3 output found under DIR
     --write-profiles    turn the outputs of PROFILE_COMMANDS (under gpurun_out/) into profiles/ summaries
+    --bwd-pmc-pass      like --pmc-pass for the gradient call (copy kernel, then fa_bwd a few times)
+    --write-profiles-bwd  the same for BWD_PROFILE_COMMANDS: profiles/bwd_<workload>_rocprof.md
 """
 from __future__ import annotations
 
@@ -60,6 +62,20 @@ PROFILE_COMMANDS = {
     "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA "
           "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
           "-d gpurun_out/prof_{w}_sq -o run -- python bench.py --workload {w} --pmc-pass",
+}
+
+
+# The same four runs for the gradient call (two kernels per call).
+BWD_PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bwd_{w}_trace -o run -- "
+             "python bench.py --workload {w} --bwd-only --steps 20 --warmup 3",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_bwd_{w}_fetch -o run -- "
+             "python bench.py --workload {w} --bwd-pmc-pass",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_bwd_{w}_write -o run -- "
+             "python bench.py --workload {w} --bwd-pmc-pass",
+    "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA "
+          "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+          "-d gpurun_out/prof_bwd_{w}_sq -o run -- python bench.py --workload {w} --bwd-pmc-pass",
 }
 
 
@@ -233,8 +249,8 @@ def cpu_baseline(w, n_rows: int):
             "seconds": dt}
 
 
-def pmc_pass(w, reps: int):
-    """Kernels for the rocprofv3 counter runs: a plain copy of known size, then the workload kernel."""
+def _copy_kernel_pass(reps: int) -> int:
+    """A plain copy of known size (the calibration kernel of the FETCH_SIZE / WRITE_SIZE counters)."""
     import torch
 
     n = 1 << 28  # 512 MiB of bf16 read + 512 MiB written by torch.neg
@@ -244,6 +260,22 @@ def pmc_pass(w, reps: int):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
+    return n
+
+
+def bwd_pmc_pass(w, reps: int):
+    """Kernels for the rocprofv3 counter runs of the gradient call: the copy, then fa_bwd."""
+    n = _copy_kernel_pass(reps)
+    time_backward(w, steps=reps, warmup=0)
+    print(json.dumps({"bwd_pmc_pass": w.name, "copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "reps": reps,
+                      "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}), flush=True)
+
+
+def pmc_pass(w, reps: int):
+    """Kernels for the rocprofv3 counter runs: a plain copy of known size, then the workload kernel."""
+    import torch
+
+    n = _copy_kernel_pass(reps)
     q, k, v, o, lse, lens = _device_inputs(w)
     call = _caller(w, q, k, v, o, lse, lens, torch.cuda.current_stream().cuda_stream)
     for _ in range(reps):
@@ -391,6 +423,72 @@ LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active,
     print(md)
 
 
+def write_profiles_bwd(w):
+    """Summary of the BWD_PROFILE_COMMANDS outputs: profiles/bwd_<workload>_rocprof.md (both gradient kernels)."""
+    dirs = {k: f"gpurun_out/prof_bwd_{w.name}_{k}" for k in BWD_PROFILE_COMMANDS}
+    stats = _stats(dirs["trace"])
+    fetch, write, sq = _counters(dirs["fetch"]), _counters(dirs["write"]), _counters(dirs["sq"])
+    copy = "neg_kernel"
+    known_kib = 2 * (1 << 28) / 1024
+    f_fetch = known_kib / _pick(fetch, "FETCH_SIZE", copy)
+    f_write = known_kib / _pick(write, "WRITE_SIZE", copy)
+    n_simd = 256 * 4
+    rows, total_us = [], 0.0
+    for kname in ("fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"):
+        t = [r for r in stats if kname in r["Name"]]
+        if not t:
+            raise RuntimeError(f"no kernel statistics for {kname}")
+        avg_us = float(t[0]["AverageNs"]) / 1e3
+        total_us += avg_us
+        busy = _pick(sq, "SQ_VALU_MFMA_BUSY_CYCLES", kname)
+        gui = _pick(sq, "GRBM_GUI_ACTIVE", kname)
+        rows.append({"kernel": kname, "calls": t[0]["Calls"], "avg_us": avg_us,
+                     "read": _pick(fetch, "FETCH_SIZE", kname) * f_fetch * 1024,
+                     "write": _pick(write, "WRITE_SIZE", kname) * f_write * 1024,
+                     "mfma_insts": _pick(sq, "SQ_INSTS_MFMA", kname), "mfma_busy": busy,
+                     "util_spec": busy / n_simd / (avg_us * 1e-6 * 2.4e9),
+                     "util_clock": busy / n_simd / (gui / 8),
+                     "valu": _pick(sq, "SQ_INSTS_VALU", kname),
+                     "lds_conflict": _pick(sq, "SQ_LDS_BANK_CONFLICT", kname),
+                     "lds_active": _pick(sq, "SQ_LDS_IDX_ACTIVE", kname)})
+    flops = 2.5 * w.flops
+    cmds = "\n".join(f"    {BWD_PROFILE_COMMANDS[k].format(w=w.name)}" for k in BWD_PROFILE_COMMANDS)
+    kb = w.B * w.Hk * w.N * w.d * 2
+    qb = w.B * w.H * w.N * w.d * 2
+    alg_read = 3 * qb + 2 * kb + 4 * w.B * w.H * w.N  # q, o, dout, k, v, lse
+    alg_write = qb + 2 * kb                          # dq, dk, dv (the workspace pairs are extra)
+    table = "\n".join(
+        f"| {r['kernel']} | {r['calls']} | {r['avg_us']:.1f} | {r['read']:.4g} | {r['write']:.4g} | "
+        f"{r['mfma_insts']:.4g} | {100 * r['util_spec']:.1f} % | {100 * r['util_clock']:.1f} % | {r['valu']:.4g} | "
+        f"{r['lds_conflict']:.4g} |" for r in rows)
+    md = f"""# rocprofv3 summary: gradient call (fa_bwd) on {w.name}
+
+Kernel sources sha256[:16]: `{kernel_src_hash(BWD_SRCS)}` (exact_attention_13_amd/csrc/fa_bwd_kernel.hip and fa_gfx950.h).
+Workload: B={w.B} H={w.H} H_kv={w.Hk} N={w.N} d={w.d} causal={w.causal} bf16; {flops:.4g} FLOP per call in the usual
+convention (2.5 x the forward's 4*B*H*N^2*d{', halved' if w.causal else ''}: five matrix products); the kernels
+execute seven (S and dP are formed in both), {7 / 5 * flops:.4g} FLOP of MFMA work.
+
+Commands (run from the repository root; outputs under gpurun_out/, summarised by
+`python bench.py --workload {w.name} --write-profiles-bwd`):
+
+{cmds}
+
+| kernel | calls | avg us | HBM read B | HBM write B | MFMA insts | MFMA busy (2.4 GHz) | MFMA busy (measured clock) | VALU insts | LDS bank conflicts |
+|---|---|---|---|---|---|---|---|---|---|
+{table}
+
+Gradient call at the traced averages: {total_us:.1f} us, {flops / (total_us * 1e-6) / 1e12:.1f} TFLOP/s
+({100 * flops / (total_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
+Algorithmic HBM bytes per call: read {alg_read} (q, o, dout, lse, k, v), write {alg_write} (dq, dk, dv).
+FETCH_SIZE x {f_fetch:.4f} and WRITE_SIZE x {f_write:.4f} (calibrated on a copy of 2^28 bf16).
+MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over the traced average at 2.4 GHz, and over GRBM_GUI_ACTIVE / 8
+(the clock actually measured during the kernel).
+"""
+    PROFILES.mkdir(exist_ok=True)
+    (PROFILES / f"bwd_{w.name}_rocprof.md").write_text(md)
+    print(md)
+
+
 def main():
     import attn_inputs as ai
 
@@ -406,6 +504,8 @@ def main():
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--write-profiles", action="store_true")
     ap.add_argument("--bwd-only", action="store_true")
+    ap.add_argument("--bwd-pmc-pass", action="store_true")
+    ap.add_argument("--write-profiles-bwd", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     args = ap.parse_args()
 
@@ -414,6 +514,9 @@ def main():
         return 0
     if args.write_profiles:
         write_profiles(ai.WORKLOADS[args.workload])
+        return 0
+    if args.write_profiles_bwd:
+        write_profiles_bwd(ai.WORKLOADS[args.workload])
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -431,6 +534,9 @@ def main():
     w = ai.WORKLOADS[args.workload]
     if args.pmc_pass:
         pmc_pass(w, reps=5)
+        return 0
+    if args.bwd_pmc_pass:
+        bwd_pmc_pass(w, reps=3)
         return 0
     if args.bwd_only:
         print(json.dumps(backward_record(w, args.steps, args.warmup)), flush=True)

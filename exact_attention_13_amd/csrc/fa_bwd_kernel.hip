@@ -26,7 +26,7 @@
 // S and dP are computed in both kernels (7 matrix products instead of the 5 of a single pass with atomic dq
 // updates): the price of determinism.
 //
-// LDS tiles (64 rows) are read both row-wise (16 bytes per lane, A operands) and transposed (8 bytes per lane, 4
+// LDS tiles are read both row-wise (16 bytes per lane, A operands) and transposed (8 bytes per lane, 4
 // rows x 64 bytes per 32 lanes). One XOR swizzle of the 16-byte chunks serves both without bank conflicts:
 // chunk c of row r is stored at c ^ (4 (t % (CPR/4)) + (t / (CPR/4)) % 4), t = r / RPG (CPR = d/8 chunks per row,
 // RPG = 16/CPR rows per 256 bytes).
@@ -43,7 +43,7 @@ constexpr int kBwdTile = 64;                   // keys per LDS tile (dq)
 constexpr int kWsTileBytes = 1024;             // LDS slot for one tile of workspace pairs (one copy: 64 x 16 B)
 
 // Workspace rows per head: N rounded up to the dq workgroup's 128 rows (its grid writes exactly these rows),
-// which is also a whole number of the dk/dv kernel's 64-row query tiles.
+// which is also a whole number of the dk/dv kernel's 128-row query tiles.
 __host__ __device__ constexpr int ws_rows(int N) { return (N + kBwdBlock - 1) / kBwdBlock * kBwdBlock; }
 
 template <int D, int ROWS = kBwdTile>
