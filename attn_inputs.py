@@ -33,7 +33,7 @@ class Workload:
     N: int
     d: int
     causal: bool
-    dtype: str          # "bf16" or "f32"
+    dtype: str          # "bf16", "f32" or "fp8" (float8_e4m3fn q, k, v with per-tensor scales)
     seed: int
     k_scale: float = 1.0
     sampled_rows: int = 0   # 0: every row is checked; else rows sampled per check
@@ -62,7 +62,7 @@ class Workload:
 
     @property
     def elt_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return {"bf16": 2, "f32": 4, "fp8": 1}[self.dtype]
 
     @property
     def kv_rows(self) -> int:
@@ -71,9 +71,11 @@ class Workload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """Q read once, valid K and V rows read once, O written once (input dtype); lse written once (fp32)."""
+        """Q read once, valid K and V rows read once, O written once (input dtype; bf16 for fp8 inputs); lse
+        written once (fp32)."""
         n = self.B * self.H * self.N
-        return (2 * n + 2 * self.kv_rows) * self.d * self.elt_bytes + 4 * n
+        out = 2 if self.dtype == "fp8" else self.elt_bytes
+        return (n + 2 * self.kv_rows) * self.d * self.elt_bytes + n * self.d * out + 4 * n
 
 
 # The workloads: seed = workload number; C2 has a causal and a non-causal variant.
@@ -117,6 +119,22 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16", k_s
         k = k * float(k_scale)
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
     return q.to(tdt).contiguous(), k.to(tdt).contiguous(), v.to(tdt).contiguous()
+
+
+FP8_MAX = 448.0  # largest finite float8_e4m3fn value
+
+
+def make_qkv_fp8(B: int, H: int, N: int, d: int, seed: int, k_scale: float = 1.0):
+    """The same fp32 draws as make_qkv, quantized per tensor to float8_e4m3fn (round-to-nearest-even):
+    s_x = max|x| / 448 rounded to fp32, x8 = x / s_x. Returns (q8, k8, v8, s_q, s_k, s_v); the real inputs the
+    fp8 path is given are x8 * s_x."""
+    q, k, v = make_qkv(B, H, N, d, seed, "f32", k_scale)
+    out, scales = [], []
+    for x in (q, k, v):
+        s = float(np.float32(float(x.abs().max()) / FP8_MAX))
+        out.append((x / s).to(torch.float8_e4m3fn).contiguous())
+        scales.append(s)
+    return (*out, *scales)
 
 
 def make_workload(w: Workload):

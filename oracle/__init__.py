@@ -68,13 +68,13 @@ def default_threads() -> int:
 
 
 def _as_f32(x) -> np.ndarray:
-    """Widen a CPU torch tensor (bf16 or fp32) or array to a contiguous fp32 ndarray, exactly."""
+    """Widen a CPU torch tensor (fp8 e4m3fn, bf16 or fp32) or array to a contiguous fp32 ndarray, exactly."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
             x = x.detach().to("cpu")
-            if x.dtype not in (torch.bfloat16, torch.float32):
-                raise TypeError(f"oracle takes bf16 or fp32 inputs, got {x.dtype}")
+            if x.dtype not in (torch.float8_e4m3fn, torch.bfloat16, torch.float32):
+                raise TypeError(f"oracle takes fp8 e4m3fn, bf16 or fp32 inputs, got {x.dtype}")
             return np.ascontiguousarray(x.to(torch.float32).numpy())
     except ImportError:  # pragma: no cover
         pass
@@ -106,7 +106,13 @@ def attention_rows(q, k, v, causal: bool, scale: float, rows=None, threads: int 
         len_arr = np.ascontiguousarray(np.asarray(kv_len, dtype=np.int64).reshape(-1))
         if len_arr.size != B or (len_arr < 0).any() or (len_arr > Nk).any():
             raise ValueError(f"kv_len must hold {B} counts in [0, {Nk}], got {len_arr}")
-    sc = float(np.float32(scale))
+    return _rows_exact_scale(qa, ka, va, causal, float(np.float32(scale)), rows, threads, len_arr)
+
+
+def _rows_exact_scale(qa, ka, va, causal, sc: float, rows, threads, len_arr):
+    """attention_rows on fp32 arrays with the score scale sc used as the given fp64 value."""
+    B, H, N, d = qa.shape
+    Hkv, Nk = ka.shape[1], ka.shape[2]
     if rows is None:
         n = B * H * N
         rows_arr = None
@@ -179,3 +185,21 @@ def attention_bwd(q, k, v, dout, causal: bool, scale: float, threads: int | None
     Hkv = tuple(k.shape)[1]
     dq, dk, dv = attention_bwd_rows(q, k, v, dout, causal, scale, None, None, threads)
     return dq.reshape(B, H, N, d), dk.reshape(B, Hkv, N, d), dv.reshape(B, Hkv, N, d)
+
+
+def attention_fp8_rows(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, causal: bool, scale: float,
+                       rows=None, threads: int | None = None):
+    """Attention of per-tensor-scaled fp8 inputs: the real inputs are q8 * q_scale, k8 * k_scale, v8 * v_scale.
+
+    q8, k8, v8: [B, H, N, d] torch float8_e4m3fn CPU tensors (v not transposed). Every fp8 value is exact in
+    fp32; the score scale scale * q_scale * k_scale (the fp32 values handed to the GPU, multiplied in fp64) is
+    applied to the raw fp8 dot products, and o is multiplied by v_scale (attention is linear in v).
+    Returns (o [n_rows, d] float64, lse [n_rows] float64).
+    """
+    qa, ka, va = _as_f32(q8), _as_f32(k8), _as_f32(v8)
+    if qa.ndim != 4 or qa.shape != ka.shape or ka.shape != va.shape:
+        raise ValueError(f"q, k, v must all be [B,H,N,d]: {qa.shape} {ka.shape} {va.shape}")
+    f32 = lambda x: float(np.float32(x))
+    sc = f32(scale) * f32(q_scale) * f32(k_scale)
+    o, lse = _rows_exact_scale(qa, ka, va, causal, sc, rows, threads, None)
+    return o * f32(v_scale), lse
