@@ -10,7 +10,8 @@ sample of the same workload on this host's cores.
 
 The line also carries `backward`: the gradient call fa_bwd (dq, then dk and dv) on the headline workload and on
 the long causal one, timed the same way, in the usual FLOP convention 2.5 x the forward's (five matrix products:
-the recomputed QK^T, dO V^T, dV, dQ, dK).
+the recomputed QK^T, dO V^T, dV, dQ, dK); and `fp8`: fa_fwd_fp8 on the same two shapes with the inputs quantized
+per tensor to float8_e4m3fn, against the fp8 peak.
 
     --bwd-only          time only the gradient call of --workload (one JSON line; for profiling)
 
@@ -39,6 +40,7 @@ sys.path.insert(0, str(ROOT))
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk (AMD's published 2.5 PF)
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (AMD's published 5.0 PF; twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "c3_bf16_b2h16n4096d128"
 KERNEL_SRC = ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_kernel.hip"
@@ -46,6 +48,9 @@ KERNEL_SRCS = (KERNEL_SRC, ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950
 BWD_SRCS = (ROOT / "exact_attention_13_amd" / "csrc" / "fa_bwd_kernel.hip",
             ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
 BWD_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal")
+FP8_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal")  # the same shapes, fp8 inputs
+FP8_SRCS = (ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_fp8_kernel.hip",
+            ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
 PROFILES = ROOT / "profiles"
 
 
@@ -207,6 +212,50 @@ def backward_record(w, steps: int, warmup: int):
                          "frac": round(flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "flops_per_call": flops, "kernels": ["fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"],
             "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}
+
+
+def fp8_record(w, steps: int, warmup: int):
+    """fa_fwd_fp8 on workload w's shape with the seeded inputs quantized per tensor to float8_e4m3fn."""
+    import torch
+
+    import attn_inputs as ai
+    import exact_attention_13_amd as fa
+
+    q8, k8, v8, sq, sk, sv = ai.make_qkv_fp8(w.B, w.H, w.N, w.d, w.seed, w.k_scale)
+    q, k, vt = q8.cuda(), k8.cuda(), v8.transpose(2, 3).contiguous().cuda()
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    args = (q.data_ptr(), k.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(), sq, sk, sv, w.B, w.H, w.N, w.d,
+            int(w.causal), w.scale, stream.cuda_stream)
+
+    def call():
+        rc = fa.fa_fwd_fp8(*args)
+        if rc != 0:
+            raise RuntimeError(f"fa_fwd_fp8 failed: {fa.fa_strerror(rc)}")
+    for _ in range(warmup):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    mean = statistics.fmean(durs)
+    return {"workload": w.name.replace("_bf16_", "_fp8_"), "dtype": "fp8 e4m3 (bf16 o)",
+            "tflops": round(w.flops * steps / wall / 1e12, 2),
+            "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
+                          "min": round(min(durs), 4)},
+            "roofline": {"bound": "mfma", "achieved": round(w.flops / (mean * 1e-3) / 1e12, 2),
+                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(w.flops / (mean * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)},
+            "flops_per_launch": w.flops, "kernel": "fa_fwd_fp8_kernel",
+            "kernel_src_sha256_16": kernel_src_hash(FP8_SRCS)}
 
 
 def traffic_from_profiles(w):
@@ -507,6 +556,7 @@ def main():
     ap.add_argument("--bwd-pmc-pass", action="store_true")
     ap.add_argument("--write-profiles-bwd", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--fp8-only", action="store_true", help="time only fa_fwd_fp8 on --workload's shape")
     args = ap.parse_args()
 
     if args.summarize:
@@ -534,6 +584,9 @@ def main():
     w = ai.WORKLOADS[args.workload]
     if args.pmc_pass:
         pmc_pass(w, reps=5)
+        return 0
+    if args.fp8_only:
+        print(json.dumps(fp8_record(w, args.steps, args.warmup)), flush=True)
         return 0
     if args.bwd_pmc_pass:
         bwd_pmc_pass(w, reps=3)
@@ -578,6 +631,7 @@ def main():
         line["other_workloads"] = others
     if not args.no_backward:
         line["backward"] = [backward_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in BWD_WORKLOADS]
+        line["fp8"] = [fp8_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in FP8_WORKLOADS]
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_rows)
         cb.pop("seconds")

@@ -111,3 +111,31 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_bwd failed ({rc}): {binding.fa_strerror(rc)}")
     return dq, dk, dv
+
+
+def forward_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, q_scale: float, k_scale: float, v_scale: float,
+                causal: bool = False, scale: float | None = None, stream: int | None = None):
+    """Attention of fp8 inputs: q, k [B, H, N, d] and vt = v transposed [B, H, d, N], all float8_e4m3fn, with
+    per-tensor scales (real inputs q*q_scale, ...). Returns o (bf16 [B, H, N, d]) and lse (fp32 [B, H, N])."""
+    for name, t in (("q", q), ("k", k), ("vt", vt)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor")
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"{name} must be float8_e4m3fn, got {t.dtype}")
+    B, H, N, d = q.shape
+    if k.shape != q.shape or vt.shape != (B, H, d, N) or not (q.device == k.device == vt.device):
+        raise ValueError(f"q, k [B,H,N,d] and vt [B,H,d,N] disagree: {tuple(q.shape)} {tuple(k.shape)} "
+                         f"{tuple(vt.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        rc = binding.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                float(q_scale), float(k_scale), float(v_scale), B, H, N, d, int(bool(causal)),
+                                float(scale), int(stream))
+    if rc != binding.FA_OK:
+        raise RuntimeError(f"fa_fwd_fp8 failed ({rc}): {binding.fa_strerror(rc)}")
+    return o, lse

@@ -25,8 +25,8 @@ FA_ERR_ARG = 5
 FA_ERR_ALIAS = 6
 FA_ERR_HIP = 7
 
-EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_strerror",
-           "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_f32",
+           "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_attention_13_amd/build.py` "
@@ -41,6 +41,8 @@ _lib.fa_fwd_gqa.restype = _I
 _lib.fa_fwd_gqa.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _lib.fa_fwd_kpad.restype = _I
 _lib.fa_fwd_kpad.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_lib.fa_fwd_fp8.restype = _I
+_lib.fa_fwd_fp8.argtypes = [_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _P]
 _lib.fa_bwd.restype = _I
 _lib.fa_bwd.argtypes = [_P] * 10 + [_I] * 6 + [ctypes.c_float, _P]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -73,6 +75,12 @@ def fa_fwd_kpad(q: int, k: int, v: int, o: int, lse: int, kv_len: int, B: int, H
                 causal: int, scale: float, stream: int) -> int:
     """Raw entry point: fa_fwd_gqa plus kv_len, a device int32 [B] array of valid-key counts (key padding)."""
     return _lib.fa_fwd_kpad(q, k, v, o, lse, kv_len, B, H, H_kv, N, d, causal, scale, stream)
+
+
+def fa_fwd_fp8(q: int, k: int, vt: int, o: int, lse: int, q_scale: float, k_scale: float, v_scale: float, B: int,
+               H: int, N: int, d: int, causal: int, scale: float, stream: int) -> int:
+    """Raw entry point: float8_e4m3fn q, k [B,H,N,d] and vt [B,H,d,N] with per-tensor scales; bf16 o."""
+    return _lib.fa_fwd_fp8(q, k, vt, o, lse, q_scale, k_scale, v_scale, B, H, N, d, causal, scale, stream)
 
 
 def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, workspace: int, B: int,

@@ -16,7 +16,8 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libfa.so"
-SOURCES = [CSRC / "fa_fwd_kernel.hip", CSRC / "fa_bwd_kernel.hip", CSRC / "fa_api.hip"]
+SOURCES = [CSRC / "fa_fwd_kernel.hip", CSRC / "fa_fwd_fp8_kernel.hip", CSRC / "fa_bwd_kernel.hip",
+           CSRC / "fa_api.hip"]
 ARCH = "gfx950"
 
 

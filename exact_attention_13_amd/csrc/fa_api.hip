@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 10200;  // 1.2.0
+constexpr int kVersion = 10300;  // 1.3.0
 constexpr long long kMaxHeads = 65535;   // B*H is the grid's y extent
 constexpr long long kMaxN = 1LL << 30;
 
@@ -139,6 +139,31 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   return fa::bwd_workspace_bytes(B, H, N);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, float q_scale, float k_scale,
+               float v_scale, int B, int H, int N, int d, int causal, float scale, hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+  for (float s : {q_scale, k_scale, v_scale})
+    if (!(s > 0.f) || !isfinite(s)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  // v^T rows of N bytes start on 16-byte boundaries; byte offsets inside one head's v^T stay below 2^31
+  if ((long long)B * H > kMaxHeads || N % 16 != 0 || N > (1 << 24)) return FA_ERR_SHAPE;
+  if (!q || !k || !vt || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)vt | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t ob = 2 * elems, lb = (size_t)B * H * N * 4;
+  if (overlaps(o, ob, q, elems) || overlaps(o, ob, k, elems) || overlaps(o, ob, vt, elems)) return FA_ERR_ALIAS;
+  if (overlaps(lse, lb, q, elems) || overlaps(lse, lb, k, elems) || overlaps(lse, lb, vt, elems) ||
+      overlaps(lse, lb, o, ob))
+    return FA_ERR_ALIAS;
+  const hipError_t e = fa::launch_fwd_fp8(q, k, vt, o, lse, B * H, N, d, causal != 0, scale, q_scale, k_scale,
+                                          v_scale, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
                int causal, float scale, hipStream_t stream) {
   bool empty = false;
@@ -152,11 +177,13 @@ const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a tensor, lse, kv_len or workspace pointer is NULL";
-    case FA_ERR_SHAPE: return "bad shape: B, H, N must be >= 0, B*H <= 65535, N <= 2^30, H_kv >= 1 dividing H";
+    case FA_ERR_SHAPE:
+      return "bad shape: B, H, N must be >= 0, B*H <= 65535, N <= 2^30, H_kv >= 1 dividing H "
+             "(fp8: N a multiple of 16, at most 2^24)";
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
     case FA_ERR_ALIGN:
       return "misaligned pointer: tensors and the workspace need 16-byte alignment, lse and kv_len 4-byte";
-    case FA_ERR_ARG: return "bad argument: scale must be finite and > 0, causal must be 0 or 1";
+    case FA_ERR_ARG: return "bad argument: scales must be finite and > 0, causal must be 0 or 1";
     case FA_ERR_ALIAS: return "an output (o, lse, dq, dk, dv, workspace) overlaps an input or another output";
     case FA_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";
     default: return "unknown error code";

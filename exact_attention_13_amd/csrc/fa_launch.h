@@ -9,6 +9,9 @@ namespace fa {
 // is NULL or B device int32 counts of valid keys (clamped to [0, N] by the kernel).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                            int N, int d, bool causal, float scale, const int* kv_len, hipStream_t stream);
+// fp8 (float8_e4m3fn) q, k [B*H, N, d] and v^T [B*H, d, N] with per-tensor scales; bf16 o. N % 16 == 0.
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int BH, int N, int d,
+                          bool causal, float scale, float q_scale, float k_scale, float v_scale, hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, hipStream_t stream);
 // Enqueue the two gradient kernels (dq and the workspace pairs, then dk and dv). Arguments must already be valid

@@ -140,6 +140,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*
+ * fa_fwd_fp8 -- the attention forward of fp8 inputs with per-tensor scales
+ * (FP8 is listed among the FlashAttention-3 techniques on the unite.ai page,
+ * section "FlashAttention-3", items 2-3; the scaling scheme is a reading).
+ *   q, k    : const float8_e4m3fn [B,H,N,d] (device), one byte per element
+ *   vt      : const float8_e4m3fn [B,H,d,N] (device): v transposed, element
+ *             (b,h,c,j) at ((b*H + h)*d + c)*N + j
+ *   q_scale, k_scale, v_scale : the real inputs are q*q_scale, k*k_scale,
+ *             v*v_scale (finite, > 0)
+ *   o       : bf16 [B,H,N,d] (device, written); lse : float [B,H,N] as fa_fwd
+ *   N       : a multiple of 16, at most 2^24 (FA_ERR_SHAPE otherwise)
+ * The scores and the weighted sum run on fp8 matrix instructions with fp32
+ * accumulation; the softmax weights are rounded to e4m3 before the product
+ * with v, and l sums the rounded weights (o is their weighted average). The
+ * other arguments, errors and ownership as fa_fwd; no grouped heads, no key
+ * padding. NaN inputs give undefined results.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, float q_scale, float k_scale,
+               float v_scale, int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
  * fa_fwd_f32 -- the same operation with fp32 q, k, v and o. Products and sums
  * stay in fp32 throughout (fp32 matrix-core instructions, no bf16 step).
  * Arguments, layout, ownership and errors as fa_fwd.

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 10200
+    assert fa.fa_version() == 10300
     for code in range(8):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
@@ -143,6 +143,22 @@ def test_backward_error_codes():
     assert _bwd(ws=BWD["dq"] - 16) == fa.FA_ERR_ALIAS             # workspace runs into dq
     # empty problem: success, pointers ignored
     assert _bwd(N=0, **{name: 0 for name in BWD}) == fa.FA_OK
+
+
+def test_fp8_error_codes():
+    def f8(q=A, k=A + 0x1000000, vt=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, sq=0.01, sk=0.01, sv=0.01,
+           B=1, H=2, N=64, d=64, causal=0, scale=0.125):
+        return fa.fa_fwd_fp8(q, k, vt, o, lse, sq, sk, sv, B, H, N, d, causal, scale, 0)
+    assert f8(N=70) == fa.FA_ERR_SHAPE                 # v^T rows must be 16-byte multiples
+    assert f8(N=(1 << 24) + 16) == fa.FA_ERR_SHAPE
+    assert f8(d=96) == fa.FA_ERR_HEADDIM
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert f8(sq=bad) == fa.FA_ERR_ARG and f8(sk=bad) == fa.FA_ERR_ARG and f8(sv=bad) == fa.FA_ERR_ARG
+    assert f8(vt=0) == fa.FA_ERR_NULL
+    assert f8(vt=A + 0x2000000 + 4) == fa.FA_ERR_ALIGN
+    assert f8(o=A + 0x2000000 + 4096) == fa.FA_ERR_ALIAS    # o inside v^T (8 KiB of fp8)
+    assert f8(lse=A + 0x3000000 + 1024) == fa.FA_ERR_ALIAS  # lse inside o (16 KiB of bf16)
+    assert f8(N=0, q=0, k=0, vt=0, o=0, lse=0) == fa.FA_OK
 
 
 def test_backward_workspace_bytes():
