@@ -242,23 +242,39 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
-  // Two-stage ring: copy tile j+1 while tile j is computed; one barrier per tile.
-  auto step = [&](int j, int S) __attribute__((always_inline)) {
+  // Two-stage ring: copy tile j+1 while tile j is computed; one barrier per tile. The tiles this wave computes
+  // (j < wave_tiles) run in a loop of their own, two per iteration with the stage fixed at compile time and no
+  // condition around the computation (a conditional there made the compiler copy the accumulators at every
+  // join); the remaining tiles of the workgroup only copy and join the barriers.
+  auto issue = [&](int j, int S) __attribute__((always_inline)) {
     if (j + 1 < n_tiles) {
       copy_tile(kh, kst + (S ^ 1) * T::kBytes, j + 1);
       copy_tile(vh, vst + (S ^ 1) * T::kBytes, j + 1);
     }
-    if (j < wave_tiles) compute(j, S * T::kBytes);
-    wait_copies_and_barrier<0>();
   };
   if (n_tiles > 0) {
     copy_tile(kh, kst, 0);
     copy_tile(vh, vst, 0);
     wait_copies_and_barrier<0>();
   }
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(j, 0);
-    if (j + 1 < n_tiles) step(j + 1, 1);
+  int j = 0;
+  for (; j + 1 < wave_tiles; j += 2) {
+    issue(j, 0);
+    compute(j, 0);
+    wait_copies_and_barrier<0>();
+    issue(j + 1, 1);
+    compute(j + 1, T::kBytes);
+    wait_copies_and_barrier<0>();
+  }
+  if (j < wave_tiles) {
+    issue(j, 0);
+    compute(j, 0);
+    wait_copies_and_barrier<0>();
+    ++j;
+  }
+  for (; j < n_tiles; ++j) {
+    issue(j, j & 1);
+    wait_copies_and_barrier<0>();
   }
 
   // dq_i = scale * acc; acc[cb][4g + i] is column 32cb + 8g + 4h + i of row my_q
@@ -383,8 +399,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
 
   // Sub-block sb of the query tile in stage S. In S and dP, lane = key my_k and value r is query row
   // 16(r/8) + 8h + r%8 of the sub-block (q and dO rows fed in swap_bits23 order); p travels from the p wave to
-  // the dS wave through the pair's LDS slot (sb % 2) in exactly that register layout.
-  auto sub_block = [&](int it, int S, int sb) __attribute__((always_inline)) {
+  // the dS wave through the pair's LDS slot (sb % 2) in exactly that register layout. The role is a compile-time
+  // parameter: each role runs a loop of its own (with the same barriers), so the accumulators are not merged
+  // across role branches inside the loop.
+  auto sub_block = [&](int it, int S, int sb, auto role_c) __attribute__((always_inline)) {
+    constexpr bool pw = decltype(role_c)::value;
     const lds_char* qs = qst + S * T::kBytes;
     const lds_char* os = dst + S * T::kBytes;
     const lds_char* wsl = wst + S * kWsTileBytes;
@@ -399,7 +418,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     }
     schedule_reads_ahead<kDB>();
     const lds_char* tr_src = pw ? os : qs;    // dO^T for dV^T, q^T for dK^T
-    if (pw) {
+    if constexpr (pw) {
       const int qlo = row0 + 32 * sb;
       if ((qlo + kBwdRows > N) || (CAUSAL && qlo < kw0 + kBwdRows - 1)) {
 #pragma unroll
@@ -458,19 +477,27 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
 
   // Stage ring: the copy of tile it+1 goes into the other stage after the first sub-block of tile it; every wave
   // finished reading that stage (tile it-1) before the barrier that ended tile it-1, and the barrier that ends
-  // tile it also waits for the copies.
+  // tile it also waits for the copies. The last tile copies itself again (harmless, in bounds), so the copy is
+  // unconditional.
   if (n_iter > 0) {
     copy_iter(0, 0);
     wait_copies_and_barrier<0>();
   }
-  for (int it = 0; it < n_iter; ++it) {
-    const int S = it & 1;
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    for (int it = 0; it < n_iter; ++it) {
+      const int S = it & 1;
 #pragma unroll
-    for (int sb = 0; sb < kSub; ++sb) {
-      sub_block(it, S, sb);
-      if (sb == 0 && it + 1 < n_iter) copy_iter(it + 1, S ^ 1);
+      for (int sb = 0; sb < kSub; ++sb) {
+        sub_block(it, S, sb, role_c);
+        if (sb == 0) copy_iter(min(it + 1, n_iter - 1), S ^ 1);
+      }
+      wait_copies_and_barrier<0>();
     }
-    wait_copies_and_barrier<0>();
+  };
+  if (pw) {
+    run(std::true_type{});
+  } else {
+    run(std::false_type{});
   }
 
   // dk_j = scale * dK^T, dv_j = dV^T; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k
