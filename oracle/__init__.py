@@ -55,6 +55,7 @@ def _load():
         g = lib.oracle_attn_bwd_rows
         g.restype = ctypes.c_int
         g.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_long] * 5 + [ctypes.c_int, ctypes.c_double,
+                                                                     ctypes.c_void_p,
                                                                      ctypes.c_void_p, ctypes.c_long,
                                                                      ctypes.c_void_p, ctypes.c_long,
                                                                      ctypes.c_void_p, ctypes.c_void_p,
@@ -140,12 +141,13 @@ def attention(q, k, v, causal: bool, scale: float, threads: int | None = None, k
 
 
 def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, q_rows=None, kv_rows=None,
-                       threads: int | None = None):
+                       threads: int | None = None, kv_len=None):
     """Gradients of the attention forward for an upstream gradient dout of o (none for lse).
 
     q, dout: [B, H, N, d]; k, v: [B, Hkv, N, d] (Hkv divides H); bf16/fp32 CPU tensors or fp32 arrays.
     q_rows: flat query rows (b*H + h)*N + i for dq, or None for every row; kv_rows: flat key rows
     (b*Hkv + g)*N + j for dk and dv, or None for every row (an empty list skips that part).
+    kv_len: None, or B valid-key counts (the key-padding lengths of the forward, clamped to [0, N]).
     Returns (dq [n_q, d], dk [n_kv, d], dv [n_kv, d]) as float64 arrays.
     """
     qa, ka, va, da = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
@@ -161,6 +163,11 @@ def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, q_rows=None, k
         arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
         return arr, int(arr.size)
 
+    lens = None
+    if kv_len is not None:
+        lens = np.ascontiguousarray(np.asarray(kv_len, dtype=np.int32).reshape(-1))
+        if lens.size != B:
+            raise ValueError(f"kv_len needs {B} entries, got {lens.size}")
     qr, n_q = rows_arg(q_rows, B * H * N)
     kr, n_kv = rows_arg(kv_rows, B * Hkv * N)
     dq = np.zeros((n_q, d), dtype=np.float64)
@@ -170,6 +177,7 @@ def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, q_rows=None, k
         return dq, dk, dv
     rc = _load().oracle_attn_bwd_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, B, H, Hkv, N, d,
                                       int(bool(causal)), float(np.float32(scale)),
+                                      None if lens is None else lens.ctypes.data,
                                       None if qr is None else qr.ctypes.data, n_q,
                                       None if kr is None else kr.ctypes.data, n_kv,
                                       dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
@@ -179,11 +187,11 @@ def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, q_rows=None, k
     return dq, dk, dv
 
 
-def attention_bwd(q, k, v, dout, causal: bool, scale: float, threads: int | None = None):
+def attention_bwd(q, k, v, dout, causal: bool, scale: float, threads: int | None = None, kv_len=None):
     """Every gradient row: (dq [B,H,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) as float64 arrays."""
     B, H, N, d = tuple(q.shape)
     Hkv = tuple(k.shape)[1]
-    dq, dk, dv = attention_bwd_rows(q, k, v, dout, causal, scale, None, None, threads)
+    dq, dk, dv = attention_bwd_rows(q, k, v, dout, causal, scale, None, None, threads, kv_len)
     return dq.reshape(B, H, N, d), dk.reshape(B, Hkv, N, d), dv.reshape(B, Hkv, N, d)
 
 

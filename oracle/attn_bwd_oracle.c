@@ -22,7 +22,10 @@
  *   dv_j  = sum_i p_ij dO_i                    (likewise)
  *
  * with s_ij, J_i, lse_i and the key/value head g of query head h exactly as in
- * attn_oracle.c (no key padding here). Everything is fp64, sums sequential in
+ * attn_oracle.c, including its key-padding lengths: with a length L_b for batch
+ * b, J_i keeps only the keys j < L_b, so a key j >= L_b gets dk_j = dv_j = 0
+ * and a query row with no visible key (L_b = 0) has o_i = 0, D_i = 0 and
+ * dq_i = 0 (its lse is -inf and never used). Everything is fp64, sums sequential in
  * index order. The statistics lse_i and D_i of a head are computed from a
  * materialised score row, as the forward oracle does, before the gradient rows.
  *
@@ -38,6 +41,7 @@ typedef struct {
     long B, H, Hkv, N, d;
     int causal;
     double scale;
+    const int *kv_len;     /* [B] valid keys per batch (clamped to [0, N]), or NULL: all N */
     double *lse, *D;       /* [B*H*N]: statistics of every query row of the needed heads */
     const long *items;     /* work items of the current phase */
     long n_items;
@@ -51,7 +55,18 @@ typedef struct {
     int status;
 } job_t;
 
-static long nvis_of(const ctx_t *C, long i) { return (C->causal && i + 1 < C->N) ? i + 1 : C->N; }
+/* valid keys of batch b: the prefix j < L_b */
+static long len_of(const ctx_t *C, long b) {
+    if (!C->kv_len) return C->N;
+    const long L = C->kv_len[b];
+    return L < 0 ? 0 : (L > C->N ? C->N : L);
+}
+
+/* visible keys of query row i of batch b: j < nvis_of (causal: j <= i; key padding: j < L_b) */
+static long nvis_of(const ctx_t *C, long b, long i) {
+    const long n = (C->causal && i + 1 < C->N) ? i + 1 : C->N, L = len_of(C, b);
+    return n < L ? n : L;
+}
 
 static double dot(const float *a, const float *b, long d) {
     double s = 0.0;
@@ -65,7 +80,12 @@ static void row_stats(const ctx_t *C, long fr, double *s) {
     const long g = h / (C->H / C->Hkv);
     const float *qi = C->q + fr * d, *doi = C->dout + fr * d;
     const float *kh = C->k + (b * C->Hkv + g) * N * d, *vh = C->v + (b * C->Hkv + g) * N * d;
-    const long nv = nvis_of(C, i);
+    const long nv = nvis_of(C, b, i);
+    if (nv == 0) { /* the empty softmax: o_i = 0, lse_i = ln 0 */
+        C->lse[fr] = -INFINITY;
+        C->D[fr] = 0.0;
+        return;
+    }
     double m = -INFINITY, l = 0.0;
     for (long j = 0; j < nv; ++j) {
         s[j] = C->scale * dot(qi, kh + j * d, d);
@@ -93,7 +113,7 @@ static void dq_row(const ctx_t *C, long r, double *unused) {
     const float *kh = C->k + (b * C->Hkv + g) * N * d, *vh = C->v + (b * C->Hkv + g) * N * d;
     double *dq = C->out0 + r * d;
     for (long c = 0; c < d; ++c) dq[c] = 0.0;
-    for (long j = 0; j < nvis_of(C, i); ++j) {
+    for (long j = 0; j < nvis_of(C, b, i); ++j) {
         const double p = exp(C->scale * dot(qi, kh + j * d, d) - C->lse[fr]);
         const double ds = p * (dot(doi, vh + j * d, d) - C->D[fr]);
         for (long c = 0; c < d; ++c) dq[c] += C->scale * ds * (double)kh[j * d + c];
@@ -108,6 +128,7 @@ static void dkdv_row(const ctx_t *C, long r, double *unused) {
     const float *kj = C->k + fk * d, *vj = C->v + fk * d;
     double *dk = C->out1 + r * d, *dv = C->out2 + r * d;
     for (long c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
+    if (j >= len_of(C, b)) return; /* a padded key is visible to no query */
     for (long h = g * group; h < (g + 1) * group; ++h) {
         const long bh = b * C->H + h;
         for (long i = C->causal ? j : 0; i < N; ++i) { /* queries that see key j */
@@ -176,11 +197,12 @@ static void row_stats_item(const ctx_t *C, long r, double *s) { row_stats(C, C->
  *   q_rows  : n_q flat query rows (b*H + h)*N + i  -> dq [n_q, d]
  *   kv_rows : n_kv flat key rows (b*Hkv + g)*N + j -> dk, dv [n_kv, d]
  *   (NULL with n = the full count: every row in order)
+ *   kv_len  : [B] valid keys per batch (clamped to [0, N]), or NULL for all N
  * Returns 0 on success, 1 on a bad argument, 2 when memory runs out.
  */
 int oracle_attn_bwd_rows(const float *q, const float *k, const float *v, const float *dout, long B, long H, long Hkv,
-                         long N, long d, int causal, double scale, const long *q_rows, long n_q, const long *kv_rows,
-                         long n_kv, double *dq, double *dk, double *dv, int threads) {
+                         long N, long d, int causal, double scale, const int *kv_len, const long *q_rows, long n_q,
+                         const long *kv_rows, long n_kv, double *dq, double *dk, double *dv, int threads) {
     if (!q || !k || !v || !dout || B < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || N < 1 || d < 1 || threads < 1 ||
         n_q < 0 || n_kv < 0 || (n_q && !dq) || (n_kv && (!dk || !dv)))
         return 1;
@@ -205,7 +227,7 @@ int oracle_attn_bwd_rows(const float *q, const float *k, const float *v, const f
         const long bg = (kv_rows ? kv_rows[r] : r) / N, b = bg / Hkv, g = bg % Hkv;
         for (long h = g * group; h < (g + 1) * group; ++h) need[b * H + h] = 1;
     }
-    ctx_t C = {q, k, v, dout, B, H, Hkv, N, d, causal, scale, lse, D, items, 0, dq, dk, dv};
+    ctx_t C = {q, k, v, dout, B, H, Hkv, N, d, causal, scale, kv_len, lse, D, items, 0, dq, dk, dv};
     int rc = 0;
     /* phase 1: statistics of every row of the needed heads */
     for (long bh = 0; bh < B * H; ++bh)

@@ -170,3 +170,98 @@ def test_bad_arguments_rejected():
     with pytest.raises(ValueError):
         oracle.attention_bwd_rows(q, k[:, :, :4].contiguous(), v[:, :, :4].contiguous(), dout, False, 1.0)
     assert math.isfinite(float(oracle.attention_bwd(q, k, v, dout, False, 1.0)[0].sum()))
+
+
+# Key padding (per-batch valid-key counts L_b, the right-padding reading of the triton-transformer README's
+# boolean (batch, seq) mask): keys j >= L_b are invisible to every query of batch b.
+
+def _keep_mask(B, N, lens, causal):
+    """Boolean [B, 1, N, N] mask of visible (i, j): j < L_b, and j <= i when causal."""
+    j = torch.arange(N)
+    keep = (j[None, :] < torch.tensor(lens)[:, None])[:, None, None, :].expand(B, 1, N, N).clone()
+    if causal:
+        keep &= torch.tril(torch.ones(N, N, dtype=torch.bool))
+    return keep
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 1)])
+def test_key_padding_matches_torch_autograd_fp64_with_a_boolean_mask(H, Hkv, causal):
+    B, N, d = 3, 50, 64
+    lens = [50, 17, 1]
+    q, _, _ = ai.make_qkv(B, H, N, d, seed=81)
+    _, k, v = ai.make_qkv(B, Hkv, N, d, seed=82)
+    dout = _dout(B, H, N, d, seed=83)
+    scale = ai.default_scale(d)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dout, causal, scale, kv_len=lens)
+    qd, kd, vd = (x.to(torch.float64).requires_grad_() for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=_keep_mask(B, N, lens, causal),
+                                                         scale=scale, enable_gqa=(H != Hkv))
+    o.backward(dout.to(torch.float64))
+    np.testing.assert_allclose(dq, qd.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, kd.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, vd.grad.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_padding_matches_richardson_finite_differences(causal):
+    """Central differences of L = sum dO*o through the forward oracle with the same lengths (itself pinned to
+    brute force and SDPA with a mask), on a tiny grouped problem with a partly padded and a fully visible batch."""
+    B, H, Hkv, N, d = 2, 2, 1, 5, 3
+    lens = [3, 5]
+    q, _, _ = ai.make_qkv(B, H, N, d, seed=84, dtype="bf16")
+    _, k, v = ai.make_qkv(B, Hkv, N, d, seed=85, dtype="bf16")
+    q, k, v = q.float(), k.float(), v.float()
+    dout = _dout(B, H, N, d, seed=86, dtype="f32")
+    scale = 0.7
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dout, causal, scale, kv_len=lens)
+
+    def loss():
+        o, _ = oracle.attention(q, k, v, causal, scale, threads=1, kv_len=lens)
+        return float(np.sum(o * dout.to(torch.float64).numpy()))
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        flat = x.view(-1)
+        fd = np.zeros(flat.numel())
+        for e in range(flat.numel()):
+            def central(h):
+                x0 = float(flat[e])
+                flat[e] = x0 + h
+                up = loss()
+                flat[e] = x0 - h
+                dn = loss()
+                flat[e] = x0
+                return (up - dn) / (2 * h)
+            fd[e] = (4 * central(2.0 ** -9) - central(2.0 ** -8)) / 3
+        np.testing.assert_allclose(g.reshape(-1), fd, rtol=0, atol=2e-8, err_msg=f"d{name}")
+
+
+def test_key_padding_ignores_padded_contents_and_zeroes_their_gradients():
+    """Rewriting k and v past L_b changes nothing; dk and dv of padded keys are exactly 0."""
+    B, H, N, d = 2, 2, 40, 64
+    lens = [23, 40]
+    q, k, v = ai.make_qkv(B, H, N, d, seed=87)
+    dout = _dout(B, H, N, d, seed=88)
+    k2, v2 = k.clone(), v.clone()
+    k2[0, :, 23:] = 50.0
+    v2[0, :, 23:] = -7.0
+    for causal in (False, True):
+        a = oracle.attention_bwd(q, k, v, dout, causal, 0.125, kv_len=lens)
+        b = oracle.attention_bwd(q, k2, v2, dout, causal, 0.125, kv_len=lens)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+        assert np.all(a[1][0, :, 23:] == 0.0) and np.all(a[2][0, :, 23:] == 0.0)
+        assert np.abs(a[1][0, :, :23]).max() > 0 and np.abs(a[2][0, :, :23]).max() > 0
+
+
+def test_key_padding_empty_batch_and_clamping():
+    """L_b = 0: no query of the batch sees a key, every gradient of the batch is 0 (the other batch is untouched);
+    lengths are clamped to [0, N], so L_b >= N is no padding and L_b < 0 is L_b = 0."""
+    B, H, N, d = 2, 2, 30, 64
+    q, k, v = ai.make_qkv(B, H, N, d, seed=89)
+    dout = _dout(B, H, N, d, seed=90)
+    full = oracle.attention_bwd(q, k, v, dout, True, 0.2)
+    for lens in ([0, 30], [-5, 1000]):
+        got = oracle.attention_bwd(q, k, v, dout, True, 0.2, kv_len=lens)
+        for x, y in zip(got, full):
+            assert np.all(x[0] == 0.0)
+            np.testing.assert_array_equal(x[1], y[1])
