@@ -21,6 +21,9 @@ Other modes (used to produce the rocprofv3 summaries under profiles/):
     --write-profiles    turn the outputs of PROFILE_COMMANDS (under gpurun_out/) into profiles/ summaries
     --bwd-pmc-pass      like --pmc-pass for the gradient call (copy kernel, then fa_bwd a few times)
     --write-profiles-bwd  the same for BWD_PROFILE_COMMANDS: profiles/bwd_<workload>_rocprof.md
+    --fp8-only          time only fa_fwd_fp8 on --workload's shape (one JSON line; for profiling)
+    --fp8-pmc-pass      like --pmc-pass for the fp8 forward
+    --write-profiles-fp8  the same for FP8_PROFILE_COMMANDS: profiles/fp8_<workload>_rocprof.md and _hbm_traffic.txt
 """
 from __future__ import annotations
 
@@ -81,6 +84,20 @@ BWD_PROFILE_COMMANDS = {
     "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA "
           "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
           "-d gpurun_out/prof_bwd_{w}_sq -o run -- python bench.py --workload {w} --bwd-pmc-pass",
+}
+
+
+# The same four runs for the fp8 forward (fa_fwd_fp8 on a bf16 workload's shape, inputs quantized to e4m3).
+FP8_PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_fp8_{w}_trace -o run -- "
+             "python bench.py --workload {w} --fp8-only --steps 50 --warmup 10",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fp8_{w}_fetch -o run -- "
+             "python bench.py --workload {w} --fp8-pmc-pass",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_fp8_{w}_write -o run -- "
+             "python bench.py --workload {w} --fp8-pmc-pass",
+    "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT "
+          "SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+          "-d gpurun_out/prof_fp8_{w}_sq -o run -- python bench.py --workload {w} --fp8-pmc-pass",
 }
 
 
@@ -255,19 +272,20 @@ def fp8_record(w, steps: int, warmup: int):
                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(w.flops / (mean * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)},
             "flops_per_launch": w.flops, "kernel": "fa_fwd_fp8_kernel",
+            "traffic": traffic_from_profiles(w, "fp8_", FP8_SRCS),
             "kernel_src_sha256_16": kernel_src_hash(FP8_SRCS)}
 
 
-def traffic_from_profiles(w):
+def traffic_from_profiles(w, prefix="", srcs=KERNEL_SRCS):
     """HBM bytes per launch from the committed PMC summary, if it was taken on the current kernel source."""
-    f = PROFILES / f"{w.name}_hbm_traffic.txt"
+    f = PROFILES / f"{prefix}{w.name}_hbm_traffic.txt"
     if not f.exists():
         return None
     try:
         rec = json.loads(f.read_text())
     except json.JSONDecodeError:
         return None
-    if rec.get("kernel_src_sha256_16") != kernel_src_hash():
+    if rec.get("kernel_src_sha256_16") != kernel_src_hash(srcs):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -318,6 +336,14 @@ def bwd_pmc_pass(w, reps: int):
     time_backward(w, steps=reps, warmup=0)
     print(json.dumps({"bwd_pmc_pass": w.name, "copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "reps": reps,
                       "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}), flush=True)
+
+
+def fp8_pmc_pass(w, reps: int):
+    """Kernels for the rocprofv3 counter runs of the fp8 forward: the copy, then fa_fwd_fp8."""
+    n = _copy_kernel_pass(reps)
+    fp8_record(w, steps=reps, warmup=0)
+    print(json.dumps({"fp8_pmc_pass": w.name, "copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "reps": reps,
+                      "kernel_src_sha256_16": kernel_src_hash(FP8_SRCS)}), flush=True)
 
 
 def pmc_pass(w, reps: int):
@@ -472,6 +498,91 @@ LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active,
     print(md)
 
 
+def write_profiles_fp8(w):
+    """Summary of the FP8_PROFILE_COMMANDS outputs: profiles/fp8_<workload>_rocprof.md and ..._hbm_traffic.txt."""
+    dirs = {k: f"gpurun_out/prof_fp8_{w.name}_{k}" for k in FP8_PROFILE_COMMANDS}
+    kname = "fa_fwd_fp8_kernel"
+    trace = [r for r in _stats(dirs["trace"]) if kname in r["Name"]]
+    if not trace:
+        raise RuntimeError("no kernel statistics for the fp8 attention kernel")
+    t = trace[0]
+    avg_us = float(t["AverageNs"]) / 1e3
+    fetch, write, sq = _counters(dirs["fetch"]), _counters(dirs["write"]), _counters(dirs["sq"])
+    known_kib = 2 * (1 << 28) / 1024
+    copy_read_kib = _pick(fetch, "FETCH_SIZE", "neg_kernel")
+    copy_write_kib = _pick(write, "WRITE_SIZE", "neg_kernel")
+    f_fetch, f_write = known_kib / copy_read_kib, known_kib / copy_write_kib
+    k_read = _pick(fetch, "FETCH_SIZE", kname) * f_fetch * 1024
+    k_write = _pick(write, "WRITE_SIZE", kname) * f_write * 1024
+    busy = _pick(sq, "SQ_VALU_MFMA_BUSY_CYCLES", kname)
+    gui = _pick(sq, "GRBM_GUI_ACTIVE", kname)
+    conflict = _pick(sq, "SQ_LDS_BANK_CONFLICT", kname)
+    lds_active = _pick(sq, "SQ_LDS_IDX_ACTIVE", kname)
+    n_simd = 256 * 4
+    alg_read = (w.B * w.H * w.N + 2 * w.kv_rows) * w.d  # q, k, v: one byte per element
+    alg_write = w.B * w.H * w.N * (2 * w.d + 4)         # o in bf16, lse in fp32
+    tf = w.flops / (avg_us * 1e-6) / 1e12
+    traffic = {"kernel": t["Name"][:120], "workload": w.name.replace("_bf16_", "_fp8_"),
+               "kernel_src_sha256_16": kernel_src_hash(FP8_SRCS), "hbm_bytes_per_launch": round(k_read + k_write),
+               "read_bytes": round(k_read), "write_bytes": round(k_write),
+               "algorithmic_bytes": alg_read + alg_write, "fetch_scale": round(f_fetch, 5),
+               "write_scale": round(f_write, 5)}
+    PROFILES.mkdir(exist_ok=True)
+    (PROFILES / f"fp8_{w.name}_hbm_traffic.txt").write_text(json.dumps(traffic, indent=1) + "\n")
+    cmds = "\n".join(f"    {FP8_PROFILE_COMMANDS[k].format(w=w.name)}" for k in FP8_PROFILE_COMMANDS)
+    md = f"""# rocprofv3 summary: fa_fwd_fp8_kernel on {w.name.replace('_bf16_', '_fp8_')}
+
+Kernel source sha256[:16]: `{kernel_src_hash(FP8_SRCS)}` (exact_attention_13_amd/csrc/fa_fwd_fp8_kernel.hip and fa_gfx950.h).
+Workload: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}; q, k, v quantized per tensor to float8_e4m3fn from the
+seeded bf16-shaped inputs (v passed transposed), o in bf16, lse in fp32;
+{w.flops:.4g} FLOP per launch (4*d*H per visible query-key pair, causal triangles counted as N^2/2),
+{alg_read + alg_write} algorithmic HBM bytes per launch.
+
+Commands (run from the repository root; outputs under gpurun_out/, summarised by
+`python bench.py --workload {w.name} --write-profiles-fp8`):
+
+{cmds}
+
+## Kernel trace (--kernel-trace --stats)
+
+| kernel | calls | avg us | min us | max us |
+|---|---|---|---|---|
+| {t['Name'][:90]} | {t['Calls']} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
+
+Attention TFLOP/s at the traced average: {tf:.1f} ({100 * tf / PEAK_FP8_TFLOPS:.1f} % of {PEAK_FP8_TFLOPS} dense fp8,
+{100 * tf / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
+
+## HBM traffic (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+
+Calibration: the copy kernel (torch.neg over 2^28 bf16) reads and writes {known_kib:.0f} KiB;
+FETCH_SIZE reads {copy_read_kib:.1f} KiB (scale {f_fetch:.4f}), WRITE_SIZE reads {copy_write_kib:.1f} KiB (scale {f_write:.4f}).
+
+| | counter KiB | scaled bytes | algorithmic bytes |
+|---|---|---|---|
+| read | {k_read / f_fetch / 1024:.1f} | {k_read:.0f} | {alg_read} (q, k, v) |
+| write | {k_write / f_write / 1024:.1f} | {k_write:.0f} | {alg_write} (o, lse) |
+
+## Matrix cores and LDS (SQ counters, per dispatch)
+
+| counter | value |
+|---|---|
+| SQ_VALU_MFMA_BUSY_CYCLES | {busy:.4g} |
+| SQ_INSTS_VALU | {_pick(sq, 'SQ_INSTS_VALU', kname):.4g} |
+| SQ_INSTS_MFMA | {_pick(sq, 'SQ_INSTS_MFMA', kname):.4g} |
+| SQ_LDS_BANK_CONFLICT | {conflict:.4g} |
+| SQ_LDS_IDX_ACTIVE | {lds_active:.4g} |
+| SQ_WAIT_INST_LDS | {_pick(sq, 'SQ_WAIT_INST_LDS', kname):.4g} |
+| SQ_WAVE_CYCLES | {_pick(sq, 'SQ_WAVE_CYCLES', kname):.4g} |
+| GRBM_GUI_ACTIVE | {gui:.4g} |
+
+MFMA busy = busy cycles / 1024 SIMDs over the traced average at 2.4 GHz: {100 * busy / n_simd / (avg_us * 1e-6 * 2.4e9):.1f} %;
+over GRBM_GUI_ACTIVE / 8 (the clock measured during the kernel): {100 * busy / n_simd / (gui / 8):.1f} %.
+LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active, 1):.1f} %.
+"""
+    (PROFILES / f"fp8_{w.name}_rocprof.md").write_text(md)
+    print(md)
+
+
 def write_profiles_bwd(w):
     """Summary of the BWD_PROFILE_COMMANDS outputs: profiles/bwd_<workload>_rocprof.md (both gradient kernels)."""
     dirs = {k: f"gpurun_out/prof_bwd_{w.name}_{k}" for k in BWD_PROFILE_COMMANDS}
@@ -557,6 +668,8 @@ def main():
     ap.add_argument("--write-profiles-bwd", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--fp8-only", action="store_true", help="time only fa_fwd_fp8 on --workload's shape")
+    ap.add_argument("--fp8-pmc-pass", action="store_true")
+    ap.add_argument("--write-profiles-fp8", action="store_true")
     args = ap.parse_args()
 
     if args.summarize:
@@ -567,6 +680,9 @@ def main():
         return 0
     if args.write_profiles_bwd:
         write_profiles_bwd(ai.WORKLOADS[args.workload])
+        return 0
+    if args.write_profiles_fp8:
+        write_profiles_fp8(ai.WORKLOADS[args.workload])
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -590,6 +706,9 @@ def main():
         return 0
     if args.bwd_pmc_pass:
         bwd_pmc_pass(w, reps=3)
+        return 0
+    if args.fp8_pmc_pass:
+        fp8_pmc_pass(w, reps=5)
         return 0
     if args.bwd_only:
         print(json.dumps(backward_record(w, args.steps, args.warmup)), flush=True)
