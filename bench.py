@@ -50,7 +50,7 @@ KERNEL_SRC = ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_kernel.hip"
 KERNEL_SRCS = (KERNEL_SRC, ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
 BWD_SRCS = (ROOT / "exact_attention_13_amd" / "csrc" / "fa_bwd_kernel.hip",
             ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
-BWD_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal")
+BWD_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal", "kpad_bf16_b8h16n4096d128")
 FP8_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal")  # the same shapes, fp8 inputs
 FP8_SRCS = (ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_fp8_kernel.hip",
             ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
@@ -182,8 +182,6 @@ def time_backward(w, steps: int, warmup: int):
     import exact_attention_13_amd as fa
 
     q, k, v, o, lse, lens = _device_inputs(w)
-    if lens is not None:
-        raise ValueError("the gradient call has no key padding")
     g = torch.Generator("cpu").manual_seed(w.seed + 500)
     dout = torch.randn(tuple(q.shape), generator=g).to(torch.bfloat16).cuda()
     stream = torch.cuda.current_stream()
@@ -191,12 +189,13 @@ def time_backward(w, steps: int, warmup: int):
     fwd()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty((fa.fa_bwd_workspace_bytes(w.B, w.H, w.N),), dtype=torch.uint8, device="cuda")
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-            dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), w.B, w.H, w.Hk, w.N, w.d, int(w.causal), w.scale,
-            stream.cuda_stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
+    tail = (w.B, w.H, w.Hk, w.N, w.d, int(w.causal), w.scale, stream.cuda_stream)
+    entry, args = (fa.fa_bwd, ptrs + tail) if lens is None else (fa.fa_bwd_kpad, ptrs + (lens.data_ptr(),) + tail)
 
     def call():
-        rc = fa.fa_bwd(*args)
+        rc = entry(*args)
         if rc != 0:
             raise RuntimeError(f"fa_bwd failed: {fa.fa_strerror(rc)}")
     for _ in range(warmup):

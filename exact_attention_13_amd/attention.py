@@ -79,11 +79,14 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
 
 
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-             dout: torch.Tensor, causal: bool = False, scale: float | None = None, stream: int | None = None):
-    """Gradients (dq, dk, dv) of forward(q, k, v, causal, scale) -> (o, lse) for an upstream gradient dout of o.
+             dout: torch.Tensor, causal: bool = False, scale: float | None = None, stream: int | None = None,
+             kv_len: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv) of forward(q, k, v, causal, scale, kv_len=kv_len) -> (o, lse) for an upstream
+    gradient dout of o.
 
-    bf16 tensors: q, o, dout [B, H, N, d]; k, v [B, H_kv, N, d]; lse [B, H, N] fp32 from the same forward call.
-    Allocates dq, dk, dv and the workspace with torch and calls fa_bwd on torch's current stream (or `stream`).
+    bf16 tensors: q, o, dout [B, H, N, d]; k, v [B, H_kv, N, d]; lse [B, H, N] fp32 from the same forward call;
+    kv_len: None or the forward's device int32 [B] key-padding lengths. Allocates dq, dk, dv and the workspace with
+    torch and calls fa_bwd (fa_bwd_kpad with kv_len) on torch's current stream (or `stream`).
     """
     _check(q, k, v)
     if q.dtype != torch.bfloat16:
@@ -96,6 +99,9 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             raise ValueError(f"{name} must be a contiguous tensor of q's shape, dtype and device")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if kv_len is not None and (not isinstance(kv_len, torch.Tensor) or kv_len.dtype != torch.int32
+                               or kv_len.shape != (B,) or not kv_len.is_contiguous() or kv_len.device != q.device):
+        raise ValueError("kv_len must be a contiguous int32 [B] tensor on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q)
@@ -105,9 +111,13 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     with torch.cuda.device(q.device):
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
-        rc = binding.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, H_kv, N, d,
-                            int(bool(causal)), float(scale), int(stream))
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
+        tail = (B, H, H_kv, N, d, int(bool(causal)), float(scale), int(stream))
+        if kv_len is not None:
+            rc = binding.fa_bwd_kpad(*ptrs, kv_len.data_ptr(), *tail)
+        else:
+            rc = binding.fa_bwd(*ptrs, *tail)
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_bwd failed ({rc}): {binding.fa_strerror(rc)}")
     return dq, dk, dv

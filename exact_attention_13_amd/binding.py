@@ -25,8 +25,8 @@ FA_ERR_ARG = 5
 FA_ERR_ALIAS = 6
 FA_ERR_HIP = 7
 
-EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_f32",
-           "fa_strerror", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_fp8", "fa_bwd", "fa_bwd_kpad", "fa_bwd_workspace_bytes",
+           "fa_fwd_f32", "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_attention_13_amd/build.py` "
@@ -45,6 +45,8 @@ _lib.fa_fwd_fp8.restype = _I
 _lib.fa_fwd_fp8.argtypes = [_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _P]
 _lib.fa_bwd.restype = _I
 _lib.fa_bwd.argtypes = [_P] * 10 + [_I] * 6 + [ctypes.c_float, _P]
+_lib.fa_bwd_kpad.restype = _I
+_lib.fa_bwd_kpad.argtypes = [_P] * 11 + [_I] * 6 + [ctypes.c_float, _P]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.fa_fwd_f32.restype = _I
@@ -88,6 +90,13 @@ def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int
     """Raw entry point: gradients dq [B,H,N,d], dk, dv [B,H_kv,N,d] (bf16) of the forward for upstream dout;
     workspace: fa_bwd_workspace_bytes(B, H, N) bytes of device memory."""
     return _lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H_kv, N, d, causal, scale, stream)
+
+
+def fa_bwd_kpad(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, workspace: int,
+                kv_len: int, B: int, H: int, H_kv: int, N: int, d: int, causal: int, scale: float, stream: int) -> int:
+    """Raw entry point: fa_bwd for a forward made with fa_fwd_kpad; kv_len is the same device int32 [B] array."""
+    return _lib.fa_bwd_kpad(q, k, v, o, lse, dout, dq, dk, dv, workspace, kv_len, B, H, H_kv, N, d, causal, scale,
+                            stream)
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:

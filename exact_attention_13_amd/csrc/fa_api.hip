@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 10300;  // 1.3.0
+constexpr int kVersion = 10400;  // 1.4.0
 constexpr long long kMaxHeads = 65535;   // B*H is the grid's y extent
 constexpr long long kMaxN = 1LL << 30;
 
@@ -89,6 +89,35 @@ int validate_bwd(const void* const* in, int n_in, void* const* out, int n_out, c
   return FA_OK;
 }
 
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+            void* dk, void* dv, float* workspace, const int* kv_len, bool with_len, int B, int H, int H_kv, int N,
+            int d, int causal, float scale, hipStream_t stream) {
+  const void* in[] = {q, k, v, o, dout};
+  void* out[] = {dq, dk, dv};
+  bool empty = false;
+  int rc = validate_bwd(in, 5, out, 3, lse, workspace, B, H, H_kv, N, d, causal, scale, &empty);
+  if (rc != FA_OK || empty) return rc;
+  if (with_len && !kv_len) return FA_ERR_NULL;
+  if (with_len && ((uintptr_t)kv_len & 3)) return FA_ERR_ALIGN;
+  // byte ranges: q, o, dout, dq are [B,H,N,d]; k, v, dk, dv are [B,H_kv,N,d]; lse [B,H,N]; kv_len [B]; the
+  // workspace
+  const size_t tq = (size_t)B * H * N * d * 2, tk = (size_t)B * H_kv * N * d * 2, tl = (size_t)B * H * N * 4;
+  const size_t tw = fa::bwd_workspace_bytes(B, H, N);
+  const void* rin[] = {q, k, v, o, dout, lse, kv_len};
+  const size_t nin[] = {tq, tk, tk, tq, tq, tl, with_len ? (size_t)B * sizeof(int) : 0};
+  void* rout[] = {dq, dk, dv, workspace};
+  const size_t nout[] = {tq, tk, tk, tw};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(rout[i], nout[i], rin[j], nin[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(rout[i], nout[i], rout[j], nout[j])) return FA_ERR_ALIAS;
+  }
+  const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H_kv, N, d,
+                                           causal != 0, scale, with_len ? kv_len : nullptr, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,27 +140,15 @@ int fa_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* workspace, int B, int H, int H_kv, int N, int d, int causal, float scale,
            hipStream_t stream) {
-  const void* in[] = {q, k, v, o, dout};
-  void* out[] = {dq, dk, dv};
-  bool empty = false;
-  int rc = validate_bwd(in, 5, out, 3, lse, workspace, B, H, H_kv, N, d, causal, scale, &empty);
-  if (rc != FA_OK || empty) return rc;
-  // byte ranges: q, o, dout, dq are [B,H,N,d]; k, v, dk, dv are [B,H_kv,N,d]; lse [B,H,N]; the workspace
-  const size_t tq = (size_t)B * H * N * d * 2, tk = (size_t)B * H_kv * N * d * 2, tl = (size_t)B * H * N * 4;
-  const size_t tw = fa::bwd_workspace_bytes(B, H, N);
-  const void* rin[] = {q, k, v, o, dout, lse};
-  const size_t nin[] = {tq, tk, tk, tq, tq, tl};
-  void* rout[] = {dq, dk, dv, workspace};
-  const size_t nout[] = {tq, tk, tk, tw};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(rout[i], nout[i], rin[j], nin[j])) return FA_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(rout[i], nout[i], rout[j], nout[j])) return FA_ERR_ALIAS;
-  }
-  const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H_kv, N, d,
-                                           causal != 0, scale, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, nullptr, false, B, H, H_kv, N, d, causal, scale,
+                 stream);
+}
+
+int fa_bwd_kpad(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, float* workspace, const int* kv_len, int B, int H, int H_kv, int N, int d,
+                int causal, float scale, hipStream_t stream) {
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, kv_len, true, B, H, H_kv, N, d, causal, scale,
+                 stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {

@@ -23,6 +23,10 @@
 //     passes from the first wave of the pair to the second through LDS.
 // The workspace holds the pairs (D_i, lse_i*log2e) as [B*H][Npad] float2, Npad = N rounded up to 128; rows
 // N .. Npad-1 hold (0, +inf), which makes p (and dS) of those rows exactly 0 in the dk/dv kernel.
+// Key padding (the forward's per-batch count Nk of valid keys, triton-transformer README usage example "ex. BERT"):
+// the dq kernel visits only the key tiles below Nk and masks keys >= Nk like the sequence end; the dk/dv kernel
+// masks them, loads no k or v row past Nk and writes zero gradients for them. With Nk = 0 no tile is visited
+// (o = 0, lse = -inf there), so every gradient of the batch is 0.
 // S and dP are computed in both kernels (7 matrix products instead of the 5 of a single pass with atomic dq
 // updates): the price of determinism.
 //
@@ -95,7 +99,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ o, const float* __restrict__ lse, const __bf16* __restrict__ dout,
-    __bf16* __restrict__ dq, float* __restrict__ ws, int N, int BH, float scale, int group) {
+    __bf16* __restrict__ dq, float* __restrict__ ws, int N, int BH, float scale, int group, int H,
+    const int* __restrict__ kv_len) {
   using T = BwdTile<D>;
   constexpr int NW = kBwdWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
@@ -112,10 +117,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;
   const __bf16* kh = k + kv_off;
   const __bf16* vh = v + kv_off;
+  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bh / H], 0), N)) : N;
 
   const int q_lo = qb * kBwdBlock;
   const int q_last = min(q_lo + kBwdBlock, N) - 1;
-  const int n_tiles = CAUSAL ? (q_last / kBwdTile + 1) : (N + kBwdTile - 1) / kBwdTile;
+  const int key_tiles = (Nk + kBwdTile - 1) / kBwdTile;
+  const int n_tiles = CAUSAL ? min(q_last / kBwdTile + 1, key_tiles) : key_tiles;
   const int q0w = q_lo + wave * kBwdRows;
   const int my_q = q0w + l32;
   const int wave_tiles =
@@ -155,9 +162,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   auto copy_tile = [&](const __bf16* src, lds_char* dst, int j) __attribute__((always_inline)) {
     const int row0 = j * kBwdTile;
-    // rows past N arrive as zeros; scalar byte count and base keep the descriptor in scalar registers
-    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kBwdTile)) * T::RB);
-    const int row_base = __builtin_amdgcn_readfirstlane(min(row0, N - 1));
+    // rows past Nk arrive as zeros (only tiles below Nk are copied, so Nk >= 1 here); scalar byte count and base
+    // keep the descriptor in scalar registers
+    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(Nk - row0, kBwdTile)) * T::RB);
+    const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Nk - 1));
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * D, bytes);
 #pragma unroll
     for (int p = 0; p < kCopies; ++p) lds_copy16_inline(r, dst + (wave + NW * p) * 1024, dma[p]);
@@ -205,13 +213,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       }
     schedule_reads_ahead<4 * kDB>();
     const int kv0 = j * kBwdTile;
-    if ((kv0 + kBwdTile > N) || (CAUSAL && kv0 + kBwdTile - 1 > q0w)) {
+    if ((kv0 + kBwdTile > Nk) || (CAUSAL && kv0 + kBwdTile - 1 > q0w)) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool vis = (key < N) && (!CAUSAL || key <= my_q);
+          const bool vis = (key < Nk) && (!CAUSAL || key <= my_q);
           s[b][r] = vis ? s[b][r] : -INFINITY;
         }
     }
@@ -311,7 +319,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ ws, __bf16* __restrict__ dk,
-    __bf16* __restrict__ dv, int N, int BHkv, float scale, int group) {
+    __bf16* __restrict__ dv, int N, int BHkv, float scale, int group, int Hkv, const int* __restrict__ kv_len) {
   using T = BwdTile<D, kDkdvTile>;
   constexpr int NW = kDkdvWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   constexpr int kSub = kDkdvTile / kBwdRows;  // 32-row sub-blocks per query tile
@@ -333,17 +341,19 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const int kblk = CAUSAL ? nk - 1 - t : t;
   const size_t kv_off = (size_t)bkv * (size_t)N * D;
   const int bh0 = bkv * group;  // first query head of this key/value head's group
+  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bkv / Hkv], 0), N)) : N;
 
   const int k0 = kblk * kBwdBlock;
   const int kw0 = k0 + pair * kBwdRows;
   const int my_k = kw0 + l32;
 
-  // This lane's key: k fragments (p wave, B operand of S = Q K^T) or v fragments (dS wave, of dP = dO V^T)
+  // This lane's key: k fragments (p wave, B operand of S = Q K^T) or v fragments (dS wave, of dP = dO V^T); keys
+  // past Nk read as zeros (their contents may be anything), so dP and dS stay finite and exactly 0 there
   bf16x8 kvf[kDB];
   const __bf16* kvsrc = pw ? k : v;
 #pragma unroll
   for (int kb = 0; kb < kDB; ++kb)
-    kvf[kb] = (my_k < N) ? *(const bf16x8*)(kvsrc + kv_off + (size_t)my_k * D + 16 * kb + 8 * h) : (bf16x8){};
+    kvf[kb] = (my_k < Nk) ? *(const bf16x8*)(kvsrc + kv_off + (size_t)my_k * D + 16 * kb + 8 * h) : (bf16x8){};
 
   int dma[kCopies];
 #pragma unroll
@@ -357,7 +367,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const int nqt = (N + kDkdvTile - 1) / kDkdvTile;
   const int t0 = CAUSAL ? kblk : 0;
   const int per_head = nqt - t0;
-  const int n_iter = (k0 < N) ? group * per_head : 0;
+  const int n_iter = (k0 < Nk) ? group * per_head : 0;  // a block of padded keys only writes zeros
   const int npad = ws_rows(N);
   auto copy_iter = [&](int it, int S) __attribute__((always_inline)) {
     const int hq = bh0 + it / per_head;
@@ -420,11 +430,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     const lds_char* tr_src = pw ? os : qs;    // dO^T for dV^T, q^T for dK^T
     if constexpr (pw) {
       const int qlo = row0 + 32 * sb;
-      if ((qlo + kBwdRows > N) || (CAUSAL && qlo < kw0 + kBwdRows - 1)) {
+      if ((qlo + kBwdRows > N) || (kw0 + kBwdRows > Nk) || (CAUSAL && qlo < kw0 + kBwdRows - 1)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = qlo + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool vis = (qi < N) && (!CAUSAL || my_k <= qi);
+          const bool vis = (qi < N) && (my_k < Nk) && (!CAUSAL || my_k <= qi);
           x[r] = vis ? x[r] : -INFINITY;
         }
       }
@@ -500,10 +510,10 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     run(std::false_type{});
   }
 
-  // dk_j = scale * dK^T, dv_j = dV^T; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k
+  // dk_j = scale * dK^T, dv_j = dV^T; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k (0 past Nk)
   if (my_k < N) {
     __bf16* row = (pw ? dv : dk) + kv_off + (size_t)my_k * D;
-    const float f = pw ? 1.f : scale;
+    const float f = (my_k < Nk) ? (pw ? 1.f : scale) : 0.f;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
@@ -520,7 +530,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv,
-                             int N, float scale, hipStream_t stream) {
+                             int N, float scale, const int* kv_len, hipStream_t stream) {
   const int group = H / Hkv;
   constexpr int lds_a = 4 * BwdTile<D>::kBytes;
   constexpr int lds_b = 2 * (2 * BwdTile<D, kDkdvTile>::kBytes + kWsTileBytes) + 8 * kPSlotBytes;
@@ -533,23 +543,22 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   const unsigned nblk = (unsigned)((N + kBwdBlock - 1) / kBwdBlock);
   hipLaunchKernelGGL(ka, dim3(nblk, (unsigned)(B * H)), dim3(kBwdThreads), lds_a, stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse, (const __bf16*)dout, (__bf16*)dq, ws,
-                     N, B * H, scale, group);
+                     N, B * H, scale, group, H, kv_len);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv)), dim3(64 * kDkdvWaves), lds_b, stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const float*)ws, (__bf16*)dk,
-                     (__bf16*)dv, N, B * Hkv, scale, group);
+                     (__bf16*)dv, N, B * Hkv, scale, group, Hkv, kv_len);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv, int N,
-                           int d, bool causal, float scale, hipStream_t stream) {
-  if (d == 64)
-    return causal ? launch_bwd<64, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream)
-                  : launch_bwd<64, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream);
-  return causal ? launch_bwd<128, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream)
-                : launch_bwd<128, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, stream);
+                           int d, bool causal, float scale, const int* kv_len, hipStream_t stream) {
+#define FA_BWD(D, C) launch_bwd<D, C>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, kv_len, stream)
+  if (d == 64) return causal ? FA_BWD(64, true) : FA_BWD(64, false);
+  return causal ? FA_BWD(128, true) : FA_BWD(128, false);
+#undef FA_BWD
 }
 
 }  // namespace fa

@@ -16,10 +16,11 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           bool causal, float scale, hipStream_t stream);
 // Enqueue the two gradient kernels (dq and the workspace pairs, then dk and dv). Arguments must already be valid
 // (d is 64 or 128, B, H, N >= 1, Hkv >= 1 dividing H, pointers device-resident and aligned, ws of
-// bwd_workspace_bytes(B, H, N) bytes); returns the launch status.
+// bwd_workspace_bytes(B, H, N) bytes); kv_len as launch_fwd_bf16 (the forward's lengths); returns the launch
+// status.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv, int N,
-                           int d, bool causal, float scale, hipStream_t stream);
+                           int d, bool causal, float scale, const int* kv_len, hipStream_t stream);
 // Workspace of the gradient kernels: (D_i, lse_i*log2e) float pairs, [B*H][N rounded up to 128].
 inline size_t bwd_workspace_bytes(int B, int H, int N) {
   return (size_t)B * (size_t)H * (size_t)((N + 127) / 128 * 128) * 2 * sizeof(float);

@@ -136,7 +136,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dk, void* dv, float* workspace, int B, int H, int H_kv, int N, int d, int causal, float scale,
            hipStream_t stream);
 
-/* fa_bwd_workspace_bytes -- bytes of the fa_bwd workspace (0 for an empty problem). */
+/*
+ * fa_bwd_kpad -- fa_bwd for a forward call made with fa_fwd_kpad: the
+ * gradients under the same key-padding lengths.
+ *   kv_len  : const int32 [B] (device), the lengths given to fa_fwd_kpad
+ *             (clamped to [0, N] on the device); o and lse must come from
+ *             that call. Key j >= kv_len[b] is visible to no query of batch
+ *             b, so its dk and dv rows are written as 0 (whatever k and v
+ *             hold there); with kv_len[b] = 0 every gradient of batch b is 0.
+ * kv_len must be non-NULL (FA_ERR_NULL), 4-byte aligned (FA_ERR_ALIGN) and
+ * must not overlap an output or the workspace (FA_ERR_ALIAS); it is only
+ * read, by the kernels. Everything else as fa_bwd; fa_bwd_kpad with every
+ * kv_len[b] >= N gives fa_bwd's results.
+ */
+int fa_bwd_kpad(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, float* workspace, const int* kv_len, int B, int H, int H_kv, int N, int d,
+                int causal, float scale, hipStream_t stream);
+
+/* fa_bwd_workspace_bytes -- bytes of the fa_bwd / fa_bwd_kpad workspace (0 for an empty problem). */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 10300
+    assert fa.fa_version() == 10400
     for code in range(8):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
@@ -143,6 +143,26 @@ def test_backward_error_codes():
     assert _bwd(ws=BWD["dq"] - 16) == fa.FA_ERR_ALIAS             # workspace runs into dq
     # empty problem: success, pointers ignored
     assert _bwd(N=0, **{name: 0 for name in BWD}) == fa.FA_OK
+
+
+def _bwd_kpad(B=1, H=2, H_kv=2, N=64, d=64, causal=0, scale=0.125, kv_len=A + 0xA000000, **ptrs):
+    p = dict(BWD, **ptrs)
+    return fa.fa_bwd_kpad(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"], p["dv"], p["ws"],
+                          kv_len, B, H, H_kv, N, d, causal, scale, 0)
+
+
+def test_backward_kpad_error_codes():
+    for name in BWD:
+        assert _bwd_kpad(**{name: 0}) == fa.FA_ERR_NULL, name
+    assert _bwd_kpad(kv_len=0) == fa.FA_ERR_NULL
+    assert _bwd_kpad(kv_len=A + 0xA000000 + 2) == fa.FA_ERR_ALIGN
+    assert _bwd_kpad(dq=BWD["dq"] + 8) == fa.FA_ERR_ALIGN
+    assert _bwd_kpad(kv_len=BWD["dk"] + 64) == fa.FA_ERR_ALIAS     # lengths inside dk
+    assert _bwd_kpad(kv_len=BWD["ws"] + 16) == fa.FA_ERR_ALIAS     # lengths inside the workspace
+    assert _bwd_kpad(H_kv=3) == fa.FA_ERR_SHAPE
+    assert _bwd_kpad(d=80) == fa.FA_ERR_HEADDIM
+    assert _bwd_kpad(causal=2) == fa.FA_ERR_ARG
+    assert _bwd_kpad(N=0, kv_len=0, **{name: 0 for name in BWD}) == fa.FA_OK
 
 
 def test_fp8_error_codes():

@@ -174,3 +174,111 @@ def test_backward_writes_nothing_outside_its_outputs(fa):
     ref = fa.backward(q, k, v, o, lse, dout)
     torch.cuda.synchronize()
     assert all(torch.equal(views[i], ref[i]) for i in range(3))
+
+
+# Key padding (fa_bwd_kpad): the forward and the gradients take the same per-batch valid-key counts; the oracle
+# gets them clamped to [0, N] as the kernels clamp them. Same bar as above per gradient tensor, and structural
+# checks: gradients of padded keys (and of a batch with no valid key) are exactly 0, padded key contents are never
+# read (NaN there changes nothing), lengths >= N give fa_bwd's bits.
+
+def _run_kpad(fa, q, k, v, dout, causal, scale, lens):
+    qd, kd, vd, dd = (t.to("cuda:0") for t in (q, k, v, dout))
+    kl = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, kv_len=kl)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dd, causal=causal, scale=scale, kv_len=kl)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _clamp(lens, N):
+    return [min(max(int(x), 0), N) for x in lens]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,lens", [(63, [63, 1, 0, 40]), (130, [129, 64, 65, 200]), (333, [333, 128, 7, -3]),
+                                    (1000, [999, 513, 256, 1])])
+def test_backward_key_padding(fa, N, lens, d, causal):
+    B, H, Hkv = 4, 4, 2
+    label = f"bwd kpad B{B} H{H} Hkv{Hkv} N{N} d{d} lens={lens} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v, dout = _inputs(B, H, Hkv, N, d, 700 + N)
+    scale = ai.default_scale(d)
+    dq, dk, dv = _run_kpad(fa, q, k, v, dout, causal, scale, lens)
+    cl = _clamp(lens, N)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, dout, causal, scale, kv_len=cl)
+    _check(f"{label} dq", dq, rq)
+    _check(f"{label} dk", dk, rk)
+    _check(f"{label} dv", dv, rv)
+    for b, L in enumerate(cl):
+        assert torch.count_nonzero(dk[b, :, L:]) == 0 and torch.count_nonzero(dv[b, :, L:]) == 0, (b, L)
+        if L == 0:
+            assert torch.count_nonzero(dq[b]) == 0, b
+
+
+def test_backward_key_padding_large_sampled_rows(fa):
+    """The padded encoder workload's shape (B8 H16 N4096 d128, lengths 4096 ... 777), sampled dq and dk/dv rows."""
+    w = ai.WORKLOADS["kpad_bf16_b8h16n4096d128"]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    lens = ai.kv_len_of(w)
+    label = f"bwd kpad {w.name}"
+    print(f"[case] {label}", flush=True)
+    q, k, v = ai.make_workload(w)
+    dout = _dout(B, H, N, d, 720)
+    dq, dk, dv = _run_kpad(fa, q, k, v, dout, False, w.scale, lens)
+    g = torch.Generator("cpu").manual_seed(721)
+    heads = np.array([0, 5 * H + 3, 6 * H + 7, B * H - 1])  # batches 0, 5 (L=777), 6, 7
+    edges = np.array([0, 1, 776, 777, 2047, 2048, N - 1])
+    rows = np.unique(np.concatenate([(heads[:, None] * N + edges[None, :]).ravel(),
+                                     heads[torch.randint(0, 4, (160,), generator=g).numpy()] * N
+                                     + torch.randint(0, N, (160,), generator=g).numpy()]))
+    rq, rk, rv = oracle.attention_bwd_rows(q, k, v, dout, False, w.scale, q_rows=rows, kv_rows=rows, kv_len=lens)
+    idx = torch.from_numpy(rows).to(dq.device)
+    _check(f"{label} dq", dq.reshape(-1, d)[idx], rq)
+    _check(f"{label} dk", dk.reshape(-1, d)[idx], rk)
+    _check(f"{label} dv", dv.reshape(-1, d)[idx], rv)
+    for b, L in enumerate(lens):
+        assert torch.count_nonzero(dk[b, :, L:]) == 0 and torch.count_nonzero(dv[b, :, L:]) == 0, (b, L)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_key_padding_never_reads_padded_keys(fa, causal):
+    B, H, Hkv, N, d = 3, 4, 2, 300, 128
+    lens = [300, 131, 64]
+    q, k, v, dout = _inputs(B, H, Hkv, N, d, 730)
+    scale = ai.default_scale(d)
+    a = _run_kpad(fa, q, k, v, dout, causal, scale, lens)
+    k2, v2 = k.clone(), v.clone()
+    for b, L in enumerate(lens):
+        k2[b, :, L:] = float("nan")
+        v2[b, :, L:] = float("inf")
+    b_ = _run_kpad(fa, q, k2, v2, dout, causal, scale, lens)
+    assert all(torch.equal(x, y) for x, y in zip(a, b_))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_full_lengths_equal_fa_bwd(fa, causal):
+    B, H, Hkv, N, d = 2, 4, 1, 257, 64
+    q, k, v, dout = _inputs(B, H, Hkv, N, d, 740)
+    scale = ai.default_scale(d)
+    a = _run_kpad(fa, q, k, v, dout, causal, scale, [N, N + 100])
+    b = _run(fa, q, k, v, dout, causal, scale)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_backward_kpad_raw_entry_point(fa):
+    B, H, Hkv, N, d = 2, 4, 2, 100, 64
+    q, k, v, dout = (t.to("cuda:0") for t in _inputs(B, H, Hkv, N, d, 750))
+    kl = torch.tensor([37, 100], dtype=torch.int32, device="cuda:0")
+    o, lse = fa.forward(q, k, v, causal=True, kv_len=kl)
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, N),), dtype=torch.uint8, device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    sc = ai.default_scale(d)
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = fa.fa_bwd_kpad(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), kl.data_ptr(), B, H, Hkv, N, d, 1,
+                        sc, stream)
+    assert rc == fa.FA_OK
+    ref = fa.backward(q, k, v, o, lse, dout, causal=True, kv_len=kl)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
