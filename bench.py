@@ -304,15 +304,30 @@ def cpu_baseline(w, n_rows: int):
     t0 = time.perf_counter()
     oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows, threads=threads, kv_len=lens)
     dt = time.perf_counter() - t0
-    i = rows % w.N
-    n_valid = np.array(lens)[rows // (w.H * w.N)] if lens else np.full_like(i, w.N)
-    keys = np.minimum(i + 1, n_valid) if w.causal else n_valid
-    flops = float(np.sum(4.0 * keys * w.d))  # 2 FLOP per q.k product term + 2 per p.v term, per visible key
+    def sample_flops(r):
+        i = r % w.N
+        n_valid = np.array(lens)[r // (w.H * w.N)] if lens else np.full_like(i, w.N)
+        keys = np.minimum(i + 1, n_valid) if w.causal else n_valid
+        return float(np.sum(4.0 * keys * w.d))  # 2 FLOP per q.k product term + 2 per p.v term, per visible key
     # the metric counts 4*N*d per row (halved on average when causal); sampled rows use their real key counts
+    flops = sample_flops(rows)
+    # the same oracle on one thread, over the first 1/16 of the sample
+    rows1 = rows[: max(1, len(rows) // 16)]
+    t1 = time.perf_counter()
+    oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows1, threads=1, kv_len=lens)
+    dt1 = time.perf_counter() - t1
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} seeded random query rows of {w.name} ({len(rows) / (w.B * w.H * w.N):.1%} of "
                       f"the rows), fp64, {dt:.2f} s wall on {threads} threads; FLOPs counted as 4*d per visible key",
-            "seconds": dt}
+            "single_thread": {"value": sample_flops(rows1) / dt1 / 1e12, "rows": len(rows1),
+                              "seconds": round(dt1, 3)},
+            "cpu_model": cpu, "host_cpus": os.cpu_count(), "seconds": dt}
 
 
 def _copy_kernel_pass(reps: int) -> int:
