@@ -140,6 +140,40 @@ def attention(q, k, v, causal: bool, scale: float, threads: int | None = None, k
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
 
 
+def attention_varlen(q, k, v, cu_seqlens, causal: bool, scale: float, rows=None, threads: int | None = None):
+    """Attention of packed variable-length sequences: every sequence is its own attention problem.
+
+    q: [T, H, d], k and v: [T, Hkv, d] (tokens of all sequences back to back; Hkv divides H); cu_seqlens: B+1
+    offsets, sequence b holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (the variable-length batches of the
+    survey's key-padding row, read as FlashAttention-style packing). Queries of sequence b see only the keys of
+    sequence b (and, when causal, only those at or before their own position in it). rows: flat ids t*H + h
+    (token t, query head h), or None for all T*H in that order. Each sequence is handed to attention_rows as a
+    [1, H, L, d] problem. Returns (o [n, d] float64, lse [n] float64).
+    """
+    qa, ka, va = _as_f32(q), _as_f32(k), _as_f32(v)
+    if qa.ndim != 3 or ka.shape != va.shape or ka.ndim != 3 or ka.shape[0] != qa.shape[0] or \
+            ka.shape[2] != qa.shape[2] or qa.shape[1] % ka.shape[1] != 0:
+        raise ValueError(f"q [T,H,d] and k, v [T,Hkv,d] disagree: {qa.shape} {ka.shape} {va.shape}")
+    T, H, d = qa.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    if cu.size < 1 or cu[0] != 0 or cu[-1] != T or (np.diff(cu) < 0).any():
+        raise ValueError(f"cu_seqlens must rise from 0 to {T}: {cu}")
+    ids = np.arange(T * H, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    if ids.size and (ids.min() < 0 or ids.max() >= T * H):
+        raise ValueError("row ids out of range")
+    tok, head = ids // H, ids % H
+    seq = np.searchsorted(cu, tok, side="right") - 1  # the sequence holding each token
+    o = np.zeros((ids.size, d), dtype=np.float64)
+    lse = np.zeros((ids.size,), dtype=np.float64)
+    for b in np.unique(seq):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        sel = np.nonzero(seq == b)[0]
+        per = lambda x: np.ascontiguousarray(x[lo:hi].transpose(1, 0, 2)[None])  # [1, heads, L, d]
+        flat = head[sel] * (hi - lo) + (tok[sel] - lo)
+        o[sel], lse[sel] = attention_rows(per(qa), per(ka), per(va), causal, scale, rows=flat, threads=threads)
+    return o, lse
+
+
 def attention_bwd_rows(q, k, v, dout, causal: bool, scale: float, q_rows=None, kv_rows=None,
                        threads: int | None = None, kv_len=None):
     """Gradients of the attention forward for an upstream gradient dout of o (none for lse).
