@@ -101,6 +101,75 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Packed variable-length batch: B = len(lens) sequences back to back, q [T, H, d], k and v [T, Hkv, d]."""
+    name: str
+    lens: tuple
+    H: int
+    d: int
+    causal: bool
+    seed: int
+    Hkv: int = 0
+    sampled_rows: int = 256
+
+    @property
+    def B(self) -> int:
+        return len(self.lens)
+
+    @property
+    def T(self) -> int:
+        return sum(self.lens)
+
+    @property
+    def max_len(self) -> int:
+        return max(self.lens)
+
+    @property
+    def Hk(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    @property
+    def cu_seqlens(self) -> list:
+        return [0] + list(np.cumsum(self.lens).tolist())
+
+    @property
+    def flops(self) -> float:
+        """4*H*d per visible (query, key) pair of every sequence; causal triangles counted as L^2/2."""
+        return 4.0 * self.H * self.d * sum(L * L / 2 if self.causal else float(L * L) for L in self.lens)
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """q, k, v read once, o written once (bf16), lse written once (fp32)."""
+        return 2 * self.T * self.d * (2 * self.H + 2 * self.Hk) + 4 * self.T * self.H
+
+
+# Packed batches: the key-padding lengths without the padding (encoder-style), and a causal mix of short and
+# long sequences with grouped heads (decoder-style).
+VARLEN_WORKLOADS = {
+    "varlen_bf16_b8h16d128": VarlenWorkload("varlen_bf16_b8h16d128", (4096, 3001, 2500, 4000, 1234, 777, 3333, 2048),
+                                           16, 128, False, 9),
+    "varlen_bf16_b12h32kv8d128_causal": VarlenWorkload(
+        "varlen_bf16_b12h32kv8d128_causal", (8192, 512, 3000, 1, 6000, 4096, 777, 2048, 5555, 64, 100, 1900),
+        32, 128, True, 10, Hkv=8),
+}
+
+
+def make_qkv_varlen(lens, H: int, d: int, seed: int, Hkv: int | None = None):
+    """Packed inputs of sum(lens) tokens: q [T, H, d] and k, v [T, Hkv, d] ~ N(0, 1) in fp32 (CPU generator, drawn
+    in that order), rounded to bf16. Returns CPU tensors."""
+    T = int(sum(lens))
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((T, H, d), generator=g, dtype=torch.float32)
+    k = torch.randn((T, Hkv or H, d), generator=g, dtype=torch.float32)
+    v = torch.randn((T, Hkv or H, d), generator=g, dtype=torch.float32)
+    return tuple(x.to(torch.bfloat16).contiguous() for x in (q, k, v))
+
+
 def default_scale(d: int) -> float:
     """1/sqrt(d) rounded to fp32 (the value handed to both sides)."""
     return float(np.float32(1.0 / math.sqrt(d)))

@@ -149,3 +149,37 @@ def forward_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, q_scale: flo
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_fwd_fp8 failed ({rc}): {binding.fa_strerror(rc)}")
     return o, lse
+
+
+def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                   causal: bool = False, scale: float | None = None, stream: int | None = None):
+    """Attention over packed variable-length sequences: q [total, H, d], k and v [total, H_kv, d] (bf16, contiguous,
+    on the GPU), cu_seqlens a device int32 [B+1] tensor of sequence offsets (0 .. total), max_seqlen >= the longest
+    sequence. Every sequence is its own attention problem. Returns o (bf16 [total, H, d]) and lse (fp32 [H, total]).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-d GPU tensor [total, heads, d]")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    total, H, d = q.shape
+    if k.shape != v.shape or k.shape[0] != total or k.shape[2] != d or k.shape[1] < 1 or H % k.shape[1] != 0 \
+            or not (q.device == k.device == v.device):
+        raise ValueError(f"q [total,H,d] and k, v [total,H_kv,d] disagree: {tuple(q.shape)} {tuple(k.shape)}")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or not cu_seqlens.is_contiguous() or cu_seqlens.device != q.device):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    B = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        rc = binding.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   cu_seqlens.data_ptr(), B, H, k.shape[1], total, int(max_seqlen), d,
+                                   int(bool(causal)), float(scale), int(stream))
+    if rc != binding.FA_OK:
+        raise RuntimeError(f"fa_fwd_varlen failed ({rc}): {binding.fa_strerror(rc)}")
+    return o, lse

@@ -25,8 +25,8 @@ FA_ERR_ARG = 5
 FA_ERR_ALIAS = 6
 FA_ERR_HIP = 7
 
-EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_fp8", "fa_bwd", "fa_bwd_kpad", "fa_bwd_workspace_bytes",
-           "fa_fwd_f32", "fa_strerror", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_kpad",
+           "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_attention_13_amd/build.py` "
@@ -41,6 +41,8 @@ _lib.fa_fwd_gqa.restype = _I
 _lib.fa_fwd_gqa.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _lib.fa_fwd_kpad.restype = _I
 _lib.fa_fwd_kpad.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_lib.fa_fwd_varlen.restype = _I
+_lib.fa_fwd_varlen.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _P]
 _lib.fa_fwd_fp8.restype = _I
 _lib.fa_fwd_fp8.argtypes = [_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _P]
 _lib.fa_bwd.restype = _I
@@ -77,6 +79,13 @@ def fa_fwd_kpad(q: int, k: int, v: int, o: int, lse: int, kv_len: int, B: int, H
                 causal: int, scale: float, stream: int) -> int:
     """Raw entry point: fa_fwd_gqa plus kv_len, a device int32 [B] array of valid-key counts (key padding)."""
     return _lib.fa_fwd_kpad(q, k, v, o, lse, kv_len, B, H, H_kv, N, d, causal, scale, stream)
+
+
+def fa_fwd_varlen(q: int, k: int, v: int, o: int, lse: int, cu_seqlens: int, B: int, H: int, H_kv: int, total: int,
+                  max_seqlen: int, d: int, causal: int, scale: float, stream: int) -> int:
+    """Raw entry point: packed sequences, bf16 q/o [total,H,d], k/v [total,H_kv,d], lse [H,total], cu_seqlens
+    int32 [B+1] on the device."""
+    return _lib.fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, H_kv, total, max_seqlen, d, causal, scale, stream)
 
 
 def fa_fwd_fp8(q: int, k: int, vt: int, o: int, lse: int, q_scale: float, k_scale: float, v_scale: float, B: int,

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 10400;  // 1.4.0
+constexpr int kVersion = 10500;  // 1.5.0
 constexpr long long kMaxHeads = 65535;   // B*H is the grid's y extent
 constexpr long long kMaxN = 1LL << 30;
 
@@ -118,6 +118,31 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int run_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens, int B,
+               int H, int Hkv, int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream) {
+  if (B < 0 || H < 0 || Hkv < 0 || total < 0 || max_seqlen < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || total == 0) return FA_OK;  // no token: nothing to compute
+  if (max_seqlen == 0 || max_seqlen > total) return FA_ERR_SHAPE;
+  if (Hkv == 0 || H % Hkv != 0) return FA_ERR_SHAPE;
+  if ((long long)B * H > kMaxHeads || total > kMaxN) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return FA_ERR_ALIGN;
+  const size_t tq = (size_t)total * H * d * 2, tk = (size_t)total * Hkv * d * 2, tl = (size_t)total * H * 4;
+  const size_t tc = (size_t)(B + 1) * sizeof(int);
+  const void* in[] = {q, k, v, cu_seqlens};
+  const size_t nin[] = {tq, tk, tk, tc};
+  for (int j = 0; j < 4; ++j)
+    if (overlaps(o, tq, in[j], nin[j]) || overlaps(lse, tl, in[j], nin[j])) return FA_ERR_ALIAS;
+  if (overlaps(o, tq, lse, tl)) return FA_ERR_ALIAS;
+  const hipError_t e = fa::launch_fwd_varlen_bf16(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d,
+                                                  causal != 0, scale, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,6 +160,11 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse, const int* kv_len, int B, int H,
                 int H_kv, int N, int d, int causal, float scale, hipStream_t stream) {
   return run_bf16(q, k, v, o, lse, kv_len, true, B, H, H_kv, N, d, causal, scale, stream);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens, int B,
+                  int H, int H_kv, int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream) {
+  return run_varlen(q, k, v, o, lse, cu_seqlens, B, H, H_kv, total, max_seqlen, d, causal, scale, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
@@ -193,13 +223,14 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 const char* fa_strerror(int code) {
   switch (code) {
     case FA_OK: return "success";
-    case FA_ERR_NULL: return "a tensor, lse, kv_len or workspace pointer is NULL";
+    case FA_ERR_NULL: return "a tensor, lse, kv_len, cu_seqlens or workspace pointer is NULL";
     case FA_ERR_SHAPE:
       return "bad shape: B, H, N must be >= 0, B*H <= 65535, N <= 2^30, H_kv >= 1 dividing H "
-             "(fp8: N a multiple of 16, at most 2^24)";
+             "(fp8: N a multiple of 16, at most 2^24; packed: 1 <= max_seqlen <= total <= 2^30)";
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
     case FA_ERR_ALIGN:
-      return "misaligned pointer: tensors and the workspace need 16-byte alignment, lse and kv_len 4-byte";
+      return "misaligned pointer: tensors and the workspace need 16-byte alignment, lse, kv_len and cu_seqlens "
+             "4-byte";
     case FA_ERR_ARG: return "bad argument: scales must be finite and > 0, causal must be 0 or 1";
     case FA_ERR_ALIAS: return "an output (o, lse, dq, dk, dv, workspace) overlaps an input or another output";
     case FA_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";

@@ -39,6 +39,11 @@
 //   * Key padding (a per-batch count Nk of valid keys, triton-transformer README usage example "ex. BERT"):
 //     tiles past Nk are not visited and keys >= Nk are masked like the sequence end; a row with no visible key
 //     gets o = 0 and lse = -inf.
+//   * Packed variable-length batches (VARLEN): q, o [T, H, d] and k, v [T, Hkv, d] hold B sequences back to back,
+//     sequence b being tokens cu[b] .. cu[b+1]-1; each is its own attention problem. Rows of one head are then
+//     H*d (or Hkv*d) elements apart instead of d; the copies and loads take that pitch, and a tile's copy range
+//     ends with the sequence's last row, so rows past it arrive as zeros exactly as past N. Query blocks past
+//     the sequence's end return at once. lse is [H, T].
 // The fp32 kernel keeps the same decomposition on v_mfma_f32_32x32x2f32 with a simple single-buffered loop.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -88,11 +93,11 @@ constexpr float kRescaleLog2 = 8.f;
 // bf16 kernel: NW waves x 32 query rows per workgroup, K/V tiles of KT x 64 keys (each 64-key part is one
 // swizzled Tile in LDS), ST-stage ring holding K and V of the same tile; every wave runs S_j, softmax,
 // O += P_j V_j.
-template <int D, bool CAUSAL, int NW, int ST, int KT>
+template <int D, bool CAUSAL, int NW, int ST, int KT, bool VARLEN>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale, int H, int group,
-    const int* __restrict__ kv_len) {
+    const int* __restrict__ kv_len, const int* __restrict__ cu_seqlens, int T_total) {
   using T = Tile<D>;
   constexpr int kThr = 64 * NW;
   constexpr int kBrW = NW * kRowsPerWave;        // query rows per workgroup
@@ -119,30 +124,46 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   int bh, qb;
   map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
 
-  const size_t head_off = (size_t)bh * (size_t)N * D;
-  const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;  // key/value head of this query head
+  // Packed sequences: this head's sequence starts at token `start` and has Ns tokens (offsets clamped to
+  // [0, T_total], so a malformed offset array cannot send an access outside the tensors); otherwise Ns = N.
+  int start = 0, Ns = N;
+  if constexpr (VARLEN) {
+    const int lo = min(max(cu_seqlens[bh / H], 0), T_total);
+    const int hi = min(max(cu_seqlens[bh / H + 1], lo), T_total);
+    start = __builtin_amdgcn_readfirstlane(lo);
+    Ns = __builtin_amdgcn_readfirstlane(hi - lo);
+  }
+  const int q_lo = qb * kBrW;
+  if (VARLEN && q_lo >= Ns) return;  // the whole workgroup: its query block lies past this sequence
+  const int hq = bh % H;
+  const int qpitch = VARLEN ? H * D : D;              // elements between consecutive rows of q and o
+  const int kpitch = VARLEN ? (H / group) * D : D;    // ... of k and v
+  const int kpitch_b = 2 * kpitch;
+  const size_t head_off = VARLEN ? ((size_t)start * H + hq) * D : (size_t)bh * (size_t)N * D;
+  const size_t kv_off = VARLEN ? ((size_t)start * (H / group) + hq / group) * D
+                               : (size_t)(bh / group) * (size_t)N * D;  // key/value head of this query head
+  const size_t lse_off = VARLEN ? (size_t)hq * T_total + start : (size_t)bh * N;
   const __bf16* qh = q + head_off;
   const __bf16* kh = k + kv_off;
   const __bf16* vh = v + kv_off;
   // valid keys of this batch (key-padding mask), clamped to [0, N]
-  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bh / H], 0), N)) : N;
+  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bh / H], 0), N)) : Ns;
 
-  const int q_lo = qb * kBrW;
-  const int q_last = min(q_lo + kBrW, N) - 1;              // last real query row of the workgroup
+  const int q_last = min(q_lo + kBrW, Ns) - 1;             // last real query row of the workgroup
   const int key_tiles = (Nk + kBcT - 1) / kBcT;             // tiles holding valid keys
   const int n_tiles = CAUSAL ? min(q_last / kBcT + 1, key_tiles) : key_tiles;
   const int q0w = q_lo + wave * kRowsPerWave;               // first query row of this wave
   const int my_q = q0w + l32;                               // query row of this lane
   // Tiles j < wave_tiles hold at least one key visible to this wave's rows.
   const int wave_tiles =
-      (q0w >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kRowsPerWave - 1) / kBcT + 1) : n_tiles);
+      (q0w >= Ns) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kRowsPerWave - 1) / kBcT + 1) : n_tiles);
 
   // ---- Q fragments: lane holds q[my_q][16*kb + 8*h .. +7] (B operand of S^T = K Q^T)
   bf16x8 qf[kDB];
 #pragma unroll
   for (int kb = 0; kb < kDB; ++kb) {
-    if (my_q < N) {
-      qf[kb] = *(const bf16x8*)(qh + (size_t)my_q * D + 16 * kb + 8 * h);
+    if (my_q < Ns) {
+      qf[kb] = *(const bf16x8*)(qh + (size_t)my_q * qpitch + 16 * kb + 8 * h);
     } else {
       qf[kb] = (bf16x8){};
     }
@@ -155,8 +176,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int p = 0; p < kCopies; ++p) {
     const int pos = (wave + NW * p) * 64 + lane;
     const int row = pos / T::CPR, phys = pos % T::CPR;
-    dma_k[p] = row * T::RB + (phys ^ T::swz_k(row)) * 16;
-    dma_v[p] = row * T::RB + (phys ^ T::swz_v(row)) * 16;
+    dma_k[p] = row * kpitch_b + (phys ^ T::swz_k(row)) * 16;
+    dma_v[p] = row * kpitch_b + (phys ^ T::swz_v(row)) * 16;
   }
   // Copy tile j of K (or V) into the stage starting `at` bytes into the K (or V) ring.
   auto copy_part = [&](const __bf16* src, lds_char* ring, int j, int at, const int(&dma)[kCopies])
@@ -164,11 +185,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       const int row0 = j * kBcT + t * kBc;
-      // rows past Nk arrive as zeros. (The clamp would compile to a vector instruction; readfirstlane keeps the
-      // descriptor in scalar registers, otherwise every copy is wrapped in a loop over distinct descriptors.)
-      const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(Nk - row0, kBc)) * T::RB);
+      // rows past Nk arrive as zeros: the range ends with the last valid row (rows are kpitch_b >= RB bytes
+      // apart). (The clamp would compile to a vector instruction; readfirstlane keeps the descriptor in scalar
+      // registers, otherwise every copy is wrapped in a loop over distinct descriptors.)
+      const int rows = max(0, min(Nk - row0, kBc));
+      const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * kpitch_b + T::RB : 0);
       const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Nk - 1));
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * D, bytes);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * kpitch, bytes);
 #pragma unroll
       for (int p = 0; p < kCopies; ++p)
         lds_copy16_inline(r, ring + at + t * T::kBytes + (wave + NW * p) * 1024, dma[p]);
@@ -347,9 +370,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // ---- epilogue: o = acc / l once per row, lse = m*scale + ln l. l >= 1 whenever a key is visible (the weight
   // of the maximum is >= 1); l == 0 only for a row without visible keys: o = 0, lse = -inf.
   const float l_tot = pair_sum32(l_run);
-  if (my_q < N) {
+  if (my_q < Ns) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* orow = o + head_off + (size_t)my_q * D;
+    __bf16* orow = o + head_off + (size_t)my_q * qpitch;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
 #pragma unroll
@@ -361,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
     if (h == 0)
-      lse[(size_t)bh * N + my_q] = l_tot > 0.f ? (m_ref * c2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      lse[lse_off + my_q] = l_tot > 0.f ? (m_ref * c2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -513,17 +536,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(const float* __res
 // ------------------------------------------------------------------------------------------------------------
 // launchers (arguments already validated by the C ABI layer)
 // ------------------------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, int NW, int ST, int KT>
+template <int D, bool CAUSAL, int NW, int ST, int KT, bool VARLEN = false>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                              float scale, int H, int group, const int* kv_len, hipStream_t stream) {
+                              float scale, int H, int group, const int* kv_len, hipStream_t stream,
+                              const int* cu_seqlens = nullptr, int T_total = 0) {
   constexpr int lds = 2 * ST * KT * Tile<D>::kBytes;
   constexpr int rows = NW * kRowsPerWave;
-  auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST, KT>;
+  auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST, KT, VARLEN>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)BH);
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, (const __bf16*)q, (const __bf16*)k,
-                     (const __bf16*)v, (__bf16*)o, lse, N, BH, scale, H, group, kv_len);
+                     (const __bf16*)v, (__bf16*)o, lse, N, BH, scale, H, group, kv_len, cu_seqlens, T_total);
   return hipGetLastError();
 }
 
@@ -551,6 +575,22 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   const int BH = B * H, group = H / Hkv;
   const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
 #define FA_LAUNCH(D, C, NW, KT) launch_bf16<D, C, NW, 2, KT>(q, k, v, o, lse, BH, N, scale, H, group, kv_len, stream)
+  if (wide) {
+    if (d == 64) return causal ? FA_LAUNCH(64, true, 8, 2) : FA_LAUNCH(64, false, 8, 2);
+    return causal ? FA_LAUNCH(128, true, 8, 2) : FA_LAUNCH(128, false, 8, 2);
+  }
+  if (d == 64) return causal ? FA_LAUNCH(64, true, 4, 1) : FA_LAUNCH(64, false, 4, 1);
+  return causal ? FA_LAUNCH(128, true, 4, 1) : FA_LAUNCH(128, false, 4, 1);
+#undef FA_LAUNCH
+}
+
+hipError_t launch_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  const int* cu_seqlens, int B, int H, int Hkv, int T_total, int max_seqlen, int d,
+                                  bool causal, float scale, hipStream_t stream) {
+  const int BH = B * H, group = H / Hkv, N = max_seqlen;
+  const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
+#define FA_LAUNCH(D, C, NW, KT) \
+  launch_bf16<D, C, NW, 2, KT, true>(q, k, v, o, lse, BH, N, scale, H, group, nullptr, stream, cu_seqlens, T_total)
   if (wide) {
     if (d == 64) return causal ? FA_LAUNCH(64, true, 8, 2) : FA_LAUNCH(64, false, 8, 2);
     return causal ? FA_LAUNCH(128, true, 8, 2) : FA_LAUNCH(128, false, 8, 2);

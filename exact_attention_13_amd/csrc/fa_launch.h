@@ -9,6 +9,11 @@ namespace fa {
 // is NULL or B device int32 counts of valid keys (clamped to [0, N] by the kernel).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                            int N, int d, bool causal, float scale, const int* kv_len, hipStream_t stream);
+// Packed variable-length batches: q, o [T, H, d], k, v [T, Hkv, d], lse [H, T]; sequence b is tokens
+// cu_seqlens[b] .. cu_seqlens[b+1]-1 (device int32, B+1 entries), none longer than max_seqlen >= 1.
+hipError_t launch_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  const int* cu_seqlens, int B, int H, int Hkv, int T_total, int max_seqlen, int d,
+                                  bool causal, float scale, hipStream_t stream);
 // fp8 (float8_e4m3fn) q, k [B*H, N, d] and v^T [B*H, d, N] with per-tensor scales; bf16 o. N % 16 == 0.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, float q_scale, float k_scale, float v_scale, hipStream_t stream);

@@ -105,6 +105,34 @@ int fa_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse
                 int H_kv, int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
+ * fa_fwd_varlen -- the forward over packed variable-length batches: B
+ * sequences of different lengths stored back to back without padding (the
+ * variable-length batches with per-batch lengths that go with the key-padding
+ * mask of the triton-transformer README's usage example; packing is a reading).
+ * Every sequence is its own attention problem: its queries see only its own
+ * keys (causal: those at or before their own position in the sequence).
+ *   q, o       : bf16 [total, H, d] (device; o written): token t, head h at
+ *                (t*H + h)*d
+ *   k, v       : const bf16 [total, H_kv, d] (device); H_kv divides H, query
+ *                head h reads key/value head h / (H / H_kv)
+ *   lse        : float [H, total] (device, written), element (h, t) at h*total + t
+ *   cu_seqlens : const int32 [B+1] (device): sequence b is tokens
+ *                cu_seqlens[b] .. cu_seqlens[b+1]-1; it must rise from 0 to
+ *                total. The kernel clamps every offset to [0, total], so a
+ *                malformed array cannot make it read or write outside the
+ *                tensors (the results are then meaningless).
+ *   max_seqlen : at least the longest sequence, at most total (it sizes the
+ *                grid; rows of a longer sequence past max_seqlen are not written)
+ * An empty sequence writes nothing. B, H or total = 0 is an empty problem;
+ * max_seqlen = 0 or above total with tokens present is FA_ERR_SHAPE; cu_seqlens
+ * NULL is FA_ERR_NULL, not 4-byte aligned FA_ERR_ALIGN; o and lse must not
+ * overlap the inputs, cu_seqlens or each other (FA_ERR_ALIAS). The rest
+ * (numerics, ownership, errors) as fa_fwd.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens, int B,
+                  int H, int H_kv, int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream);
+
+/*
  * fa_bwd -- gradients of fa_fwd / fa_fwd_gqa (bf16 tensors, fp32 arithmetic).
  * The pages name a faster backward pass that recomputes attention from stored
  * statistics instead of storing the attention matrix (unite.ai page, the key

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 10400
+    assert fa.fa_version() == 10500
     for code in range(8):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
@@ -163,6 +163,25 @@ def test_backward_kpad_error_codes():
     assert _bwd_kpad(d=80) == fa.FA_ERR_HEADDIM
     assert _bwd_kpad(causal=2) == fa.FA_ERR_ARG
     assert _bwd_kpad(N=0, kv_len=0, **{name: 0 for name in BWD}) == fa.FA_OK
+
+
+def test_varlen_error_codes():
+    def vl(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, cu=A + 0x5000000, B=2, H=4,
+           Hkv=2, total=100, max_seqlen=60, d=64, causal=0, scale=0.125):
+        return fa.fa_fwd_varlen(q, k, v, o, lse, cu, B, H, Hkv, total, max_seqlen, d, causal, scale, 0)
+    for name in ("q", "k", "v", "o", "lse", "cu"):
+        assert vl(**{name: 0}) == fa.FA_ERR_NULL, name
+    assert vl(cu=A + 0x5000000 + 2) == fa.FA_ERR_ALIGN
+    assert vl(lse=A + 0x4000000 + 2) == fa.FA_ERR_ALIGN
+    assert vl(o=A + 0x3000000 + 8) == fa.FA_ERR_ALIGN
+    assert vl(max_seqlen=0) == fa.FA_ERR_SHAPE and vl(max_seqlen=101) == fa.FA_ERR_SHAPE
+    assert vl(Hkv=3) == fa.FA_ERR_SHAPE and vl(total=-1) == fa.FA_ERR_SHAPE
+    assert vl(d=96) == fa.FA_ERR_HEADDIM and vl(scale=float("nan")) == fa.FA_ERR_ARG
+    assert vl(lse=A + 0x3000000 + 1024) == fa.FA_ERR_ALIAS        # lse inside o (100*4*64*2 bytes)
+    assert vl(o=A + 0x5000000) == fa.FA_ERR_ALIAS and vl(lse=A + 0x4000000, cu=A + 0x4000000 + 64) == fa.FA_ERR_ALIAS
+    assert vl(o=A + 0x1000000 + 16) == fa.FA_ERR_ALIAS            # o inside k
+    assert vl(total=0, q=0, k=0, v=0, o=0, lse=0, cu=0) == fa.FA_OK  # no token: nothing to do
+    assert vl(B=0, q=0, cu=0) == fa.FA_OK
 
 
 def test_fp8_error_codes():

@@ -1,0 +1,116 @@
+"""Parity of the packed variable-length forward (fa_fwd_varlen, through the C ABI) with the fp64 oracle.
+
+Same bar as the plain forward: max |o_gpu - o_oracle| and max |lse_gpu - lse_oracle| <= 2e-2 over every checked
+element (bf16 inputs). Structural checks are bitwise: one packed sequence equals the [1, H, N, d] forward of the
+same data, and nothing outside o and lse is written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as ai
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_13_amd as fa_mod
+    return fa_mod
+
+
+def _run(fa, q, k, v, lens, causal, scale):
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda:0")
+    o, lse = fa.forward_varlen(q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0"), cu, max(max(lens), 1), causal=causal,
+                               scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _compare(label, o, lse, q, k, v, lens, causal, scale, rows=None):
+    T, H, d = q.shape
+    cu = [0] + list(np.cumsum(lens))
+    o_ref, lse_ref = oracle.attention_varlen(q, k, v, cu, causal, scale, rows=rows)
+    og = o.float().cpu().numpy().astype(np.float64).reshape(T * H, d)
+    lg = lse.cpu().numpy().astype(np.float64).T.reshape(T * H)  # [H, T] -> rows t*H + h
+    if rows is not None:
+        og, lg = og[rows], lg[rows]
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg)), label
+    eo = float(np.abs(og - o_ref).max()) if og.size else 0.0
+    el = float(np.abs(lg - lse_ref).max()) if lg.size else 0.0
+    print(f"[parity] {label} max|do|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= TOL, f"{label}: o error {eo}"
+    assert el <= TOL, f"{label}: lse error {el}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (4, 2), (4, 1)])
+@pytest.mark.parametrize("lens", [(1, 7, 63, 64, 65, 300, 0, 129), (1000,), (0, 257, 0, 5)])
+def test_varlen_ragged(fa, lens, H, Hkv, d, causal):
+    label = f"varlen lens={lens} H{H} Hkv{Hkv} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v = ai.make_qkv_varlen(lens, H, d, seed=800 + sum(lens), Hkv=Hkv)
+    scale = ai.default_scale(d)
+    o, lse = _run(fa, q, k, v, lens, causal, scale)
+    _compare(label, o, lse, q, k, v, lens, causal, scale)
+
+
+@pytest.mark.parametrize("name", sorted(ai.VARLEN_WORKLOADS))
+def test_varlen_workload_sampled_rows(fa, name):
+    w = ai.VARLEN_WORKLOADS[name]
+    print(f"[case] {name}", flush=True)
+    q, k, v = ai.make_qkv_varlen(w.lens, w.H, w.d, w.seed, Hkv=w.Hkv or None)
+    o, lse = _run(fa, q, k, v, w.lens, w.causal, w.scale)
+    cu = np.array(w.cu_seqlens)
+    g = torch.Generator("cpu").manual_seed(w.seed + 1000)
+    rnd = torch.randperm(w.T * w.H, generator=g)[: w.sampled_rows].numpy()
+    # every sequence's first and last token and the tokens around 128-row blocks, for the first and last head
+    toks = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, np.minimum(cu[:-1] + 127, cu[1:] - 1),
+                                     np.minimum(cu[:-1] + 128, cu[1:] - 1)]))
+    toks = toks[(toks >= 0) & (toks < w.T)]
+    edges = np.concatenate([toks * w.H, toks * w.H + w.H - 1])
+    rows = np.unique(np.concatenate([rnd, edges]))
+    _compare(name, o, lse, q, k, v, w.lens, w.causal, w.scale, rows=rows)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T,H,Hkv", [(333, 4, 4), (4096, 4, 2), (4096, 32, 8)])
+def test_one_packed_sequence_equals_the_padded_forward(fa, T, H, Hkv, causal):
+    """The same data as one [1, H, T, d] problem through fa_fwd_gqa gives the same bits (same tiles, same order;
+    the last shape takes the 8-wave workgroups, the others the 4-wave ones)."""
+    d = 128
+    q, k, v = ai.make_qkv_varlen((T,), H, d, seed=850, Hkv=Hkv)
+    o, lse = _run(fa, q, k, v, (T,), causal, ai.default_scale(d))
+    qp, kp, vp = (x.transpose(0, 1)[None].contiguous().to("cuda:0") for x in (q, k, v))
+    o2, l2 = fa.forward(qp, kp, vp, causal=causal, scale=ai.default_scale(d))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2[0].transpose(0, 1)) and torch.equal(lse, l2[0])
+
+
+def test_varlen_writes_nothing_outside_o_and_lse(fa):
+    lens = (5, 0, 130, 64)
+    H, Hkv, d = 4, 2, 64
+    T = sum(lens)
+    q, k, v = (x.to("cuda:0") for x in ai.make_qkv_varlen(lens, H, d, seed=860, Hkv=Hkv))
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda:0")
+    pad = 4096
+    n_o, n_l = T * H * d, T * H
+    ob = torch.full((n_o + 2 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda:0")
+    lb = torch.full((n_l + 2 * pad,), 777.0, dtype=torch.float32, device="cuda:0")
+    o, lse = ob[pad: pad + n_o], lb[pad: pad + n_l]
+    rc = fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu.data_ptr(),
+                          len(lens), H, Hkv, T, max(lens), d, 1, ai.default_scale(d),
+                          torch.cuda.current_stream().cuda_stream)
+    assert rc == fa.FA_OK
+    torch.cuda.synchronize()
+    assert torch.all(ob[:pad] == 1234.0) and torch.all(ob[pad + n_o:] == 1234.0)
+    assert torch.all(lb[:pad] == 777.0) and torch.all(lb[pad + n_l:] == 777.0)
+    ref = fa.forward_varlen(q, k, v, cu, max(lens), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(T, H, d), ref[0]) and torch.equal(lse.view(H, T), ref[1])
