@@ -10,8 +10,8 @@ sample of the same workload on this host's cores.
 
 The line also carries `backward`: the gradient call fa_bwd (dq, then dk and dv) on the headline workload and on
 the long causal one, timed the same way, in the usual FLOP convention 2.5 x the forward's (five matrix products:
-the recomputed QK^T, dO V^T, dV, dQ, dK); and `fp8`: fa_fwd_fp8 on the same two shapes with the inputs quantized
-per tensor to float8_e4m3fn, against the fp8 peak.
+the recomputed QK^T, dO V^T, dV, dQ, dK); `fp8`: fa_fwd_fp8 on the same two shapes with the inputs quantized
+per tensor to float8_e4m3fn, against the fp8 peak; and `varlen`: fa_fwd_varlen on the packed workloads.
 
     --bwd-only          time only the gradient call of --workload (one JSON line; for profiling)
 
@@ -99,6 +99,11 @@ FP8_PROFILE_COMMANDS = {
           "SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
           "-d gpurun_out/prof_fp8_{w}_sq -o run -- python bench.py --workload {w} --fp8-pmc-pass",
 }
+
+
+# Kernel trace of the packed variable-length forward ({w} = packed workload name).
+VARLEN_PROFILE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{w}_trace -o run -- "
+                          "python bench.py --varlen-only {w} --steps 50 --warmup 10")
 
 
 def kernel_src_hash(srcs=KERNEL_SRCS) -> str:
@@ -273,6 +278,50 @@ def fp8_record(w, steps: int, warmup: int):
             "flops_per_launch": w.flops, "kernel": "fa_fwd_fp8_kernel",
             "traffic": traffic_from_profiles(w, "fp8_", FP8_SRCS),
             "kernel_src_sha256_16": kernel_src_hash(FP8_SRCS)}
+
+
+def varlen_record(w, steps: int, warmup: int):
+    """fa_fwd_varlen on a packed variable-length workload (inputs resident on the device)."""
+    import torch
+
+    import attn_inputs as ai
+    import exact_attention_13_amd as fa
+
+    q, k, v = (x.cuda() for x in ai.make_qkv_varlen(w.lens, w.H, w.d, w.seed, Hkv=w.Hkv or None))
+    cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.H, w.T), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu.data_ptr(), w.B, w.H, w.Hk,
+            w.T, w.max_len, w.d, int(w.causal), w.scale, stream.cuda_stream)
+
+    def call():
+        rc = fa.fa_fwd_varlen(*args)
+        if rc != 0:
+            raise RuntimeError(f"fa_fwd_varlen failed: {fa.fa_strerror(rc)}")
+    for _ in range(warmup):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    mean = statistics.fmean(durs)
+    return {"workload": w.name, "lens": list(w.lens), "H": w.H, "H_kv": w.Hk, "d": w.d, "causal": w.causal,
+            "tflops": round(w.flops * steps / wall / 1e12, 2),
+            "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
+                          "min": round(min(durs), 4)},
+            "roofline": {"bound": "mfma", "achieved": round(w.flops / (mean * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(w.flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "flops_per_launch": w.flops, "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+            "kernel": "fa_fwd_bf16_kernel (VARLEN)", "kernel_src_sha256_16": kernel_src_hash()}
 
 
 def traffic_from_profiles(w, prefix="", srcs=KERNEL_SRCS):
@@ -597,6 +646,36 @@ LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active,
     print(md)
 
 
+def write_profiles_varlen(w):
+    """Summary of VARLEN_PROFILE_COMMAND's output: profiles/<packed workload>_rocprof.md."""
+    trace = [r for r in _stats(f"gpurun_out/prof_{w.name}_trace") if "fa_fwd_bf16_kernel" in r["Name"]]
+    if not trace:
+        raise RuntimeError("no kernel statistics for the attention kernel")
+    t = trace[0]
+    avg_us = float(t["AverageNs"]) / 1e3
+    tf = w.flops / (avg_us * 1e-6) / 1e12
+    md = f"""# rocprofv3 summary: fa_fwd_varlen on {w.name}
+
+Kernel source sha256[:16]: `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip and fa_gfx950.h).
+Workload: {w.B} packed sequences of lengths {list(w.lens)} (total {w.T} tokens), H={w.H} H_kv={w.Hk} d={w.d}
+causal={w.causal} bf16; {w.flops:.4g} FLOP per launch (4*H*d per visible query-key pair of every sequence, causal
+triangles counted as L^2/2), {w.algorithmic_bytes} algorithmic HBM bytes per launch.
+
+Command (run from the repository root; summarised by `python bench.py --write-profiles-varlen {w.name}`):
+
+    {VARLEN_PROFILE_COMMAND.format(w=w.name)}
+
+| kernel | calls | avg us | min us | max us |
+|---|---|---|---|---|
+| {t['Name'][:100]} | {t['Calls']} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
+
+Attention TFLOP/s at the traced average: {tf:.1f} ({100 * tf / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
+"""
+    PROFILES.mkdir(exist_ok=True)
+    (PROFILES / f"{w.name}_rocprof.md").write_text(md)
+    print(md)
+
+
 def write_profiles_bwd(w):
     """Summary of the BWD_PROFILE_COMMANDS outputs: profiles/bwd_<workload>_rocprof.md (both gradient kernels)."""
     dirs = {k: f"gpurun_out/prof_bwd_{w.name}_{k}" for k in BWD_PROFILE_COMMANDS}
@@ -683,6 +762,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--fp8-only", action="store_true", help="time only fa_fwd_fp8 on --workload's shape")
     ap.add_argument("--fp8-pmc-pass", action="store_true")
+    ap.add_argument("--varlen-only", metavar="WORKLOAD", choices=sorted(ai.VARLEN_WORKLOADS),
+                    help="time only fa_fwd_varlen on a packed workload")
+    ap.add_argument("--write-profiles-varlen", metavar="WORKLOAD", choices=sorted(ai.VARLEN_WORKLOADS))
     ap.add_argument("--write-profiles-fp8", action="store_true")
     args = ap.parse_args()
 
@@ -694,6 +776,9 @@ def main():
         return 0
     if args.write_profiles_bwd:
         write_profiles_bwd(ai.WORKLOADS[args.workload])
+        return 0
+    if args.write_profiles_varlen:
+        write_profiles_varlen(ai.VARLEN_WORKLOADS[args.write_profiles_varlen])
         return 0
     if args.write_profiles_fp8:
         write_profiles_fp8(ai.WORKLOADS[args.workload])
@@ -714,6 +799,9 @@ def main():
     w = ai.WORKLOADS[args.workload]
     if args.pmc_pass:
         pmc_pass(w, reps=5)
+        return 0
+    if args.varlen_only:
+        print(json.dumps(varlen_record(ai.VARLEN_WORKLOADS[args.varlen_only], args.steps, args.warmup)), flush=True)
         return 0
     if args.fp8_only:
         print(json.dumps(fp8_record(w, args.steps, args.warmup)), flush=True)
@@ -765,6 +853,7 @@ def main():
     if not args.no_backward:
         line["backward"] = [backward_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in BWD_WORKLOADS]
         line["fp8"] = [fp8_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in FP8_WORKLOADS]
+        line["varlen"] = [varlen_record(vw, steps=20, warmup=3) for vw in ai.VARLEN_WORKLOADS.values()]
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_rows)
         cb.pop("seconds")
