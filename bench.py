@@ -119,7 +119,7 @@ def kernel_name(w) -> str:
     if w.dtype != "bf16":
         return f"fa_fwd_f32_kernel<{w.d}, {c}>"
     wide = ((w.N + 255) // 256) * w.B * w.H >= 512
-    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {'8, 2, 2' if wide else '4, 2, 1'}>"
+    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {'8, 2, 2' if wide else '4, 2, 1'}, false>"
 
 
 def _device_inputs(w):
