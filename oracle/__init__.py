@@ -229,6 +229,29 @@ def attention_bwd(q, k, v, dout, causal: bool, scale: float, threads: int | None
     return dq.reshape(B, H, N, d), dk.reshape(B, Hkv, N, d), dv.reshape(B, Hkv, N, d)
 
 
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens, causal: bool, scale: float, threads: int | None = None):
+    """Gradients of attention_varlen for an upstream gradient dout [T, H, d] of o: every sequence's gradients are
+    those of its own attention problem (attention_bwd on its [1, H, L, d] slice); sequences share nothing.
+    Returns (dq [T, H, d], dk [T, Hkv, d], dv [T, Hkv, d]) as float64 arrays."""
+    qa, ka, va, da = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    if qa.ndim != 3 or da.shape != qa.shape or ka.shape != va.shape or ka.ndim != 3 or ka.shape[0] != qa.shape[0] \
+            or ka.shape[2] != qa.shape[2] or qa.shape[1] % ka.shape[1] != 0:
+        raise ValueError(f"q, dout [T,H,d] and k, v [T,Hkv,d] disagree: {qa.shape} {ka.shape} {da.shape}")
+    T = qa.shape[0]
+    cu = np.asarray(cu_seqlens, dtype=np.int64).reshape(-1)
+    if cu.size < 1 or cu[0] != 0 or cu[-1] != T or (np.diff(cu) < 0).any():
+        raise ValueError(f"cu_seqlens must rise from 0 to {T}: {cu}")
+    dq, dk, dv = np.zeros(qa.shape), np.zeros(ka.shape), np.zeros(ka.shape)
+    for b in range(cu.size - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi == lo:
+            continue
+        per = lambda x: np.ascontiguousarray(x[lo:hi].transpose(1, 0, 2)[None])  # [1, heads, L, d]
+        gq, gk, gv = attention_bwd(per(qa), per(ka), per(va), per(da), causal, scale, threads)
+        dq[lo:hi], dk[lo:hi], dv[lo:hi] = (g[0].transpose(1, 0, 2) for g in (gq, gk, gv))
+    return dq, dk, dv
+
+
 def attention_fp8_rows(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, causal: bool, scale: float,
                        rows=None, threads: int | None = None):
     """Attention of per-tensor-scaled fp8 inputs: the real inputs are q8 * q_scale, k8 * k_scale, v8 * v_scale.

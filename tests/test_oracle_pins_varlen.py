@@ -87,3 +87,24 @@ def test_row_lists_and_bad_offsets():
     for bad in ([1, 50], [0, 30, 20, 50], [0, 49]):
         with pytest.raises(ValueError):
             oracle.attention_varlen(q, k, v, bad, False, 0.2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 1)])
+def test_varlen_gradients_match_autograd_with_a_block_diagonal_mask(H, Hkv, causal):
+    """fp64 autograd of SDPA on the whole packed problem with the block-diagonal mask (every row of a non-empty
+    sequence sees at least its first key, so no row of the masked softmax is empty)."""
+    cu = np.array([0, 37, 38, 100, 100, 163])
+    T, d = int(cu[-1]), 64
+    q, k, v = _packed(T, H, Hkv, d, seed=41)
+    g = torch.Generator("cpu").manual_seed(42)
+    dout = torch.randn((T, H, d), generator=g).to(torch.bfloat16)
+    scale = ai.default_scale(d)
+    dq, dk, dv = oracle.attention_bwd_varlen(q, k, v, dout, cu, causal, scale)
+    keep = torch.from_numpy(_block_mask(cu, causal))
+    qd, kd, vd = (x.to(torch.float64).transpose(0, 1)[None].clone().requires_grad_() for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=keep, scale=float(np.float32(scale)),
+                                                         enable_gqa=(H != Hkv))
+    o.backward(dout.to(torch.float64).transpose(0, 1)[None])
+    for got, ref in ((dq, qd), (dk, kd), (dv, vd)):
+        np.testing.assert_allclose(got, ref.grad[0].transpose(0, 1).numpy(), rtol=0, atol=1e-12)
