@@ -183,3 +183,39 @@ def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_fwd_varlen failed ({rc}): {binding.fa_strerror(rc)}")
     return o, lse
+
+
+def backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                    dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                    scale: float | None = None, stream: int | None = None):
+    """Gradients (dq, dk, dv) of forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal, scale) -> (o, lse) for an
+    upstream gradient dout [total, H, d] of o. Allocates the outputs and the workspace with torch."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3 \
+                or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 3-d GPU tensor")
+    total, H, d = q.shape
+    if o.shape != q.shape or dout.shape != q.shape or k.shape != v.shape or k.shape[0] != total \
+            or k.shape[2] != d or H % k.shape[1] != 0:
+        raise ValueError("q, o, dout [total,H,d] and k, v [total,H_kv,d] disagree")
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [H, total] tensor on q's device")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or not cu_seqlens.is_contiguous() or cu_seqlens.device != q.device):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    B = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((max(binding.fa_bwd_workspace_bytes(B, H, int(max_seqlen)), 16),), dtype=torch.uint8,
+                     device=q.device)
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        rc = binding.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                   cu_seqlens.data_ptr(), B, H, k.shape[1], total, int(max_seqlen), d,
+                                   int(bool(causal)), float(scale), int(stream))
+    if rc != binding.FA_OK:
+        raise RuntimeError(f"fa_bwd_varlen failed ({rc}): {binding.fa_strerror(rc)}")
+    return dq, dk, dv

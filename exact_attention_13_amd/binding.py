@@ -26,7 +26,7 @@ FA_ERR_ALIAS = 6
 FA_ERR_HIP = 7
 
 EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_kpad",
-           "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_strerror", "fa_version")
+           "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_attention_13_amd/build.py` "
@@ -49,6 +49,8 @@ _lib.fa_bwd.restype = _I
 _lib.fa_bwd.argtypes = [_P] * 10 + [_I] * 6 + [ctypes.c_float, _P]
 _lib.fa_bwd_kpad.restype = _I
 _lib.fa_bwd_kpad.argtypes = [_P] * 11 + [_I] * 6 + [ctypes.c_float, _P]
+_lib.fa_bwd_varlen.restype = _I
+_lib.fa_bwd_varlen.argtypes = [_P] * 11 + [_I] * 7 + [ctypes.c_float, _P]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.fa_fwd_f32.restype = _I
@@ -106,6 +108,14 @@ def fa_bwd_kpad(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk
     """Raw entry point: fa_bwd for a forward made with fa_fwd_kpad; kv_len is the same device int32 [B] array."""
     return _lib.fa_bwd_kpad(q, k, v, o, lse, dout, dq, dk, dv, workspace, kv_len, B, H, H_kv, N, d, causal, scale,
                             stream)
+
+
+def fa_bwd_varlen(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, workspace: int,
+                  cu_seqlens: int, B: int, H: int, H_kv: int, total: int, max_seqlen: int, d: int, causal: int,
+                  scale: float, stream: int) -> int:
+    """Raw entry point: gradients of fa_fwd_varlen; workspace of fa_bwd_workspace_bytes(B, H, max_seqlen) bytes."""
+    return _lib.fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, B, H, H_kv, total,
+                              max_seqlen, d, causal, scale, stream)
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:

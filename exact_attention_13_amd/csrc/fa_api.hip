@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 10500;  // 1.5.0
+constexpr int kVersion = 10600;  // 1.6.0
 constexpr long long kMaxHeads = 65535;   // B*H is the grid's y extent
 constexpr long long kMaxN = 1LL << 30;
 
@@ -143,6 +143,41 @@ int run_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens, int B, int H, int Hkv,
+                   int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream) {
+  if (B < 0 || H < 0 || Hkv < 0 || total < 0 || max_seqlen < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || total == 0) return FA_OK;
+  if (max_seqlen == 0 || max_seqlen > total) return FA_ERR_SHAPE;
+  if (Hkv == 0 || H % Hkv != 0) return FA_ERR_SHAPE;
+  if ((long long)B * H > kMaxHeads || total > kMaxN) return FA_ERR_SHAPE;
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+  for (const void* x : ptrs) {
+    if (!x) return FA_ERR_NULL;
+    if ((uintptr_t)x & 15) return FA_ERR_ALIGN;
+  }
+  if (!lse || !cu_seqlens) return FA_ERR_NULL;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return FA_ERR_ALIGN;
+  const size_t tq = (size_t)total * H * d * 2, tk = (size_t)total * Hkv * d * 2, tl = (size_t)total * H * 4;
+  const size_t tw = fa::bwd_workspace_bytes(B, H, max_seqlen), tc = (size_t)(B + 1) * sizeof(int);
+  const void* rin[] = {q, k, v, o, dout, lse, cu_seqlens};
+  const size_t nin[] = {tq, tk, tk, tq, tq, tl, tc};
+  void* rout[] = {dq, dk, dv, workspace};
+  const size_t nout[] = {tq, tk, tk, tw};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(rout[i], nout[i], rin[j], nin[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(rout[i], nout[i], rout[j], nout[j])) return FA_ERR_ALIAS;
+  }
+  const hipError_t e = fa::launch_bwd_varlen_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, B, H,
+                                                  Hkv, total, max_seqlen, d, causal != 0, scale, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +214,13 @@ int fa_bwd_kpad(const void* q, const void* k, const void* v, const void* o, cons
                 int causal, float scale, hipStream_t stream) {
   return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, kv_len, true, B, H, H_kv, N, d, causal, scale,
                  stream);
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens, int B, int H, int H_kv,
+                  int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream) {
+  return run_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, B, H, H_kv, total, max_seqlen, d,
+                        causal, scale, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {

@@ -27,6 +27,11 @@
 // the dq kernel visits only the key tiles below Nk and masks keys >= Nk like the sequence end; the dk/dv kernel
 // masks them, loads no k or v row past Nk and writes zero gradients for them. With Nk = 0 no tile is visited
 // (o = 0, lse = -inf there), so every gradient of the batch is 0.
+// Packed variable-length batches (VARLEN, the layout of the packed forward: q, o, dO, dq [T, H, d], k, v, dk, dv
+// [T, Hkv, d], lse [H, T], sequence b = tokens cu[b] .. cu[b+1]-1, offsets clamped to [0, T]): rows of a head are
+// H*d (Hkv*d) elements apart, every copy range ends with the sequence's last row, and workgroups whose query or
+// key block lies past their sequence return at once, so no row of another sequence is read or written. The
+// workspace keeps its layout, with N = max_seqlen as the per-head stride.
 // S and dP are computed in both kernels (7 matrix products instead of the 5 of a single pass with atomic dq
 // updates): the price of determinism.
 //
@@ -95,12 +100,12 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
 // ------------------------------------------------------------------------------------------------------------
 // dq (and the workspace pairs D_i, lse_i*log2e)
 // ------------------------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ o, const float* __restrict__ lse, const __bf16* __restrict__ dout,
     __bf16* __restrict__ dq, float* __restrict__ ws, int N, int BH, float scale, int group, int H,
-    const int* __restrict__ kv_len) {
+    const int* __restrict__ kv_len, const int* __restrict__ cu_seqlens, int T_total) {
   using T = BwdTile<D>;
   constexpr int NW = kBwdWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
@@ -113,28 +118,41 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int nq = gridDim.x;
   int bh, qb;
   map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
-  const size_t head_off = (size_t)bh * (size_t)N * D;
-  const size_t kv_off = (size_t)(bh / group) * (size_t)N * D;
+  int start = 0, Ns = N;  // this head's sequence: its first token and length
+  if constexpr (VARLEN) {
+    const int lo = min(max(cu_seqlens[bh / H], 0), T_total);
+    const int hi = min(max(cu_seqlens[bh / H + 1], lo), T_total);
+    start = __builtin_amdgcn_readfirstlane(lo);
+    Ns = __builtin_amdgcn_readfirstlane(min(hi - lo, N));  // no longer than max_seqlen (= N)
+  }
+  const int q_lo = qb * kBwdBlock;
+  if (VARLEN && q_lo >= Ns) return;  // the whole workgroup: no row of this block (nor its padding) exists
+  const int hq = bh % H, Hkv = H / group;
+  const int qpitch = VARLEN ? H * D : D;   // elements between consecutive rows of q, o, dO and dq
+  const int kpitch = VARLEN ? Hkv * D : D;  // ... of k and v
+  const int kpitch_b = 2 * kpitch;
+  const size_t head_off = VARLEN ? ((size_t)start * H + hq) * D : (size_t)bh * (size_t)N * D;
+  const size_t kv_off = VARLEN ? ((size_t)start * Hkv + hq / group) * D : (size_t)(bh / group) * (size_t)N * D;
+  const size_t lse_off = VARLEN ? (size_t)hq * T_total + start : (size_t)bh * N;
   const __bf16* kh = k + kv_off;
   const __bf16* vh = v + kv_off;
-  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bh / H], 0), N)) : N;
+  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bh / H], 0), N)) : Ns;
 
-  const int q_lo = qb * kBwdBlock;
-  const int q_last = min(q_lo + kBwdBlock, N) - 1;
+  const int q_last = min(q_lo + kBwdBlock, Ns) - 1;
   const int key_tiles = (Nk + kBwdTile - 1) / kBwdTile;
   const int n_tiles = CAUSAL ? min(q_last / kBwdTile + 1, key_tiles) : key_tiles;
   const int q0w = q_lo + wave * kBwdRows;
   const int my_q = q0w + l32;
   const int wave_tiles =
-      (q0w >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kBwdRows - 1) / kBwdTile + 1) : n_tiles);
+      (q0w >= Ns) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kBwdRows - 1) / kBwdTile + 1) : n_tiles);
 
   // This lane's query row: q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T), and D_i = dO_i . o_i
   bf16x8 qf[kDB], df[kDB];
   float dpart = 0.f;
 #pragma unroll
   for (int kb = 0; kb < kDB; ++kb) {
-    if (my_q < N) {
-      const size_t e = head_off + (size_t)my_q * D + 16 * kb + 8 * h;
+    if (my_q < Ns) {
+      const size_t e = head_off + (size_t)my_q * qpitch + 16 * kb + 8 * h;
       qf[kb] = *(const bf16x8*)(q + e);
       df[kb] = *(const bf16x8*)(dout + e);
       dpart += dot8(df[kb], *(const bf16x8*)(o + e));
@@ -144,8 +162,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   }
   const float Di = pair_sum32(dpart);
-  // rows past N: lse2 = +inf makes every p of the row exactly 0 (D is 0 there: dO was not loaded)
-  const float lse2 = (my_q < N) ? lse[(size_t)bh * N + my_q] * kLog2e : INFINITY;
+  // rows past the sequence: lse2 = +inf makes every p of the row exactly 0 (D is 0 there: dO was not loaded)
+  const float lse2 = (my_q < Ns) ? lse[lse_off + my_q] * kLog2e : INFINITY;
   const int npad = ws_rows(N);
   if (my_q < npad && h == 0) {
     float2* w = (float2*)ws + (size_t)bh * npad + my_q;
@@ -158,15 +176,16 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int p = 0; p < kCopies; ++p) {
     const int pos = (wave + NW * p) * 64 + lane;
     const int row = pos / T::CPR, phys = pos % T::CPR;
-    dma[p] = row * T::RB + (phys ^ T::swz(row)) * 16;
+    dma[p] = row * kpitch_b + (phys ^ T::swz(row)) * 16;
   }
   auto copy_tile = [&](const __bf16* src, lds_char* dst, int j) __attribute__((always_inline)) {
     const int row0 = j * kBwdTile;
-    // rows past Nk arrive as zeros (only tiles below Nk are copied, so Nk >= 1 here); scalar byte count and base
-    // keep the descriptor in scalar registers
-    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(Nk - row0, kBwdTile)) * T::RB);
+    // rows past Nk arrive as zeros: the range ends with the last valid row (only tiles below Nk are copied, so
+    // Nk >= 1 here); scalar byte count and base keep the descriptor in scalar registers
+    const int rows = max(0, min(Nk - row0, kBwdTile));
+    const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * kpitch_b + T::RB : 0);
     const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Nk - 1));
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * D, bytes);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * kpitch, bytes);
 #pragma unroll
     for (int p = 0; p < kCopies; ++p) lds_copy16_inline(r, dst + (wave + NW * p) * 1024, dma[p]);
   };
@@ -286,8 +305,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // dq_i = scale * acc; acc[cb][4g + i] is column 32cb + 8g + 4h + i of row my_q
-  if (my_q < N) {
-    __bf16* row = dq + head_off + (size_t)my_q * D;
+  if (my_q < Ns) {
+    __bf16* row = dq + head_off + (size_t)my_q * qpitch;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
@@ -315,11 +334,12 @@ constexpr int kPSlotBytes = 2 * 64 * 16;  // p of one 32 x 32 sub-block, bf16, a
 // Waves w and w+4 run on the same SIMD and own the same 32 keys: the p wave (w < 4) computes S = Q K^T, p and
 // dV^T += dO^T P; the dS wave computes dP = dO V^T, then (after the sub-block's barrier) dS = p (dP - D) from the
 // p the other wave left in LDS, and dK^T += Q^T dS. Each holds half the accumulators, so two waves share a SIMD.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ ws, __bf16* __restrict__ dk,
-    __bf16* __restrict__ dv, int N, int BHkv, float scale, int group, int Hkv, const int* __restrict__ kv_len) {
+    __bf16* __restrict__ dv, int N, int BHkv, float scale, int group, int Hkv, const int* __restrict__ kv_len,
+    const int* __restrict__ cu_seqlens, int T_total) {
   using T = BwdTile<D, kDkdvTile>;
   constexpr int NW = kDkdvWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   constexpr int kSub = kDkdvTile / kBwdRows;  // 32-row sub-blocks per query tile
@@ -339,11 +359,23 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   map_workgroup(blockIdx.x + nk * blockIdx.y, nk, BHkv, 1, CAUSAL, bkv, t);
   // causal: the first key blocks see the most query rows; map_workgroup hands out the last index first
   const int kblk = CAUSAL ? nk - 1 - t : t;
-  const size_t kv_off = (size_t)bkv * (size_t)N * D;
-  const int bh0 = bkv * group;  // first query head of this key/value head's group
-  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bkv / Hkv], 0), N)) : N;
-
+  int start = 0, Ns = N;  // this head's sequence: its first token and length
+  if constexpr (VARLEN) {
+    const int lo = min(max(cu_seqlens[bkv / Hkv], 0), T_total);
+    const int hi = min(max(cu_seqlens[bkv / Hkv + 1], lo), T_total);
+    start = __builtin_amdgcn_readfirstlane(lo);
+    Ns = __builtin_amdgcn_readfirstlane(min(hi - lo, N));  // no longer than max_seqlen (= N)
+  }
   const int k0 = kblk * kBwdBlock;
+  if (VARLEN && k0 >= Ns) return;  // the whole workgroup: its keys lie past this sequence
+  const int H = Hkv * group;
+  const int qpitch = VARLEN ? H * D : D;   // elements between consecutive rows of q and dO
+  const int kpitch = VARLEN ? Hkv * D : D;  // ... of k, v, dk and dv
+  const int qpitch_b = 2 * qpitch;
+  const size_t kv_off = VARLEN ? ((size_t)start * Hkv + bkv % Hkv) * D : (size_t)bkv * (size_t)N * D;
+  const int bh0 = bkv * group;  // first query head (of B*H) of this key/value head's group
+  const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bkv / Hkv], 0), N)) : Ns;
+
   const int kw0 = k0 + pair * kBwdRows;
   const int my_k = kw0 + l32;
 
@@ -353,18 +385,18 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const __bf16* kvsrc = pw ? k : v;
 #pragma unroll
   for (int kb = 0; kb < kDB; ++kb)
-    kvf[kb] = (my_k < Nk) ? *(const bf16x8*)(kvsrc + kv_off + (size_t)my_k * D + 16 * kb + 8 * h) : (bf16x8){};
+    kvf[kb] = (my_k < Nk) ? *(const bf16x8*)(kvsrc + kv_off + (size_t)my_k * kpitch + 16 * kb + 8 * h) : (bf16x8){};
 
   int dma[kCopies];
 #pragma unroll
   for (int p = 0; p < kCopies; ++p) {
     const int pos = (wave + NW * p) * 64 + lane;
     const int row = pos / T::CPR, phys = pos % T::CPR;
-    dma[p] = row * T::RB + (phys ^ T::swz(row)) * 16;
+    dma[p] = row * qpitch_b + (phys ^ T::swz(row)) * 16;
   }
   // Query tiles t0 .. nqt-1 of each of the group's query heads. Key blocks and query tiles are both 128 rows,
   // so under causal masking the first tile (t0 = this key block) is the only one that crosses the diagonal.
-  const int nqt = (N + kDkdvTile - 1) / kDkdvTile;
+  const int nqt = (Ns + kDkdvTile - 1) / kDkdvTile;
   const int t0 = CAUSAL ? kblk : 0;
   const int per_head = nqt - t0;
   const int n_iter = (k0 < Nk) ? group * per_head : 0;  // a block of padded keys only writes zeros
@@ -372,11 +404,13 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   auto copy_iter = [&](int it, int S) __attribute__((always_inline)) {
     const int hq = bh0 + it / per_head;
     const int row0 = (t0 + it % per_head) * kDkdvTile;
-    const size_t base = (size_t)hq * N;
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - row0, kDkdvTile)));
-    const int row_base = __builtin_amdgcn_readfirstlane(min(row0, N - 1));
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (base + row_base) * D, rows * T::RB);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + (base + row_base) * D, rows * T::RB);
+    // first element of row 0 of query head hq
+    const size_t base = VARLEN ? ((size_t)start * H + hq % H) * D : (size_t)hq * N * D;
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(Ns - row0, kDkdvTile)));
+    const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Ns - 1));
+    const int bytes = rows > 0 ? (rows - 1) * qpitch_b + T::RB : 0;  // ends with the sequence's last row
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base + (size_t)row_base * qpitch, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + base + (size_t)row_base * qpitch, bytes);
 #pragma unroll
     for (int p = 0; p < kCopies; ++p) {
       lds_copy16_inline(rq, qst + S * T::kBytes + (wave + NW * p) * 1024, dma[p]);
@@ -430,11 +464,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     const lds_char* tr_src = pw ? os : qs;    // dO^T for dV^T, q^T for dK^T
     if constexpr (pw) {
       const int qlo = row0 + 32 * sb;
-      if ((qlo + kBwdRows > N) || (kw0 + kBwdRows > Nk) || (CAUSAL && qlo < kw0 + kBwdRows - 1)) {
+      if ((qlo + kBwdRows > Ns) || (kw0 + kBwdRows > Nk) || (CAUSAL && qlo < kw0 + kBwdRows - 1)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = qlo + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool vis = (qi < N) && (my_k < Nk) && (!CAUSAL || my_k <= qi);
+          const bool vis = (qi < Ns) && (my_k < Nk) && (!CAUSAL || my_k <= qi);
           x[r] = vis ? x[r] : -INFINITY;
         }
       }
@@ -511,8 +545,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   }
 
   // dk_j = scale * dK^T, dv_j = dV^T; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k (0 past Nk)
-  if (my_k < N) {
-    __bf16* row = (pw ? dv : dk) + kv_off + (size_t)my_k * D;
+  if (my_k < Ns) {
+    __bf16* row = (pw ? dv : dk) + kv_off + (size_t)my_k * kpitch;
     const float f = (my_k < Nk) ? (pw ? 1.f : scale) : 0.f;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
@@ -527,15 +561,16 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
 // ------------------------------------------------------------------------------------------------------------
 // launcher (arguments already validated by the C ABI layer)
 // ------------------------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN = false>
 static hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv,
-                             int N, float scale, const int* kv_len, hipStream_t stream) {
+                             int N, float scale, const int* kv_len, hipStream_t stream,
+                             const int* cu_seqlens = nullptr, int T_total = 0) {
   const int group = H / Hkv;
   constexpr int lds_a = 4 * BwdTile<D>::kBytes;
   constexpr int lds_b = 2 * (2 * BwdTile<D, kDkdvTile>::kBytes + kWsTileBytes) + 8 * kPSlotBytes;
-  auto ka = fa_bwd_dq_kernel<D, CAUSAL>;
-  auto kb = fa_bwd_dkdv_kernel<D, CAUSAL>;
+  auto ka = fa_bwd_dq_kernel<D, CAUSAL, VARLEN>;
+  auto kb = fa_bwd_dkdv_kernel<D, CAUSAL, VARLEN>;
   hipError_t e = hipFuncSetAttribute((const void*)ka, hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)kb, hipFuncAttributeMaxDynamicSharedMemorySize, lds_b);
@@ -543,12 +578,12 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   const unsigned nblk = (unsigned)((N + kBwdBlock - 1) / kBwdBlock);
   hipLaunchKernelGGL(ka, dim3(nblk, (unsigned)(B * H)), dim3(kBwdThreads), lds_a, stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse, (const __bf16*)dout, (__bf16*)dq, ws,
-                     N, B * H, scale, group, H, kv_len);
+                     N, B * H, scale, group, H, kv_len, cu_seqlens, T_total);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv)), dim3(64 * kDkdvWaves), lds_b, stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const float*)ws, (__bf16*)dk,
-                     (__bf16*)dv, N, B * Hkv, scale, group, Hkv, kv_len);
+                     (__bf16*)dv, N, B * Hkv, scale, group, Hkv, kv_len, cu_seqlens, T_total);
   return hipGetLastError();
 }
 
@@ -556,6 +591,18 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv, int N,
                            int d, bool causal, float scale, const int* kv_len, hipStream_t stream) {
 #define FA_BWD(D, C) launch_bwd<D, C>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, N, scale, kv_len, stream)
+  if (d == 64) return causal ? FA_BWD(64, true) : FA_BWD(64, false);
+  return causal ? FA_BWD(128, true) : FA_BWD(128, false);
+#undef FA_BWD
+}
+
+hipError_t launch_bwd_varlen_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv, float* ws, const int* cu_seqlens,
+                                  int B, int H, int Hkv, int T_total, int max_seqlen, int d, bool causal, float scale,
+                                  hipStream_t stream) {
+#define FA_BWD(D, C)                                                                                         \
+  launch_bwd<D, C, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Hkv, max_seqlen, scale, nullptr, stream, \
+                         cu_seqlens, T_total)
   if (d == 64) return causal ? FA_BWD(64, true) : FA_BWD(64, false);
   return causal ? FA_BWD(128, true) : FA_BWD(128, false);
 #undef FA_BWD

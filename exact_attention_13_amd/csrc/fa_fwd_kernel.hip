@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int lo = min(max(cu_seqlens[bh / H], 0), T_total);
     const int hi = min(max(cu_seqlens[bh / H + 1], lo), T_total);
     start = __builtin_amdgcn_readfirstlane(lo);
-    Ns = __builtin_amdgcn_readfirstlane(hi - lo);
+    Ns = __builtin_amdgcn_readfirstlane(min(hi - lo, N));  // no longer than max_seqlen (= N)
   }
   const int q_lo = qb * kBrW;
   if (VARLEN && q_lo >= Ns) return;  // the whole workgroup: its query block lies past this sequence

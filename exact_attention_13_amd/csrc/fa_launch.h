@@ -26,6 +26,12 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv, int N,
                            int d, bool causal, float scale, const int* kv_len, hipStream_t stream);
+// The gradient kernels on packed variable-length batches (layout of launch_fwd_varlen_bf16; dq as q, dk and dv
+// as k); ws of bwd_workspace_bytes(B, H, max_seqlen) bytes.
+hipError_t launch_bwd_varlen_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv, float* ws, const int* cu_seqlens,
+                                  int B, int H, int Hkv, int T_total, int max_seqlen, int d, bool causal, float scale,
+                                  hipStream_t stream);
 // Workspace of the gradient kernels: (D_i, lse_i*log2e) float pairs, [B*H][N rounded up to 128].
 inline size_t bwd_workspace_bytes(int B, int H, int N) {
   return (size_t)B * (size_t)H * (size_t)((N + 127) / 128 * 128) * 2 * sizeof(float);

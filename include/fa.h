@@ -122,7 +122,8 @@ int fa_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse
  *                malformed array cannot make it read or write outside the
  *                tensors (the results are then meaningless).
  *   max_seqlen : at least the longest sequence, at most total (it sizes the
- *                grid; rows of a longer sequence past max_seqlen are not written)
+ *                grid; tokens of a longer sequence past its first max_seqlen
+ *                are neither read nor written)
  * An empty sequence writes nothing. B, H or total = 0 is an empty problem;
  * max_seqlen = 0 or above total with tokens present is FA_ERR_SHAPE; cu_seqlens
  * NULL is FA_ERR_NULL, not 4-byte aligned FA_ERR_ALIGN; o and lse must not
@@ -181,7 +182,28 @@ int fa_bwd_kpad(const void* q, const void* k, const void* v, const void* o, cons
                 void* dq, void* dk, void* dv, float* workspace, const int* kv_len, int B, int H, int H_kv, int N, int d,
                 int causal, float scale, hipStream_t stream);
 
-/* fa_bwd_workspace_bytes -- bytes of the fa_bwd / fa_bwd_kpad workspace (0 for an empty problem). */
+/*
+ * fa_bwd_varlen -- gradients of fa_fwd_varlen (packed variable-length
+ * batches): every sequence's gradients are those of its own attention
+ * problem, as in fa_bwd.
+ *   q, o, dout, dq : [total, H, d] bf16 (dq written); k, v, dk, dv :
+ *                    [total, H_kv, d] bf16 (dk, dv written); lse : float
+ *                    [H, total] from fa_fwd_varlen with the same arguments
+ *   workspace      : fa_bwd_workspace_bytes(B, H, max_seqlen) bytes, 16-byte
+ *                    aligned, as for fa_bwd
+ *   cu_seqlens, B, H, H_kv, total, max_seqlen, d, causal, scale : as
+ *                    fa_fwd_varlen (offsets clamped on the device the same way)
+ * Errors as fa_fwd_varlen, with every tensor, lse, cu_seqlens and the
+ * workspace checked (NULL, alignment) and no output (dq, dk, dv, workspace)
+ * allowed to overlap an input or another output (FA_ERR_ALIAS). Deterministic
+ * as fa_bwd.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens, int B, int H, int H_kv,
+                  int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream);
+
+/* fa_bwd_workspace_bytes -- bytes of the fa_bwd / fa_bwd_kpad workspace for N (fa_bwd_varlen: N = max_seqlen);
+ * 0 for an empty problem. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /*

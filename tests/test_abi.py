@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 10500
+    assert fa.fa_version() == 10600
     for code in range(8):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
@@ -182,6 +182,25 @@ def test_varlen_error_codes():
     assert vl(o=A + 0x1000000 + 16) == fa.FA_ERR_ALIAS            # o inside k
     assert vl(total=0, q=0, k=0, v=0, o=0, lse=0, cu=0) == fa.FA_OK  # no token: nothing to do
     assert vl(B=0, q=0, cu=0) == fa.FA_OK
+
+
+def test_varlen_backward_error_codes():
+    P = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, dout=A + 0x5000000,
+             dq=A + 0x6000000, dk=A + 0x7000000, dv=A + 0x8000000, ws=A + 0x9000000, cu=A + 0xA000000)
+
+    def bv(B=2, H=4, Hkv=2, total=100, max_seqlen=60, d=64, causal=0, scale=0.125, **kw):
+        p = dict(P, **kw)
+        return fa.fa_bwd_varlen(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"], p["dv"],
+                                p["ws"], p["cu"], B, H, Hkv, total, max_seqlen, d, causal, scale, 0)
+    for name in P:
+        assert bv(**{name: 0}) == fa.FA_ERR_NULL, name
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv", "ws"):
+        assert bv(**{name: P[name] + 8}) == fa.FA_ERR_ALIGN, name
+    assert bv(cu=P["cu"] + 2) == fa.FA_ERR_ALIGN and bv(lse=P["lse"] + 2) == fa.FA_ERR_ALIGN
+    assert bv(max_seqlen=101) == fa.FA_ERR_SHAPE and bv(Hkv=3) == fa.FA_ERR_SHAPE
+    assert bv(dq=P["q"]) == fa.FA_ERR_ALIAS and bv(ws=P["cu"] - 16) == fa.FA_ERR_ALIAS
+    assert bv(dk=P["dv"] + 64) == fa.FA_ERR_ALIAS
+    assert bv(total=0, **{name: 0 for name in P}) == fa.FA_OK
 
 
 def test_fp8_error_codes():

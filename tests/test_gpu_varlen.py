@@ -114,3 +114,108 @@ def test_varlen_writes_nothing_outside_o_and_lse(fa):
     ref = fa.forward_varlen(q, k, v, cu, max(lens), causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o.view(T, H, d), ref[0]) and torch.equal(lse.view(H, T), ref[1])
+
+
+# Gradients (fa_bwd_varlen): per gradient tensor max |g - g_oracle| <= 2e-2 max |g_oracle| + 1e-5, the bar of the
+# padded gradient call, with o and lse from the library's packed forward.
+RTOL_G, ATOL_G = 2e-2, 1e-5
+
+
+def _bwd(fa, q, k, v, dout, lens, causal, scale):
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda:0")
+    qd, kd, vd, dd = (x.to("cuda:0") for x in (q, k, v, dout))
+    ms = max(max(lens), 1)
+    o, lse = fa.forward_varlen(qd, kd, vd, cu, ms, causal=causal, scale=scale)
+    g = fa.backward_varlen(qd, kd, vd, o, lse, dd, cu, ms, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return g
+
+
+def _check_grad(label, got, ref):
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g)), label
+    err = float(np.abs(g - ref).max()) if g.size else 0.0
+    mag = float(np.abs(ref).max()) if ref.size else 0.0
+    print(f"[parity] {label} max|err|={err:.3e} max|ref|={mag:.3e} rel={err / max(mag, 1e-300):.3e}", flush=True)
+    assert err <= RTOL_G * mag + ATOL_G, f"{label}: error {err} above {RTOL_G} x {mag} + {ATOL_G}"
+
+
+def _dout_varlen(T, H, d, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn((T, H, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (4, 1)])
+@pytest.mark.parametrize("lens", [(1, 7, 63, 64, 65, 300, 0, 129), (0, 257, 0, 5)])
+def test_varlen_backward_ragged(fa, lens, H, Hkv, d, causal):
+    label = f"bwd varlen lens={lens} H{H} Hkv{Hkv} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v = ai.make_qkv_varlen(lens, H, d, seed=900 + sum(lens), Hkv=Hkv)
+    dout = _dout_varlen(sum(lens), H, d, 901 + sum(lens))
+    scale = ai.default_scale(d)
+    dq, dk, dv = _bwd(fa, q, k, v, dout, lens, causal, scale)
+    rq, rk, rv = oracle.attention_bwd_varlen(q, k, v, dout, [0] + list(np.cumsum(lens)), causal, scale)
+    _check_grad(f"{label} dq", dq, rq)
+    _check_grad(f"{label} dk", dk, rk)
+    _check_grad(f"{label} dv", dv, rv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_backward_medium(fa, causal):
+    lens, H, Hkv, d = (700, 1, 1500, 333), 8, 2, 128
+    label = f"bwd varlen lens={lens} H{H} Hkv{Hkv} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v = ai.make_qkv_varlen(lens, H, d, seed=910, Hkv=Hkv)
+    dout = _dout_varlen(sum(lens), H, d, 911)
+    scale = ai.default_scale(d)
+    dq, dk, dv = _bwd(fa, q, k, v, dout, lens, causal, scale)
+    rq, rk, rv = oracle.attention_bwd_varlen(q, k, v, dout, [0] + list(np.cumsum(lens)), causal, scale)
+    _check_grad(f"{label} dq", dq, rq)
+    _check_grad(f"{label} dk", dk, rk)
+    _check_grad(f"{label} dv", dv, rv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_backward_one_sequence_equals_fa_bwd(fa, causal):
+    T, H, Hkv, d = 1000, 4, 2, 64
+    q, k, v = ai.make_qkv_varlen((T,), H, d, seed=920, Hkv=Hkv)
+    dout = _dout_varlen(T, H, d, 921)
+    scale = ai.default_scale(d)
+    a = _bwd(fa, q, k, v, dout, (T,), causal, scale)
+    qp, kp, vp, dp = (x.transpose(0, 1)[None].contiguous().to("cuda:0") for x in (q, k, v, dout))
+    o, lse = fa.forward(qp, kp, vp, causal=causal, scale=scale)
+    b = fa.backward(qp, kp, vp, o, lse, dp, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y[0].transpose(0, 1))
+
+
+def test_varlen_backward_writes_nothing_outside_its_outputs(fa):
+    lens, H, Hkv, d = (5, 0, 130, 64), 4, 2, 64
+    T = sum(lens)
+    q, k, v = (x.to("cuda:0") for x in ai.make_qkv_varlen(lens, H, d, seed=930, Hkv=Hkv))
+    dout = _dout_varlen(T, H, d, 931).to("cuda:0")
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda:0")
+    o, lse = fa.forward_varlen(q, k, v, cu, max(lens), causal=True)
+    pad = 4096
+    sizes = (T * H * d, T * Hkv * d, T * Hkv * d)
+    buf = torch.full((sum(sizes) + 4 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda:0")
+    offs = [pad, 2 * pad + sizes[0], 3 * pad + sizes[0] + sizes[1]]
+    views = [buf[offs[i]: offs[i] + sizes[i]] for i in range(3)]
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(len(lens), H, max(lens)),), dtype=torch.uint8, device="cuda:0")
+    rc = fa.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                          views[0].data_ptr(), views[1].data_ptr(), views[2].data_ptr(), ws.data_ptr(), cu.data_ptr(),
+                          len(lens), H, Hkv, T, max(lens), d, 1, ai.default_scale(d),
+                          torch.cuda.current_stream().cuda_stream)
+    assert rc == fa.FA_OK
+    torch.cuda.synchronize()
+    mask = torch.ones_like(buf, dtype=torch.bool)
+    for i in range(3):
+        mask[offs[i]: offs[i] + sizes[i]] = False
+    assert torch.all(buf[mask] == 1234.0)
+    ref = fa.backward_varlen(q, k, v, o, lse, dout, cu, max(lens), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(views[0].view(T, H, d), ref[0])
+    assert torch.equal(views[1].view(T, Hkv, d), ref[1]) and torch.equal(views[2].view(T, Hkv, d), ref[2])
