@@ -11,7 +11,8 @@ sample of the same workload on this host's cores.
 The line also carries `backward`: the gradient call fa_bwd (dq, then dk and dv) on the headline workload and on
 the long causal one, timed the same way, in the usual FLOP convention 2.5 x the forward's (five matrix products:
 the recomputed QK^T, dO V^T, dV, dQ, dK); `fp8`: fa_fwd_fp8 on the same two shapes with the inputs quantized
-per tensor to float8_e4m3fn, against the fp8 peak; and `varlen`: fa_fwd_varlen on the packed workloads.
+per tensor to float8_e4m3fn, against the fp8 peak; `varlen` and `varlen_backward`: fa_fwd_varlen and fa_bwd_varlen
+on the packed workloads.
 
     --bwd-only          time only the gradient call of --workload (one JSON line; for profiling)
 
@@ -322,6 +323,54 @@ def varlen_record(w, steps: int, warmup: int):
                          "frac": round(w.flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
             "flops_per_launch": w.flops, "algorithmic_bytes_per_launch": w.algorithmic_bytes,
             "kernel": "fa_fwd_bf16_kernel (VARLEN)", "kernel_src_sha256_16": kernel_src_hash()}
+
+
+def varlen_backward_record(w, steps: int, warmup: int):
+    """fa_bwd_varlen on a packed workload (o and lse from one fa_fwd_varlen call), FLOPs 2.5 x the forward's."""
+    import torch
+
+    import attn_inputs as ai
+    import exact_attention_13_amd as fa
+
+    q, k, v = (x.cuda() for x in ai.make_qkv_varlen(w.lens, w.H, w.d, w.seed, Hkv=w.Hkv or None))
+    cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device="cuda")
+    o, lse = fa.forward_varlen(q, k, v, cu, w.max_len, causal=w.causal, scale=w.scale)
+    g = torch.Generator("cpu").manual_seed(w.seed + 500)
+    dout = torch.randn(tuple(q.shape), generator=g).to(torch.bfloat16).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(w.B, w.H, w.max_len),), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), cu.data_ptr(), w.B, w.H, w.Hk, w.T, w.max_len, w.d,
+            int(w.causal), w.scale, stream.cuda_stream)
+
+    def call():
+        rc = fa.fa_bwd_varlen(*args)
+        if rc != 0:
+            raise RuntimeError(f"fa_bwd_varlen failed: {fa.fa_strerror(rc)}")
+    for _ in range(warmup):
+        call()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    mean = statistics.fmean(durs)
+    flops = 2.5 * w.flops
+    return {"workload": w.name, "call": "fa_bwd_varlen", "tflops": round(flops * steps / wall / 1e12, 2),
+            "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
+                          "min": round(min(durs), 4)},
+            "roofline": {"bound": "mfma", "achieved": round(flops / (mean * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "flops_per_call": flops, "kernels": ["fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"],
+            "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}
 
 
 def traffic_from_profiles(w, prefix="", srcs=KERNEL_SRCS):
@@ -854,6 +903,8 @@ def main():
         line["backward"] = [backward_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in BWD_WORKLOADS]
         line["fp8"] = [fp8_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in FP8_WORKLOADS]
         line["varlen"] = [varlen_record(vw, steps=20, warmup=3) for vw in ai.VARLEN_WORKLOADS.values()]
+        line["varlen_backward"] = [varlen_backward_record(vw, steps=10, warmup=2)
+                                   for vw in ai.VARLEN_WORKLOADS.values()]
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_rows)
         cb.pop("seconds")
