@@ -90,48 +90,6 @@ __device__ __forceinline__ void schedule_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-__device__ __forceinline__ int wave_sum_i32(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-__device__ __forceinline__ int wave_max_i32(int x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
-  return x;
-}
-
-// Packed batches of at most 64 sequences: the dk/dv work items (sequence b, key block kb) of one key/value head,
-// taken in decreasing order of the query tiles each visits (nb_b - kb when causal, nb_b otherwise; ties by b, then
-// kb), so that the longest items start first and the short ones fill in behind them. nb is this lane's sequence's
-// key-block count (lane b holds sequence b; 0 past the last sequence). Returns false when `rank` is past the last
-// item; all lanes get the same result.
-__device__ bool longest_first_item(int rank, int nb, bool causal, int& b_out, int& kb_out) {
-  const int lane = threadIdx.x & 63;
-  const int total = wave_sum_i32(nb);  // one item per key block
-  if (rank >= total) return false;
-  // items with more than W visited tiles
-  auto above = [&](int W) { return wave_sum_i32(causal ? max(0, nb - W) : (nb > W ? nb : 0)); };
-  int lo = 1, hi = max(wave_max_i32(nb), 1);  // above(hi) = 0 <= rank < total = above(0)
-  while (lo < hi) {  // the smallest W >= 1 with above(W) <= rank: the work of item `rank`
-    const int mid = (lo + hi) / 2;
-    if (above(mid) <= rank) hi = mid; else lo = mid + 1;
-  }
-  const int W = lo, j = rank - above(W);  // position inside that work level
-  // causal: each sequence with nb >= W holds one item of work W (kb = nb - W); otherwise each sequence with nb == W
-  // holds W of them
-  const bool in_level = causal ? (nb >= W) : (nb == W);
-  const uint64_t mask = __ballot(in_level);
-  const int s = causal ? j : j / W;  // which sequence of the level, in index order
-  const int before = __popcll(mask & ((1ull << lane) - 1ull));
-  const uint64_t pick = __ballot(in_level && before == s);
-  const int b = __builtin_ctzll(pick);
-  const int nb_b = __shfl(nb, b);
-  b_out = b;
-  kb_out = causal ? nb_b - W : j % W;
-  return true;
-}
-
 __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
   float s = 0.f;
 #pragma unroll
@@ -159,7 +117,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nq = gridDim.x;
   int bh, qb;
-  map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
+  if (VARLEN && BH / H <= 64) {
+    // packed batches: (sequence, query block) items in longest-first order (causal: the last blocks, which visit
+    // the most key tiles, first)
+    const int nb = packed_blocks(cu_seqlens, BH / H, T_total, N, kBwdBlock);
+    int rank, hq, b, kb;
+    map_packed(blockIdx.x + nq * blockIdx.y, H, group, rank, hq);
+    if (!longest_first_item(rank, nb, CAUSAL, b, kb)) return;  // the whole workgroup: no item left
+    bh = __builtin_amdgcn_readfirstlane(b * H + hq);
+    qb = __builtin_amdgcn_readfirstlane(CAUSAL ? __shfl(nb, b) - 1 - kb : kb);
+  } else {
+    map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
+  }
   int start = 0, Ns = N;  // this head's sequence: its first token and length
   if constexpr (VARLEN) {
     const int lo = min(max(cu_seqlens[bh / H], 0), T_total);
@@ -402,13 +371,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   if (VARLEN && nbatch <= 64) {
     // packed batches: consecutive workgroups are the Hkv heads of one (sequence, key block) item (so a head stays
     // on one XCD when Hkv is a multiple of 8), items in longest-first order
-    const int lane = threadIdx.x & 63;
-    int nb = 0;
-    if (lane < nbatch) {
-      const int lo = min(max(cu_seqlens[lane], 0), T_total);
-      const int hi = min(max(cu_seqlens[lane + 1], lo), T_total);
-      nb = (min(hi - lo, N) + kBwdBlock - 1) / kBwdBlock;
-    }
+    const int nb = packed_blocks(cu_seqlens, nbatch, T_total, N, kBwdBlock);
     const int lin = blockIdx.x + nk * blockIdx.y;
     int b, kb;
     if (!longest_first_item(lin / Hkv, nb, CAUSAL, b, kb)) return;  // the whole workgroup: no item left

@@ -122,7 +122,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int nq = gridDim.x;
   int bh, qb;
-  map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
+  if (VARLEN && BH / H <= 64) {
+    // packed batches: (sequence, query block) items in longest-first order (causal: the last blocks, which visit
+    // the most key tiles, first)
+    const int nb = packed_blocks(cu_seqlens, BH / H, T_total, N, kBrW);
+    int rank, hq_, b, kb;
+    map_packed(blockIdx.x + nq * blockIdx.y, H, group, rank, hq_);
+    if (!longest_first_item(rank, nb, CAUSAL, b, kb)) return;  // the whole workgroup: no item left
+    bh = __builtin_amdgcn_readfirstlane(b * H + hq_);
+    qb = __builtin_amdgcn_readfirstlane(CAUSAL ? __shfl(nb, b) - 1 - kb : kb);
+  } else {
+    map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
+  }
 
   // Packed sequences: this head's sequence starts at token `start` and has Ns tokens (offsets clamped to
   // [0, T_total], so a malformed offset array cannot send an access outside the tensors); otherwise Ns = N.

@@ -77,6 +77,73 @@ __device__ __forceinline__ void map_workgroup(int lin, int nq, int bh_count, int
   }
 }
 
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
+  return x;
+}
+
+// Packed batches of at most 64 sequences: the work items (sequence b, block kb) of one head in decreasing order of
+// their cost, nb_b - kb when `causal` (block kb of a causal kernel numbered from its most expensive end) and nb_b
+// otherwise, ties by b, then kb, so that the longest items start first and the short ones fill in behind them. nb
+// is this lane's sequence's block count (lane b holds sequence b; 0 past the last sequence). Returns false when
+// `rank` is past the last item; all lanes get the same result.
+__device__ bool longest_first_item(int rank, int nb, bool causal, int& b_out, int& kb_out) {
+  const int lane = threadIdx.x & 63;
+  const int total = wave_sum_i32(nb);  // one item per key block
+  if (rank >= total) return false;
+  // items with more than W visited tiles
+  auto above = [&](int W) { return wave_sum_i32(causal ? max(0, nb - W) : (nb > W ? nb : 0)); };
+  int lo = 1, hi = max(wave_max_i32(nb), 1);  // above(hi) = 0 <= rank < total = above(0)
+  while (lo < hi) {  // the smallest W >= 1 with above(W) <= rank: the work of item `rank`
+    const int mid = (lo + hi) / 2;
+    if (above(mid) <= rank) hi = mid; else lo = mid + 1;
+  }
+  const int W = lo, j = rank - above(W);  // position inside that work level
+  // causal: each sequence with nb >= W holds one item of work W (kb = nb - W); otherwise each sequence with nb == W
+  // holds W of them
+  const bool in_level = causal ? (nb >= W) : (nb == W);
+  const uint64_t mask = __ballot(in_level);
+  const int s = causal ? j : j / W;  // which sequence of the level, in index order
+  const int before = __popcll(mask & ((1ull << lane) - 1ull));
+  const uint64_t pick = __ballot(in_level && before == s);
+  const int b = __builtin_ctzll(pick);
+  const int nb_b = __shfl(nb, b);
+  b_out = b;
+  kb_out = causal ? nb_b - W : j % W;
+  return true;
+}
+
+// Packed batches: workgroup `lin` -> (item rank, query head hq). Consecutive groups of 8 workgroups land on the 8
+// XCDs; with H a multiple of 8, XCD x takes the key/value heads x, x+8, ... with all their query heads (when H/group
+// is a multiple of 8), else the query heads x, x+8, ..., as map_workgroup does for B*H heads.
+__device__ __forceinline__ void map_packed(int lin, int H, int group, int& rank, int& hq) {
+  if ((H & 7) == 0) {
+    const int xcd = lin & 7, t = lin >> 3, per = H >> 3;
+    const int slot = t % per;
+    rank = t / per;
+    hq = ((H / group) & 7) == 0 ? (xcd + 8 * (slot / group)) * group + slot % group : xcd + 8 * slot;
+  } else {
+    rank = lin / H;
+    hq = lin % H;
+  }
+}
+
+// The block counts (rows per block `rows`) of the sequences of a packed batch, lane b holding sequence b's; offsets
+// clamped to [0, T_total], lengths to N.
+__device__ __forceinline__ int packed_blocks(const int* cu_seqlens, int nbatch, int T_total, int N, int rows) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= nbatch) return 0;
+  const int lo = min(max(cu_seqlens[lane], 0), T_total);
+  const int hi = min(max(cu_seqlens[lane + 1], lo), T_total);
+  return (min(hi - lo, N) + rows - 1) / rows;
+}
+
 template <int V>
 using Int = std::integral_constant<int, V>;
 
