@@ -227,6 +227,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int col = 32 * cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     v_off[cb] = vrow * T::RB + ((col / 8) ^ T::swz_v(vrow)) * 16 + (col % 8) * 2;
   }
+  // Read addresses: an LDS instruction's immediate offset reaches 64 KiB and the V ring lies above that. One
+  // base register per fragment column (the ring's start plus this lane's offset, opaque to the compiler, which
+  // otherwise re-forms the sum for every read) lets every read of every stage and step carry the rest in its
+  // immediate: no address arithmetic in the loop.
+  int v_base[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    v_base[cb] = (int)(size_t)(vst + v_off[cb]);
+    asm volatile("" : "+v"(v_base[cb]));
+  }
+  int k_base[kDB];
+#pragma unroll
+  for (int kb = 0; kb < kDB; ++kb) {
+    k_base[kb] = (int)(size_t)(kst + k_off[kb]);
+    asm volatile("" : "+v"(k_base[kb]));
+  }
 
   const float c2 = scale * kLog2e;
   float m_ref = -INFINITY;  // exponent reference (raw-score units) for row my_q
@@ -238,14 +254,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // S^T = K_j Q^T from the K stage at byte `kat` (2KT blocks of 32 keys; block b = rows 32(b%2).. of part b/2).
   // s[b][r] is the score of query my_q and key j*64KT + 32b + 16(r/8) + 8h + r%8.
   auto qk = [&](f32x16(&s)[2 * KT], int kat) __attribute__((always_inline)) {
-    const lds_char* ks = kst + kat;
 #pragma unroll
     for (int b = 0; b < 2 * KT; ++b) {
       s[b] = (f32x16){};
 #pragma unroll
       for (int kb = 0; kb < kDB; ++kb) {
-        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(ks + (b >> 1) * T::kBytes + k_off[kb] +
-                                                                             32 * (b & 1) * T::RB);
+        const bf16x8 kf = *(const __attribute__((address_space(3))) bf16x8*)(
+            (lds_char*)(size_t)k_base[kb] + (kat + (b >> 1) * T::kBytes + 32 * (b & 1) * T::RB));
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], s[b], 0, 0, 0);
       }
     }
@@ -296,13 +311,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // the 8 exponentials of step m+1 can run on the vector ALU while the MFMAs of step m run, and the V fragments
   // of step m+1 are read during step m. Lane slot 8h+e of step m <-> key j*64KT + 16m + 8h + e.
   auto softmax_pv = [&](f32x16(&s)[2 * KT], int vat) __attribute__((always_inline)) {
-    const lds_char* vs = vst + vat;
     const float nb = -m_ref * c2;
     float rs[2] = {0.f, 0.f};
     auto read_v = [&](int m, bf16x8(&vf)[kCB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const lds_char* va = vs + (m >> 2) * T::kBytes + v_off[cb] + 16 * (m & 3) * T::RB;
+        const lds_char* va = (lds_char*)(size_t)v_base[cb] + (vat + (m >> 2) * T::kBytes + 16 * (m & 3) * T::RB);
         const bf16x4 v0 =
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(va));
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
