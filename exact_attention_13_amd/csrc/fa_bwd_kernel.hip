@@ -17,12 +17,14 @@
 //   * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys of one key/value head, 8 waves: each block of 32
 //     keys belongs to a pair of waves on one SIMD, one accumulating dV (from S and p), the other dK (from dP and
 //     dS), so each holds half the accumulators and two waves share every SIMD. Query tiles of 128 rows (q, dO
-//     and the workspace pairs) of every query head of the group stream through LDS. S = Q K^T and dP = dO V^T
+//     and the workspace values) of every query head of the group stream through LDS. S = Q K^T and dP = dO V^T
 //     put one key in each lane (K or V rows stay in registers as the B operand); dV^T += dO^T P and
 //     dK^T += Q^T dS take P and dS from registers as B operands and dO^T, Q^T by transposing LDS reads; p
 //     passes from the first wave of the pair to the second through LDS.
-// The workspace holds the pairs (D_i, lse_i*log2e) as [B*H][Npad] float2, Npad = N rounded up to 128; rows
-// N .. Npad-1 hold (0, +inf), which makes p (and dS) of those rows exactly 0 in the dk/dv kernel.
+// The workspace holds D_i and lse_i*log2e as two planes per head, [B*H][2][Npad] float, Npad = N rounded up to
+// 128; rows N .. Npad-1 hold D = 0 and lse2 = +inf, which makes p (and dS) of those rows exactly 0 in the dk/dv
+// kernel. With the planes apart, each wave of the dk/dv kernel reads from LDS only the plane it uses (the p wave
+// lse2, the dS wave D), half the bytes of reading interleaved pairs.
 // Key padding (the forward's per-batch count Nk of valid keys, triton-transformer README usage example "ex. BERT"):
 // the dq kernel visits only the key tiles below Nk and masks keys >= Nk like the sequence end; the dk/dv kernel
 // masks them, loads no k or v row past Nk and writes zero gradients for them. With Nk = 0 no tile is visited
@@ -49,7 +51,7 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32;                   // rows per wave: query rows (dq) or keys (dk, dv)
 constexpr int kBwdBlock = kBwdWaves * kBwdRows;  // rows per workgroup
 constexpr int kBwdTile = 64;                   // keys per LDS tile (dq)
-constexpr int kWsTileBytes = 1024;             // LDS slot for one tile of workspace pairs (one copy: 64 x 16 B)
+constexpr int kWsTileBytes = 1024;             // LDS slot for one tile of workspace values: 128 D, then 128 lse2
 
 // Workspace rows per head: N rounded up to the dq workgroup's 128 rows (its grid writes exactly these rows),
 // which is also a whole number of the dk/dv kernel's 128-row query tiles.
@@ -98,7 +100,7 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// dq (and the workspace pairs D_i, lse_i*log2e)
+// dq (and the workspace values D_i, lse_i*log2e)
 // ------------------------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
@@ -177,8 +179,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const float lse2 = (my_q < Ns) ? lse[lse_off + my_q] * kLog2e : INFINITY;
   const int npad = ws_rows(N);
   if (my_q < npad && h == 0) {
-    float2* w = (float2*)ws + (size_t)bh * npad + my_q;
-    *w = make_float2(Di, lse2);
+    float* w = ws + (size_t)bh * 2 * npad + my_q;
+    w[0] = Di;
+    w[npad] = lse2;
   }
 
   // LDS-DMA: copy instruction p of this wave writes chunk positions (wave + NW p)*64 + lane of the tile
@@ -440,9 +443,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
       lds_copy16_inline(rq, qst + S * T::kBytes + (wave + NW * p) * 1024, dma[p]);
       lds_copy16_inline(rd, dst + S * T::kBytes + (wave + NW * p) * 1024, dma[p]);
     }
-    if (wave == 0) {  // the tile's 128 pairs (1 KiB, always inside the padded workspace)
-      const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + 2 * ((size_t)hq * npad + row0), kWsTileBytes);
-      lds_copy16_inline(rw, wst + S * kWsTileBytes, lane * 16);
+    if (wave == 0) {  // the tile's 128 D values, then its 128 lse2 values (always inside the padded workspace)
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + 2 * (size_t)hq * npad + row0, (npad + kDkdvTile) * 4);
+      lds_copy16_inline(rw, wst + S * kWsTileBytes, (lane & 31) * 16 + (lane >> 5) * npad * 4);
     }
   };
 
@@ -498,15 +501,16 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        // lse2 of query rows 32sb + 16m + 8h .. +7 of the tile (the odd floats of 64 bytes of pairs)
+        // lse2 of query rows 32sb + 16m + 8h .. +7 of the tile
         const __attribute__((address_space(3))) f32x4* wp =
-            (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 16 * m + 8 * h) * 8);
+            (const __attribute__((address_space(3))) f32x4*)(wsl + 512 + (32 * sb + 16 * m + 8 * h) * 4);
         f32x8 pv;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
           const f32x4 w = wp[u];
-          pv[2 * u] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * m + 2 * u], c2, -w[1]));
-          pv[2 * u + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * m + 2 * u + 1], c2, -w[3]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pv[4 * u + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * m + 4 * u + e], c2, -w[e]));
         }
         const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
         *(__attribute__((address_space(3))) bf16x8*)(ps + (m * 64 + lane) * 16) = pb;
@@ -524,13 +528,13 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
       for (int m = 0; m < 2; ++m) {
         const bf16x8 pb = *(const __attribute__((address_space(3))) bf16x8*)(ps + (m * 64 + lane) * 16);
         const __attribute__((address_space(3))) f32x4* wp =
-            (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 16 * m + 8 * h) * 8);
+            (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 16 * m + 8 * h) * 4);
         f32x8 dsv;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
           const f32x4 w = wp[u];
-          dsv[2 * u] = (float)pb[2 * u] * (x[8 * m + 2 * u] - w[0]);
-          dsv[2 * u + 1] = (float)pb[2 * u + 1] * (x[8 * m + 2 * u + 1] - w[2]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dsv[4 * u + e] = (float)pb[4 * u + e] * (x[8 * m + 4 * u + e] - w[e]);
         }
         const bf16x8 dsb = __builtin_convertvector(dsv, bf16x8);
         const int rbase = (32 * sb + 16 * m) * T::RB;

@@ -19,7 +19,7 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* vt, void* o,
                           bool causal, float scale, float q_scale, float k_scale, float v_scale, hipStream_t stream);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, hipStream_t stream);
-// Enqueue the two gradient kernels (dq and the workspace pairs, then dk and dv). Arguments must already be valid
+// Enqueue the two gradient kernels (dq and the workspace values, then dk and dv). Arguments must already be valid
 // (d is 64 or 128, B, H, N >= 1, Hkv >= 1 dividing H, pointers device-resident and aligned, ws of
 // bwd_workspace_bytes(B, H, N) bytes); kv_len as launch_fwd_bf16 (the forward's lengths); returns the launch
 // status.
@@ -32,7 +32,7 @@ hipError_t launch_bwd_varlen_bf16(const void* q, const void* k, const void* v, c
                                   const void* dout, void* dq, void* dk, void* dv, float* ws, const int* cu_seqlens,
                                   int B, int H, int Hkv, int T_total, int max_seqlen, int d, bool causal, float scale,
                                   hipStream_t stream);
-// Workspace of the gradient kernels: (D_i, lse_i*log2e) float pairs, [B*H][N rounded up to 128].
+// Workspace of the gradient kernels: D_i and lse_i*log2e planes, [B*H][2][N rounded up to 128] float.
 inline size_t bwd_workspace_bytes(int B, int H, int N) {
   return (size_t)B * (size_t)H * (size_t)((N + 127) / 128 * 128) * 2 * sizeof(float);
 }
