@@ -12,9 +12,12 @@ The line also carries `backward`: the gradient call fa_bwd (dq, then dk and dv) 
 the long causal one, timed the same way, in the usual FLOP convention 2.5 x the forward's (five matrix products:
 the recomputed QK^T, dO V^T, dV, dQ, dK); `fp8`: fa_fwd_fp8 on the same two shapes with the inputs quantized
 per tensor to float8_e4m3fn, against the fp8 peak; `varlen` and `varlen_backward`: fa_fwd_varlen and fa_bwd_varlen
-on the packed workloads.
+on the packed workloads; `mfma_probe`: the dense bf16 rate this GPU's matrix cores sustain on back-to-back MFMAs
+with random register operands, and the shader clock meanwhile (libfa_probe.so), with roofline.frac_of_probe =
+the headline kernel's rate over it (boxes differ by up to ~15 % in the clock their power limit allows).
 
     --bwd-only          time only the gradient call of --workload (one JSON line; for profiling)
+    --no-mfma-probe     leave out the matrix-core probe (mfma_probe, roofline.frac_of_probe)
 
 Other modes (used to produce the rocprofv3 summaries under profiles/):
     --pmc-pass          run a copy kernel of known size, then the workload kernel, a few times each
@@ -373,6 +376,38 @@ def varlen_backward_record(w, steps: int, warmup: int):
             "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}
 
 
+def mfma_probe(n_wg: int = 2048, iters: int = 2048, reps: int = 5):
+    """The dense bf16 rate the matrix cores of this GPU sustain, and the shader clock meanwhile
+    (libfa_probe.so, include/fa_probe.h: v_mfma_f32_32x32x16_bf16 back to back on random register operands)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(str(ROOT / "exact_attention_13_amd" / "libfa_probe.so"))
+    lib.fa_probe_mfma_bf16.restype = ctypes.c_int
+    lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_flop_per_wg_iter.restype = ctypes.c_double
+    lib.fa_probe_threads.restype = ctypes.c_int
+    sink = torch.empty((n_wg * lib.fa_probe_threads(),), dtype=torch.float32, device="cuda")
+    clk = torch.zeros((2 * n_wg,), dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream()
+    args = (sink.data_ptr(), clk.data_ptr(), n_wg, iters, st.cuda_stream)
+    for _ in range(2):
+        if lib.fa_probe_mfma_bf16(*args) != 0:
+            raise RuntimeError("fa_probe_mfma_bf16 failed")
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        lib.fa_probe_mfma_bf16(*args)
+        b.record(st)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    c = clk.view(n_wg, 2).sum(dim=0).tolist()
+    ghz = c[0] / c[1] * 0.1  # shader cycles per 100 MHz real-time tick
+    tflops = n_wg * iters * lib.fa_probe_flop_per_wg_iter() / (statistics.median(ms) * 1e-3) / 1e12
+    return {"tflops": round(tflops, 1), "sclk_ghz": round(ghz, 3), "pct_of_spec": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+            "note": "v_mfma_f32_32x32x16_bf16 back to back on random register operands, all CUs, 2 waves per SIMD"}
+
+
 def traffic_from_profiles(w, prefix="", srcs=KERNEL_SRCS):
     """HBM bytes per launch from the committed PMC summary, if it was taken on the current kernel source."""
     f = PROFILES / f"{prefix}{w.name}_hbm_traffic.txt"
@@ -548,6 +583,7 @@ def write_profiles(w):
     mops = _pick(sq, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kname)
     conflict = _pick(sq, "SQ_LDS_BANK_CONFLICT", kname)
     lds_active = _pick(sq, "SQ_LDS_IDX_ACTIVE", kname)
+    gui = _pick(sq, "GRBM_GUI_ACTIVE", kname)
     n_simd = 256 * 4
     util = mfma_busy / n_simd / (avg_us * 1e-6 * 2.4e9)
     traffic = {"kernel": kernel_name(w), "workload": w.name, "kernel_src_sha256_16": kernel_src_hash(),
@@ -601,9 +637,11 @@ HBM bandwidth at the traced average: {(k_read + k_write) / (avg_us * 1e-6) / 1e9
 | SQ_LDS_IDX_ACTIVE | {lds_active:.4g} |
 | SQ_WAIT_INST_LDS | {_pick(sq, 'SQ_WAIT_INST_LDS', kname):.4g} |
 | SQ_WAVE_CYCLES | {_pick(sq, 'SQ_WAVE_CYCLES', kname):.4g} |
-| GRBM_GUI_ACTIVE | {_pick(sq, 'GRBM_GUI_ACTIVE', kname):.4g} |
+| GRBM_GUI_ACTIVE | {gui:.4g} |
 
-MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (traced average x 2.4 GHz) = {100 * util:.1f} %.
+MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (traced average x 2.4 GHz) = {100 * util:.1f} %;
+over GRBM_GUI_ACTIVE / 8 (the GPU cycles counted during the kernel, summed over the 8 XCDs) = {100 * mfma_busy / n_simd / (gui / 8):.1f} %.
+Clock during the kernel, GRBM_GUI_ACTIVE / 8 / traced average: {gui / 8 / (avg_us * 1e-6) / 1e9:.2f} GHz.
 LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active, 1):.1f} %.
 """
     (PROFILES / f"{w.name}_rocprof.md").write_text(md)
@@ -815,6 +853,7 @@ def main():
                     help="time only fa_fwd_varlen on a packed workload")
     ap.add_argument("--write-profiles-varlen", metavar="WORKLOAD", choices=sorted(ai.VARLEN_WORKLOADS))
     ap.add_argument("--write-profiles-fp8", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true")
     args = ap.parse_args()
 
     if args.summarize:
@@ -889,6 +928,11 @@ def main():
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
         "kernel_src_sha256_16": kernel_src_hash(),
     }
+    if not args.no_mfma_probe:
+        # the same kernel time against what this GPU's matrix cores sustain (data-sheet peak: 2516.6 at 2.4 GHz)
+        probe = mfma_probe()
+        line["mfma_probe"] = probe
+        line["roofline"]["frac_of_probe"] = round(achieved / probe["tflops"], 4)
     if not args.no_other_workloads:
         others = {}
         for name, ow in ai.WORKLOADS.items():

@@ -1,4 +1,5 @@
-"""Build libfa.so (the C-ABI library) from csrc/ with hipcc for gfx950, in-tree.
+"""Build libfa.so (the C-ABI library) and libfa_probe.so (a matrix-core throughput probe used by bench.py)
+from csrc/ with hipcc for gfx950, in-tree.
 
     python exact_attention_13_amd/build.py
 
@@ -18,6 +19,8 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libfa.so"
 SOURCES = [CSRC / "fa_fwd_kernel.hip", CSRC / "fa_fwd_fp8_kernel.hip", CSRC / "fa_bwd_kernel.hip",
            CSRC / "fa_api.hip"]
+PROBE_LIB = PKG / "libfa_probe.so"
+PROBE_SOURCES = [CSRC / "fa_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -28,18 +31,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
 
 
-def compile_cmd(out: Path) -> list[str]:
+def compile_cmd(out: Path, sources: list[Path] = SOURCES) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 VALU instructions are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-function",
             f"-I{ROOT / 'include'}", f"-I{CSRC}",
-            *map(str, SOURCES), "-o", str(out)]
+            *map(str, sources), "-o", str(out)]
 
 
 def build(verbose: bool = False) -> Path:
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = compile_cmd(tmp)
+    """Build both libraries; returns the path of libfa.so."""
+    _build_one(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _build_one(LIB, SOURCES, verbose)
+
+
+def _build_one(lib: Path, sources: list[Path], verbose: bool) -> Path:
+    tmp = lib.with_suffix(".so.tmp")
+    cmd = compile_cmd(tmp, sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +59,8 @@ def build(verbose: bool = False) -> Path:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -32,6 +32,28 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(binding._lib, sym)
 
 
+def test_probe_library_exports_what_its_header_declares():
+    """libfa_probe.so (the matrix-core probe bench.py quotes the kernels against) is built beside libfa.so and
+    exports every function include/fa_probe.h declares; its argument checks run without a GPU."""
+    import ctypes
+    header = HEADER.parent / "fa_probe.h"
+    declared = sorted(set(re.findall(r"^(?:const\s+)?\w+\s*\**\s*(fa_probe_\w+)\s*\(", header.read_text(),
+                                     flags=re.M)))
+    assert declared == ["fa_probe_flop_per_wg_iter", "fa_probe_mfma_bf16", "fa_probe_threads"]
+    path = Path(fa.library_path()).parent / "libfa_probe.so"
+    out = subprocess.run(["nm", "-D", "--defined-only", str(path)], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert set(declared) <= exported
+    lib = ctypes.CDLL(str(path))
+    lib.fa_probe_flop_per_wg_iter.restype = ctypes.c_double
+    assert lib.fa_probe_flop_per_wg_iter() == 4 * 8 * 2 * 32 * 32 * 16
+    assert lib.fa_probe_threads() == 256
+    f = lib.fa_probe_mfma_bf16
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, A, 1, 1, None) == 1 and f(A, None, 1, 1, None) == 1
+    assert f(A, B_, 0, 1, None) == 2 and f(A, B_, 1, 0, None) == 2 and f(A, B_, (1 << 20) + 1, 1, None) == 2
+
+
 def test_version_and_strerror():
     assert fa.fa_version() == 10600
     for code in range(8):
