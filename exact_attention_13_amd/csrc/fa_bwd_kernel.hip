@@ -481,13 +481,15 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     lds_char* ps = pst + ((sb & 1) * 4 + pair) * kPSlotBytes;
     const int row0 = (t0 + it % per_head) * kDkdvTile;
     const lds_char* rows_src = pw ? qs : os;  // q rows for S, dO rows for dP
+    // all of the sub-block's A fragments are read before the first MFMA needs one
+    bf16x8 a[kDB];
+#pragma unroll
+    for (int kb = 0; kb < kDB; ++kb)
+      a[kb] = *(const __attribute__((address_space(3))) bf16x8*)(rows_src + 32 * sb * T::RB + row_off[kb]);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 x = (f32x16){};
 #pragma unroll
-    for (int kb = 0; kb < kDB; ++kb) {
-      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(rows_src + 32 * sb * T::RB + row_off[kb]);
-      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kvf[kb], x, 0, 0, 0);
-    }
-    schedule_reads_ahead<kDB>();
+    for (int kb = 0; kb < kDB; ++kb) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], kvf[kb], x, 0, 0, 0);
     const lds_char* tr_src = pw ? os : qs;    // dO^T for dV^T, q^T for dK^T
     if constexpr (pw) {
       const int qlo = row0 + 32 * sb;
