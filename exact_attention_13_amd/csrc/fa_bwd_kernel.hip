@@ -8,7 +8,7 @@
 //     dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i p_ij dO_i
 // (dk, dv summed over the query heads of a key/value group). Two kernels, neither with atomics, so every call
 // gives the same bits:
-//   * fa_bwd_dq_kernel: one workgroup per block of 128 query rows (4 waves x 32 rows), K/V tiles of 64 keys
+//   * fa_bwd_dq_kernel: one workgroup per block of 256 query rows (8 waves x 32 rows), K/V tiles of 64 keys
 //     streamed through LDS exactly like the forward. S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16
 //     put one query row in each lane, so p = exp2(s*c - lse*log2e) and dS^T = p (dP^T - D) need only the lane's
 //     own lse and D; dQ^T += K^T dS^T takes dS^T from registers as the B operand and K^T by transposing LDS reads
@@ -46,15 +46,15 @@
 
 namespace fa {
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32;                   // rows per wave: query rows (dq) or keys (dk, dv)
-constexpr int kBwdBlock = kBwdWaves * kBwdRows;  // rows per workgroup
+constexpr int kBwdBlock = 4 * kBwdRows;        // keys per dk/dv workgroup (4 wave pairs); workspace row granule
+constexpr int kDqWaves = 8;                    // dq kernel: waves per workgroup
+constexpr int kDqBlock = kDqWaves * kBwdRows;  // dq kernel: query rows per workgroup
 constexpr int kBwdTile = 64;                   // keys per LDS tile (dq)
 constexpr int kWsTileBytes = 1024;             // LDS slot for one tile of workspace values: 128 D, then 128 lse2
 
-// Workspace rows per head: N rounded up to the dq workgroup's 128 rows (its grid writes exactly these rows),
-// which is also a whole number of the dk/dv kernel's 128-row query tiles.
+// Workspace rows per head: N rounded up to 128, a whole number of the dk/dv kernel's 128-row query tiles. The dq
+// grid covers them all (padding rows included) and skips its own rows past them.
 __host__ __device__ constexpr int ws_rows(int N) { return (N + kBwdBlock - 1) / kBwdBlock * kBwdBlock; }
 
 template <int D, int ROWS = kBwdTile>
@@ -103,13 +103,13 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
 // dq (and the workspace values D_i, lse_i*log2e)
 // ------------------------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ o, const float* __restrict__ lse, const __bf16* __restrict__ dout,
     __bf16* __restrict__ dq, float* __restrict__ ws, int N, int BH, float scale, int group, int H,
     const int* __restrict__ kv_len, const int* __restrict__ cu_seqlens, int T_total) {
   using T = BwdTile<D>;
-  constexpr int NW = kBwdWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
+  constexpr int NW = kDqWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   lds_char* const kst = (lds_char*)smem_raw;  // 2 K stages
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   if (VARLEN && BH / H <= 64) {
     // packed batches: (sequence, query block) items in longest-first order (causal: the last blocks, which visit
     // the most key tiles, first)
-    const int nb = packed_blocks(cu_seqlens, BH / H, T_total, N, kBwdBlock);
+    const int nb = packed_blocks(cu_seqlens, BH / H, T_total, N, kDqBlock);
     int rank, hq, b, kb;
     map_packed(blockIdx.x + nq * blockIdx.y, H, group, rank, hq);
     if (!longest_first_item(rank, nb, CAUSAL, b, kb)) return;  // the whole workgroup: no item left
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     start = __builtin_amdgcn_readfirstlane(lo);
     Ns = __builtin_amdgcn_readfirstlane(min(hi - lo, N));  // no longer than max_seqlen (= N)
   }
-  const int q_lo = qb * kBwdBlock;
+  const int q_lo = qb * kDqBlock;
   if (VARLEN && q_lo >= Ns) return;  // the whole workgroup: no row of this block (nor its padding) exists
   const int hq = bh % H, Hkv = H / group;
   const int qpitch = VARLEN ? H * D : D;   // elements between consecutive rows of q, o, dO and dq
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const __bf16* vh = v + kv_off;
   const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bh / H], 0), N)) : Ns;
 
-  const int q_last = min(q_lo + kBwdBlock, Ns) - 1;
+  const int q_last = min(q_lo + kDqBlock, Ns) - 1;
   const int key_tiles = (Nk + kBwdTile - 1) / kBwdTile;
   const int n_tiles = CAUSAL ? min(q_last / kBwdTile + 1, key_tiles) : key_tiles;
   const int q0w = q_lo + wave * kBwdRows;
@@ -606,7 +606,8 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
   e = hipFuncSetAttribute((const void*)kb, hipFuncAttributeMaxDynamicSharedMemorySize, lds_b);
   if (e != hipSuccess) return e;
   const unsigned nblk = (unsigned)((N + kBwdBlock - 1) / kBwdBlock);
-  hipLaunchKernelGGL(ka, dim3(nblk, (unsigned)(B * H)), dim3(kBwdThreads), lds_a, stream, (const __bf16*)q,
+  const unsigned nblk_dq = (unsigned)((N + kDqBlock - 1) / kDqBlock);
+  hipLaunchKernelGGL(ka, dim3(nblk_dq, (unsigned)(B * H)), dim3(64 * kDqWaves), lds_a, stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse, (const __bf16*)dout, (__bf16*)dq, ws,
                      N, B * H, scale, group, H, kv_len, cu_seqlens, T_total);
   e = hipGetLastError();
