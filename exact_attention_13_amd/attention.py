@@ -219,3 +219,56 @@ def backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_bwd_varlen failed ({rc}): {binding.fa_strerror(rc)}")
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """o = attention(q, k, v) with the library's gradient kernels as its backward (bf16 only)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale, kv_len):
+        o, lse = forward(q, k, v, causal=causal, scale=scale, kv_len=kv_len)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale, ctx.kv_len = causal, scale, kv_len
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal, scale=ctx.scale,
+                              kv_len=ctx.kv_len)
+        return dq, dk, dv, None, None, None
+
+
+class _AttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, scale):
+        o, lse = forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
+        ctx.max_seqlen, ctx.causal, ctx.scale = max_seqlen, causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse, cu_seqlens = ctx.saved_tensors
+        dq, dk, dv = backward_varlen(q, k, v, o, lse, dout.contiguous(), cu_seqlens, ctx.max_seqlen,
+                                     causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: float | None = None,
+              kv_len: torch.Tensor | None = None) -> torch.Tensor:
+    """o of forward(q, k, v, causal, scale, kv_len) as a differentiable torch op: with q, k or v requiring grad,
+    o.backward(...) runs fa_bwd (fa_bwd_kpad with kv_len) and accumulates dq, dk, dv. Gradients need bf16 inputs;
+    fp32 inputs give a forward-only result."""
+    if q.dtype != torch.bfloat16 or not torch.is_grad_enabled() or not (q.requires_grad or k.requires_grad
+                                                                          or v.requires_grad):
+        return forward(q, k, v, causal=causal, scale=scale, kv_len=kv_len)[0]
+    return _Attention.apply(q, k, v, causal, scale, kv_len)
+
+
+def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                     causal: bool = False, scale: float | None = None) -> torch.Tensor:
+    """o of forward_varlen(...) as a differentiable torch op (backward: fa_bwd_varlen)."""
+    if not torch.is_grad_enabled() or not (q.requires_grad or k.requires_grad or v.requires_grad):
+        return forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=causal, scale=scale)[0]
+    return _AttentionVarlen.apply(q, k, v, cu_seqlens, max_seqlen, causal, scale)
