@@ -12,7 +12,7 @@
 //     streamed through LDS exactly like the forward. S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16
 //     put one query row in each lane, so p = exp2(s*c - lse*log2e) and dS^T = p (dP^T - D) need only the lane's
 //     own lse and D; dQ^T += K^T dS^T takes dS^T from registers as the B operand and K^T by transposing LDS reads
-//     (ds_read_b64_tr_b16). It also computes D_i from the o and dO rows it loads anyway and writes (D_i,
+//     (ds_read_b64_tr_b16). It also computes D_i from the o and dO rows it loads anyway and writes (-D_i,
 //     lse_i*log2e) to the workspace.
 //   * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys of one key/value head, 8 waves: each block of 32
 //     keys belongs to a pair of waves on one SIMD, one accumulating dV (from S and p), the other dK (from dP and
@@ -21,10 +21,11 @@
 //     put one key in each lane (K or V rows stay in registers as the B operand); dV^T += dO^T P and
 //     dK^T += Q^T dS take P and dS from registers as B operands and dO^T, Q^T by transposing LDS reads; p
 //     passes from the first wave of the pair to the second through LDS.
-// The workspace holds D_i and lse_i*log2e as two planes per head, [B*H][2][Npad] float, Npad = N rounded up to
-// 128; rows N .. Npad-1 hold D = 0 and lse2 = +inf, which makes p (and dS) of those rows exactly 0 in the dk/dv
+// The workspace holds -D_i and lse_i*log2e as two planes per head, [B*H][2][Npad] float, Npad = N rounded up to
+// 128; rows N .. Npad-1 hold 0 and lse2 = +inf, which makes p (and dS) of those rows exactly 0 in the dk/dv
 // kernel. With the planes apart, each wave of the dk/dv kernel reads from LDS only the plane it uses (the p wave
-// lse2, the dS wave D), half the bytes of reading interleaved pairs.
+// lse2, the dS wave -D), half the bytes of reading interleaved pairs; -D goes straight into the dS wave's dP
+// accumulators as their starting value, so the MFMAs leave dP - D with no subtraction.
 // Key padding (the forward's per-batch count Nk of valid keys, triton-transformer README usage example "ex. BERT"):
 // the dq kernel visits only the key tiles below Nk and masks keys >= Nk like the sequence end; the dk/dv kernel
 // masks them, loads no k or v row past Nk and writes zero gradients for them. With Nk = 0 no tile is visited
@@ -51,7 +52,7 @@ constexpr int kBwdBlock = 4 * kBwdRows;        // keys per dk/dv workgroup (4 wa
 constexpr int kDqWaves = 8;                    // dq kernel: waves per workgroup
 constexpr int kDqBlock = kDqWaves * kBwdRows;  // dq kernel: query rows per workgroup
 constexpr int kBwdTile = 64;                   // keys per LDS tile (dq)
-constexpr int kWsTileBytes = 1024;             // LDS slot for one tile of workspace values: 128 D, then 128 lse2
+constexpr int kWsTileBytes = 1024;             // LDS slot for one tile of workspace values: 128 -D, then 128 lse2
 
 // Workspace rows per head: N rounded up to 128, a whole number of the dk/dv kernel's 128-row query tiles. The dq
 // grid covers them all (padding rows included) and skips its own rows past them.
@@ -100,7 +101,7 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b) {
 }
 
 // ------------------------------------------------------------------------------------------------------------
-// dq (and the workspace values D_i, lse_i*log2e)
+// dq (and the workspace values -D_i, lse_i*log2e)
 // ------------------------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
   const int npad = ws_rows(N);
   if (my_q < npad && h == 0) {
     float* w = ws + (size_t)bh * 2 * npad + my_q;
-    w[0] = Di;
+    w[0] = -Di;  // stored negated: the dk/dv kernel starts its dP accumulators at -D
     w[npad] = lse2;
   }
 
@@ -481,13 +482,21 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     lds_char* ps = pst + ((sb & 1) * 4 + pair) * kPSlotBytes;
     const int row0 = (t0 + it % per_head) * kDkdvTile;
     const lds_char* rows_src = pw ? qs : os;  // q rows for S, dO rows for dP
-    // all of the sub-block's A fragments are read before the first MFMA needs one
+    // all of the sub-block's A fragments are read before the first MFMA needs one; the dS wave's accumulator starts
+    // at -D of its rows (value r <-> query row 32sb + 16(r/8) + 8h + r%8), so the MFMAs leave dP - D
     bf16x8 a[kDB];
 #pragma unroll
     for (int kb = 0; kb < kDB; ++kb)
       a[kb] = *(const __attribute__((address_space(3))) bf16x8*)(rows_src + 32 * sb * T::RB + row_off[kb]);
-    __builtin_amdgcn_sched_barrier(0);
     f32x16 x = (f32x16){};
+    if constexpr (!pw) {
+      const __attribute__((address_space(3))) f32x4* wp =
+          (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 8 * h) * 4);
+      const f32x4 w0 = wp[0], w1 = wp[1], w2 = wp[4], w3 = wp[5];  // rows +0..3, +4..7, +16..19, +20..23
+      x = (f32x16){w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
+                   w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < kDB; ++kb) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], kvf[kb], x, 0, 0, 0);
     const lds_char* tr_src = pw ? os : qs;    // dO^T for dV^T, q^T for dK^T
@@ -529,15 +538,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const bf16x8 pb = *(const __attribute__((address_space(3))) bf16x8*)(ps + (m * 64 + lane) * 16);
-        const __attribute__((address_space(3))) f32x4* wp =
-            (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 16 * m + 8 * h) * 4);
         f32x8 dsv;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f32x4 w = wp[u];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dsv[4 * u + e] = (float)pb[4 * u + e] * (x[8 * m + 4 * u + e] - w[e]);
-        }
+        for (int e = 0; e < 8; ++e) dsv[e] = (float)pb[e] * x[8 * m + e];
         const bf16x8 dsb = __builtin_convertvector(dsv, bf16x8);
         const int rbase = (32 * sb + 16 * m) * T::RB;
 #pragma unroll

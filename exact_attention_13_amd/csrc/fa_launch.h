@@ -32,7 +32,7 @@ hipError_t launch_bwd_varlen_bf16(const void* q, const void* k, const void* v, c
                                   const void* dout, void* dq, void* dk, void* dv, float* ws, const int* cu_seqlens,
                                   int B, int H, int Hkv, int T_total, int max_seqlen, int d, bool causal, float scale,
                                   hipStream_t stream);
-// Workspace of the gradient kernels: D_i and lse_i*log2e planes, [B*H][2][N rounded up to 128] float.
+// Workspace of the gradient kernels: -D_i and lse_i*log2e planes, [B*H][2][N rounded up to 128] float.
 inline size_t bwd_workspace_bytes(int B, int H, int N) {
   return (size_t)B * (size_t)H * (size_t)((N + 127) / 128 * 128) * 2 * sizeof(float);
 }
