@@ -99,7 +99,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale, int H, int group,
     const int* __restrict__ kv_len, const int* __restrict__ cu_seqlens, int T_total) {
   using T = Tile<D>;
-  constexpr int kThr = 64 * NW;
   constexpr int kBrW = NW * kRowsPerWave;        // query rows per workgroup
   constexpr int kDB = D / 16;                    // K-steps of the first product
   constexpr int kCB = D / 32;                    // 32-column blocks of the output
