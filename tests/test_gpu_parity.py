@@ -213,6 +213,29 @@ def test_empty_problem(fa):
     assert o.shape == (2, 4, 0, 64) and lse.shape == (2, 4, 0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_largest_head_count(fa, causal):
+    """B*H = 65535, the largest grid the ABI accepts (B*H is the grid's y extent), with short sequences: every row
+    of every head against the oracle, forward and gradients (the dq grid is also B*H high, the dk/dv grid B*H_kv)."""
+    B, H, N, d = 65535, 1, 3, 64
+    print(f"[case] B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+    q, k, v = ai.make_qkv(B, H, N, d, seed=120, dtype="bf16")
+    o, lse = _run(fa, q, k, v, causal, ai.default_scale(d))
+    _compare(o, lse, q, k, v, causal, ai.default_scale(d), "bf16", label=f"B*H=65535 causal={causal}")
+    g = torch.Generator("cpu").manual_seed(121)
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    qd, kd, vd, dd = (t.to("cuda:0") for t in (q, k, v, dout))
+    od, ld = fa.forward(qd, kd, vd, causal=causal)
+    grads = fa.backward(qd, kd, vd, od, ld, dd, causal=causal)
+    torch.cuda.synchronize()
+    refs = oracle.attention_bwd(q, k, v, dout, causal, ai.default_scale(d))
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        err = float(np.abs(got.double().cpu().numpy() - ref).max())
+        bound = 2e-2 * float(np.abs(ref).max()) + 1e-5
+        print(f"[parity] B*H=65535 {name} max|err|={err:.3e} bound {bound:.3e}", flush=True)
+        assert err <= bound, name
+
+
 def test_raw_entry_point_reports_errors(fa):
     q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
     o = torch.empty_like(q)
