@@ -214,6 +214,18 @@ def test_empty_problem(fa):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence(fa, causal):
+    """One head of N = 2^18 + 77 keys (a ragged last tile), d = 64: 192 seeded random rows plus the tile edges of
+    the first and last blocks against the oracle (each oracle row is a full 262221-key softmax)."""
+    B, H, N, d = 1, 1, (1 << 18) + 77, 64
+    print(f"[case] B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+    q, k, v = ai.make_qkv(B, H, N, d, seed=130, dtype="bf16")
+    o, lse = _run(fa, q, k, v, causal, ai.default_scale(d))
+    rows = np.unique(np.concatenate([ai.sample_rows(B, H, N, 192, 131), ai.edge_rows(N)]))
+    _compare(o, lse, q, k, v, causal, ai.default_scale(d), "bf16", rows=rows, label=f"N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_largest_head_count(fa, causal):
     """B*H = 65535, the largest grid the ABI accepts (B*H is the grid's y extent), with short sequences: every row
     of every head against the oracle, forward and gradients (the dq grid is also B*H high, the dk/dv grid B*H_kv)."""
