@@ -163,6 +163,27 @@ def test_varlen_backward_ragged(fa, lens, H, Hkv, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_varlen_many_sequences(fa, causal):
+    """100 sequences (more than the 64 the kernels order longest-first; past that they take the plain
+    workgroup order), lengths 0 .. 200 drawn at random: every row of the forward and every gradient row."""
+    rng = np.random.default_rng(940)
+    lens = [int(x) for x in rng.integers(0, 201, size=100)]
+    H, Hkv, d = 4, 2, 64
+    label = f"varlen 100 sequences (total {sum(lens)}) H{H} Hkv{Hkv} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v = ai.make_qkv_varlen(lens, H, d, seed=941, Hkv=Hkv)
+    scale = ai.default_scale(d)
+    o, lse = _run(fa, q, k, v, lens, causal, scale)
+    _compare(label, o, lse, q, k, v, lens, causal, scale)
+    dout = _dout_varlen(sum(lens), H, d, 942)
+    dq, dk, dv = _bwd(fa, q, k, v, dout, lens, causal, scale)
+    rq, rk, rv = oracle.attention_bwd_varlen(q, k, v, dout, [0] + list(np.cumsum(lens)), causal, scale)
+    _check_grad(f"{label} dq", dq, rq)
+    _check_grad(f"{label} dk", dk, rk)
+    _check_grad(f"{label} dv", dv, rv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_varlen_backward_medium(fa, causal):
     lens, H, Hkv, d = (700, 1, 1500, 333), 8, 2, 128
     label = f"bwd varlen lens={lens} H{H} Hkv{Hkv} d{d} causal={causal}"
