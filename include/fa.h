@@ -156,7 +156,10 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *   B, H, H_kv, N, d, causal, scale : as fa_fwd_gqa (same values as the forward call)
  * Enqueues two kernels on `stream` (dq, then dk and dv); no atomics, so the
  * same inputs give bitwise-identical gradients. p and dS are rounded to bf16
- * before their matrix products, the gradients once at the end. Errors as
+ * before their matrix products, the gradients once at the end. D_i is taken
+ * from the o given (bf16): its rounding moves dq_i by at most
+ * scale |dout_i . (o_i - o_exact_i)| max_j |k_j| (and dk alike), which shows
+ * where the gradients themselves are small (few keys, one dominant). Errors as
  * fa_fwd, with every tensor and the workspace checked (NULL, 16-byte
  * alignment) and no output (dq, dk, dv, workspace) allowed to overlap an
  * input or another output (FA_ERR_ALIAS).
