@@ -122,8 +122,14 @@ def kernel_name(w) -> str:
     c = "true" if w.causal else "false"
     if w.dtype != "bf16":
         return f"fa_fwd_f32_kernel<{w.d}, {c}>"
-    wide = ((w.N + 255) // 256) * w.B * w.H >= 512
-    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {'8, 2, 2' if wide else '4, 2, 1'}, false>"
+    bh = w.B * w.H
+    if ((w.N + 255) // 256) * bh >= 512:
+        shape = "8, 2, 2, false, 1"   # wide
+    elif ((w.N + 127) // 128) * bh >= 512:
+        shape = "4, 2, 1, false, 1"   # narrow
+    else:
+        shape = "8, 2, 2, false, 2"   # split keys
+    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {shape}>"
 
 
 def _device_inputs(w):

@@ -28,6 +28,11 @@
 //     (buffer_load ... lds) through a 2-stage ring: tile j+1 is copied while tile j is computed; one barrier per
 //     tile. The LDS layouts are XOR-swizzled so that the K fragment reads, the transposing V reads and the DMA
 //     writes are all free of bank conflicts.
+//   * Few query rows (the split shape, SPL = 2): each group of 32 rows gets two waves, which take the two 64-key
+//     halves of every 128-key tile with partial (m, l, O) of their own; at the end the second hands its partial
+//     to the first through LDS and the first merges them (the block-merge rule of the unite.ai page, "The Math
+//     Behind Flash Attention" item 2, in its corrected reading) and writes o and lse. Every SIMD then holds two
+//     waves even when the rows alone would give it one.
 //   * Causal: a workgroup visits only key tiles that meet its rows, a wave skips tiles entirely above its
 //     rows, and the mask is applied only on tiles that cross the diagonal or the sequence end.
 //   * The linear workgroup id is remapped so that (when B*H is a multiple of 8) every query block of a head
@@ -93,13 +98,15 @@ constexpr float kRescaleLog2 = 8.f;
 // bf16 kernel: NW waves x 32 query rows per workgroup, K/V tiles of KT x 64 keys (each 64-key part is one
 // swizzled Tile in LDS), ST-stage ring holding K and V of the same tile; every wave runs S_j, softmax,
 // O += P_j V_j.
-template <int D, bool CAUSAL, int NW, int ST, int KT, bool VARLEN>
+template <int D, bool CAUSAL, int NW, int ST, int KT, bool VARLEN, int SPL = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int N, int BH, float scale, int H, int group,
     const int* __restrict__ kv_len, const int* __restrict__ cu_seqlens, int T_total) {
   using T = Tile<D>;
-  constexpr int kBrW = NW * kRowsPerWave;        // query rows per workgroup
+  constexpr int kGroups = NW / SPL;              // row groups (SPL waves share a group's rows, splitting the keys)
+  constexpr int kBrW = kGroups * kRowsPerWave;   // query rows per workgroup
+  constexpr int kWKT = KT / SPL;                 // 64-key parts of each tile that one wave computes
   constexpr int kDB = D / 16;                    // K-steps of the first product
   constexpr int kCB = D / 32;                    // 32-column blocks of the output
   constexpr int kCopies = T::kInsts / NW;        // copy instructions per wave per tensor per 64-key part
@@ -109,6 +116,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
   static_assert(ST == 2 || ST == 3, "pipeline depth");
   static_assert(KT == 1 || KT == 2, "tile width");
+  static_assert((SPL == 1 || SPL == 2) && KT % SPL == 0 && NW % SPL == 0, "key split");
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   lds_char* const smem = (lds_char*)smem_raw;
   lds_char* const kst = smem;                    // ST K stages
@@ -162,11 +170,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int q_last = min(q_lo + kBrW, Ns) - 1;             // last real query row of the workgroup
   const int key_tiles = (Nk + kBcT - 1) / kBcT;             // tiles holding valid keys
   const int n_tiles = CAUSAL ? min(q_last / kBcT + 1, key_tiles) : key_tiles;
-  const int q0w = q_lo + wave * kRowsPerWave;               // first query row of this wave
+  const int kpart = wave / kGroups;                         // which part of each tile's keys this wave takes
+  const int kofs = kpart * kWKT * kBc;                         // ... as an offset of keys into the tile
+  const int q0w = q_lo + (wave % kGroups) * kRowsPerWave;   // first query row of this wave
   const int my_q = q0w + l32;                               // query row of this lane
   // Tiles j < wave_tiles hold at least one key visible to this wave's rows.
   const int wave_tiles =
-      (q0w >= Ns) ? 0 : (CAUSAL ? min(n_tiles, (q0w + kRowsPerWave - 1) / kBcT + 1) : n_tiles);
+      (q0w >= Ns) ? 0
+                  : (CAUSAL ? (q0w + kRowsPerWave - 1 < kofs ? 0
+                                                             : min(n_tiles, (q0w + kRowsPerWave - 1 - kofs) / kBcT + 1))
+                            : n_tiles);
 
   // ---- Q fragments: lane holds q[my_q][16*kb + 8*h .. +7] (B operand of S^T = K Q^T)
   bf16x8 qf[kDB];
@@ -233,13 +246,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   int v_base[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    v_base[cb] = (int)(size_t)(vst + v_off[cb]);
+    v_base[cb] = (int)(size_t)(vst + kpart * kWKT * T::kBytes + v_off[cb]);
     asm volatile("" : "+v"(v_base[cb]));
   }
   int k_base[kDB];
 #pragma unroll
   for (int kb = 0; kb < kDB; ++kb) {
-    k_base[kb] = (int)(size_t)(kst + k_off[kb]);
+    k_base[kb] = (int)(size_t)(kst + kpart * kWKT * T::kBytes + k_off[kb]);
     asm volatile("" : "+v"(k_base[kb]));
   }
 
@@ -252,9 +265,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // S^T = K_j Q^T from the K stage at byte `kat` (2KT blocks of 32 keys; block b = rows 32(b%2).. of part b/2).
   // s[b][r] is the score of query my_q and key j*64KT + 32b + 16(r/8) + 8h + r%8.
-  auto qk = [&](f32x16(&s)[2 * KT], int kat) __attribute__((always_inline)) {
+  auto qk = [&](f32x16(&s)[2 * kWKT], int kat) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < 2 * KT; ++b) {
+    for (int b = 0; b < 2 * kWKT; ++b) {
       s[b] = (f32x16){};
 #pragma unroll
       for (int kb = 0; kb < kDB; ++kb) {
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // then one MFMA per further read, so each K fragment is read ~4 MFMAs before it is used.
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * KT * kDB - 4; ++i) {
+    for (int i = 0; i < 2 * kWKT * kDB - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -276,11 +289,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // Mask (only tiles that cross the diagonal or the end of the valid keys), row max and (rarely) the move of
   // the exponent reference, for tile j held in s.
-  auto stats = [&](f32x16(&s)[2 * KT], int j) __attribute__((always_inline)) {
-    const int kv0 = j * kBcT;
-    if ((kv0 + kBcT > Nk) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
+  auto stats = [&](f32x16(&s)[2 * kWKT], int j) __attribute__((always_inline)) {
+    const int kv0 = j * kBcT + kofs;  // first key of this wave's part of tile j
+    if ((kv0 + kWKT * kBc > Nk) || (CAUSAL && kv0 + kWKT * kBc - 1 > q0w)) {
 #pragma unroll
-      for (int b = 0; b < 2 * KT; ++b)
+      for (int b = 0; b < 2 * kWKT; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
@@ -290,7 +303,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     float mx = s[0][0];
 #pragma unroll
-    for (int b = 0; b < 2 * KT; ++b)
+    for (int b = 0; b < 2 * kWKT; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
     mx = pair_max32(mx);  // row max over this tile's keys
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // P = exp2(s*c2 - m_ref*c2) and O^T += V^T P^T from the V stage at byte `vat`, one 16-key step m at a time:
   // the 8 exponentials of step m+1 can run on the vector ALU while the MFMAs of step m run, and the V fragments
   // of step m+1 are read during step m. Lane slot 8h+e of step m <-> key j*64KT + 16m + 8h + e.
-  auto softmax_pv = [&](f32x16(&s)[2 * KT], int vat) __attribute__((always_inline)) {
+  auto softmax_pv = [&](f32x16(&s)[2 * kWKT], int vat) __attribute__((always_inline)) {
     const float nb = -m_ref * c2;
     float rs[2] = {0.f, 0.f};
     auto read_v = [&](int m, bf16x8(&vf)[kCB]) __attribute__((always_inline)) {
@@ -326,7 +339,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bf16x8 vfa[kCB], vfb[kCB];
     read_v(0, vfa);
 #pragma unroll
-    for (int m = 0; m < 4 * KT; ++m) {
+    for (int m = 0; m < 4 * kWKT; ++m) {
       bf16x8(&vcur)[kCB] = (m & 1) ? vfb : vfa;
       bf16x8(&vnxt)[kCB] = (m & 1) ? vfa : vfb;
       f32x8 x = (m & 1) ? s[m >> 1].hi : s[m >> 1].lo;
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       rs[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), kOnes2, rs[1], false);
       rs[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), kOnes2, rs[0], false);
       rs[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), kOnes2, rs[1], false);
-      if (m < 4 * KT - 1) read_v(m + 1, vnxt);
+      if (m < 4 * kWKT - 1) read_v(m + 1, vnxt);
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb)
         oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[cb], pf, oacc[cb], 0, 0, 0);
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     l_run += rs[0] + rs[1];
   };
 
-  f32x16 s[2 * KT];
+  f32x16 s[2 * kWKT];
   {
     // One tile: start copying tile j+ST-1 into the stage tile j-1 used (every wave finished it before the last
     // barrier), compute tile j, wait for this wave's copies of tile j+1, barrier.
@@ -393,7 +406,42 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // ---- epilogue: o = acc / l once per row, lse = m*scale + ln l. l >= 1 whenever a key is visible (the weight
   // of the maximum is >= 1); l == 0 only for a row without visible keys: o = 0, lse = -inf.
-  const float l_tot = pair_sum32(l_run);
+  float l_tot = pair_sum32(l_run);
+  if constexpr (SPL == 2) {
+    // The two waves of a row group hold partial (m, l, O) over the two halves of every tile's keys; the second
+    // hands its partial to the first through LDS (the ring is free: every wave passed the last tile's barrier),
+    // which merges them with the block-merge rule. A partial without visible keys (l = 0) has no maximum.
+    constexpr int kSlot = 64 * 16 * 4 * kCB + 2 * 64 * 4;  // O (4 kCB f32x4 per lane), then m and l per lane
+    lds_char* const slot = smem + (wave % kGroups) * kSlot;
+    if (kpart == 1) {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(__attribute__((address_space(3))) f32x4*)(slot + ((cb * 4 + g) * 64 + lane) * 16) =
+              (f32x4){oacc[cb][4 * g], oacc[cb][4 * g + 1], oacc[cb][4 * g + 2], oacc[cb][4 * g + 3]};
+      *(__attribute__((address_space(3))) float*)(slot + 16 * 64 * 4 * kCB + lane * 4) = m_ref;
+      *(__attribute__((address_space(3))) float*)(slot + 16 * 64 * 4 * kCB + 256 + lane * 4) = l_tot;
+    }
+    wait_copies_and_barrier<0>();
+    if (kpart == 1) return;  // the first wave of the group writes the row group's o and lse
+    const float m1 = *(const __attribute__((address_space(3))) float*)(slot + 16 * 64 * 4 * kCB + lane * 4);
+    const float l1 = *(const __attribute__((address_space(3))) float*)(slot + 16 * 64 * 4 * kCB + 256 + lane * 4);
+    const float m0e = l_tot > 0.f ? m_ref : -INFINITY, m1e = l1 > 0.f ? m1 : -INFINITY;
+    const float mm = fmaxf(m0e, m1e);
+    const float m_use = (mm == -INFINITY) ? 0.f : mm;
+    const float a0 = __builtin_amdgcn_exp2f((m0e - m_use) * c2), a1 = __builtin_amdgcn_exp2f((m1e - m_use) * c2);
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 w = *(const __attribute__((address_space(3))) f32x4*)(slot + ((cb * 4 + g) * 64 + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[cb][4 * g + e] = oacc[cb][4 * g + e] * a0 + w[e] * a1;
+      }
+    l_tot = l_tot * a0 + l1 * a1;
+    m_ref = m_use;
+  }
   if (my_q < Ns) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* orow = o + head_off + (size_t)my_q * qpitch;
@@ -560,13 +608,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(const float* __res
 // ------------------------------------------------------------------------------------------------------------
 // launchers (arguments already validated by the C ABI layer)
 // ------------------------------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, int NW, int ST, int KT, bool VARLEN = false>
+template <int D, bool CAUSAL, int NW, int ST, int KT, bool VARLEN = false, int SPL = 1>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                               float scale, int H, int group, const int* kv_len, hipStream_t stream,
                               const int* cu_seqlens = nullptr, int T_total = 0) {
   constexpr int lds = 2 * ST * KT * Tile<D>::kBytes;
-  constexpr int rows = NW * kRowsPerWave;
-  auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST, KT, VARLEN>;
+  constexpr int rows = NW / SPL * kRowsPerWave;
+  auto kern = fa_fwd_bf16_kernel<D, CAUSAL, NW, ST, KT, VARLEN, SPL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)BH);
@@ -587,24 +635,38 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
   return hipGetLastError();
 }
 
-// Workgroup shape: 8 waves (256 rows, one workgroup per CU, 128-key tiles, 2-stage ring) when the grid has at
-// least two such workgroups per CU of an MI355X (256 CUs); otherwise 4 waves (128 rows, two workgroups per CU,
-// 64-key tiles, 2-stage ring), which doubles the workgroups of short sequences. The two differ in where the
-// exponent reference may move and in the order of the row sums, so their outputs can differ in the last bit;
-// each is deterministic.
-constexpr long long kWideGridMin = 512;
+// Workgroup shape, from the number of query rows to spread over the 256 CUs of an MI355X:
+//  * wide: 8 waves x 32 rows (256 rows, 128-key tiles, one workgroup per CU) when the grid has at least two such
+//    workgroups per CU;
+//  * narrow: 4 waves x 32 rows (128 rows, 64-key tiles, two workgroups per CU) when it has at least two of those
+//    per CU;
+//  * split: otherwise (too few rows to give every SIMD two waves of 32 rows): 8 waves x 128 rows, the two waves
+//    of each 32-row group taking the two 64-key halves of every 128-key tile and merging their partial (m, l, O)
+//    at the end. Short sequences of few heads (and long ones of very few) get two waves per SIMD this way.
+// The three differ in where the exponent reference may move and in the order of the sums, so their outputs can
+// differ in the last bit; each is deterministic, and the packed entry point chooses the same way from max_seqlen.
+constexpr long long kTwoPerCu = 512;
+enum class Shape { kWide, kNarrow, kSplit };
+static Shape fwd_shape(int N, int BH) {
+  if ((long long)((N + 255) / 256) * BH >= kTwoPerCu) return Shape::kWide;
+  if ((long long)((N + 127) / 128) * BH >= kTwoPerCu) return Shape::kNarrow;
+  return Shape::kSplit;
+}
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                            int N, int d, bool causal, float scale, const int* kv_len, hipStream_t stream) {
   const int BH = B * H, group = H / Hkv;
-  const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
-#define FA_LAUNCH(D, C, NW, KT) launch_bf16<D, C, NW, 2, KT>(q, k, v, o, lse, BH, N, scale, H, group, kv_len, stream)
-  if (wide) {
-    if (d == 64) return causal ? FA_LAUNCH(64, true, 8, 2) : FA_LAUNCH(64, false, 8, 2);
-    return causal ? FA_LAUNCH(128, true, 8, 2) : FA_LAUNCH(128, false, 8, 2);
+#define FA_LAUNCH(D, C, NW, KT, SPL) \
+  launch_bf16<D, C, NW, 2, KT, false, SPL>(q, k, v, o, lse, BH, N, scale, H, group, kv_len, stream)
+#define FA_D(NW, KT, SPL)                                                                        \
+  (d == 64 ? (causal ? FA_LAUNCH(64, true, NW, KT, SPL) : FA_LAUNCH(64, false, NW, KT, SPL)) \
+           : (causal ? FA_LAUNCH(128, true, NW, KT, SPL) : FA_LAUNCH(128, false, NW, KT, SPL)))
+  switch (fwd_shape(N, BH)) {
+    case Shape::kWide: return FA_D(8, 2, 1);
+    case Shape::kNarrow: return FA_D(4, 1, 1);
+    default: return FA_D(8, 2, 2);
   }
-  if (d == 64) return causal ? FA_LAUNCH(64, true, 4, 1) : FA_LAUNCH(64, false, 4, 1);
-  return causal ? FA_LAUNCH(128, true, 4, 1) : FA_LAUNCH(128, false, 4, 1);
+#undef FA_D
 #undef FA_LAUNCH
 }
 
@@ -612,15 +674,18 @@ hipError_t launch_fwd_varlen_bf16(const void* q, const void* k, const void* v, v
                                   const int* cu_seqlens, int B, int H, int Hkv, int T_total, int max_seqlen, int d,
                                   bool causal, float scale, hipStream_t stream) {
   const int BH = B * H, group = H / Hkv, N = max_seqlen;
-  const bool wide = (long long)((N + 255) / 256) * BH >= kWideGridMin;
-#define FA_LAUNCH(D, C, NW, KT) \
-  launch_bf16<D, C, NW, 2, KT, true>(q, k, v, o, lse, BH, N, scale, H, group, nullptr, stream, cu_seqlens, T_total)
-  if (wide) {
-    if (d == 64) return causal ? FA_LAUNCH(64, true, 8, 2) : FA_LAUNCH(64, false, 8, 2);
-    return causal ? FA_LAUNCH(128, true, 8, 2) : FA_LAUNCH(128, false, 8, 2);
+#define FA_LAUNCH(D, C, NW, KT, SPL)                                                                                 \
+  launch_bf16<D, C, NW, 2, KT, true, SPL>(q, k, v, o, lse, BH, N, scale, H, group, nullptr, stream, cu_seqlens, \
+                                          T_total)
+#define FA_D(NW, KT, SPL)                                                                        \
+  (d == 64 ? (causal ? FA_LAUNCH(64, true, NW, KT, SPL) : FA_LAUNCH(64, false, NW, KT, SPL)) \
+           : (causal ? FA_LAUNCH(128, true, NW, KT, SPL) : FA_LAUNCH(128, false, NW, KT, SPL)))
+  switch (fwd_shape(N, BH)) {
+    case Shape::kWide: return FA_D(8, 2, 1);
+    case Shape::kNarrow: return FA_D(4, 1, 1);
+    default: return FA_D(8, 2, 2);
   }
-  if (d == 64) return causal ? FA_LAUNCH(64, true, 4, 1) : FA_LAUNCH(64, false, 4, 1);
-  return causal ? FA_LAUNCH(128, true, 4, 1) : FA_LAUNCH(128, false, 4, 1);
+#undef FA_D
 #undef FA_LAUNCH
 }
 

@@ -261,12 +261,15 @@ def test_raw_entry_point_reports_errors(fa):
 
 @pytest.mark.parametrize("d,causal", [(64, False), (128, True)])
 def test_both_workgroup_shapes(fa, d, causal):
-    """4x32 heads at N=1024 launch the 8-wave instance (256-row workgroups, 128-key tiles); the first 32 heads
-    alone launch the 4-wave instance (128-row workgroups, 64-key tiles). Both must match the oracle, and each
-    is deterministic run to run."""
+    """4x32 heads at N=1024 launch the wide instance (8 waves, 256-row workgroups, 128-key tiles); the first 2x32
+    heads the narrow one (4 waves, 128-row workgroups, 64-key tiles); the first 32 heads alone the split one (8
+    waves on 128 rows, two waves per 32-row group splitting every 128-key tile and merging at the end). All must
+    match the oracle on the first batch, and each is deterministic run to run."""
     q, k, v = (t.cuda() for t in ai.make_qkv(4, 32, 1024, d, seed=110, dtype="bf16"))
     rows = ai.sample_rows(1, 32, 1024, 300, seed=110)
-    for qq, kk, vv, label in ((q, k, v, "wide"), (q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(), "narrow")):
+    cases = [(q[:nb].contiguous(), k[:nb].contiguous(), v[:nb].contiguous(), label)
+             for nb, label in ((4, "wide"), (2, "narrow"), (1, "split"))]
+    for qq, kk, vv, label in cases:
         o1, l1 = fa.forward(qq, kk, vv, causal=causal)
         o2, l2 = fa.forward(qq, kk, vv, causal=causal)
         torch.cuda.synchronize()
