@@ -13,6 +13,9 @@ namespace {
 constexpr int kVersion = 10600;  // 1.6.0
 constexpr long long kMaxHeads = 65535;   // B*H is the grid's y extent
 constexpr long long kMaxN = 1LL << 30;
+// The gradient kernels read the workspace's two planes of one head through a 32-bit byte range and offset
+// (2 x 4 bytes per row), so their sequence length stays well below 2^29.
+constexpr long long kMaxNBwd = 1LL << 28;
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
@@ -75,7 +78,7 @@ int validate_bwd(const void* const* in, int n_in, void* const* out, int n_out, c
     return FA_OK;
   }
   if (Hkv == 0 || H % Hkv != 0) return FA_ERR_SHAPE;
-  if ((long long)B * H > kMaxHeads || N > kMaxN) return FA_ERR_SHAPE;
+  if ((long long)B * H > kMaxHeads || N > kMaxNBwd) return FA_ERR_SHAPE;
   for (int i = 0; i < n_in; ++i)
     if (!in[i]) return FA_ERR_NULL;
   for (int i = 0; i < n_out; ++i)
@@ -153,7 +156,7 @@ int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   if (B == 0 || H == 0 || total == 0) return FA_OK;
   if (max_seqlen == 0 || max_seqlen > total) return FA_ERR_SHAPE;
   if (Hkv == 0 || H % Hkv != 0) return FA_ERR_SHAPE;
-  if ((long long)B * H > kMaxHeads || total > kMaxN) return FA_ERR_SHAPE;
+  if ((long long)B * H > kMaxHeads || total > kMaxN || max_seqlen > kMaxNBwd) return FA_ERR_SHAPE;
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
   for (const void* x : ptrs) {
     if (!x) return FA_ERR_NULL;

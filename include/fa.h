@@ -50,7 +50,8 @@ extern "C" {
 
 #define FA_OK 0
 #define FA_ERR_NULL 1    /* a pointer is NULL (non-empty problem) */
-#define FA_ERR_SHAPE 2   /* B, H, N or H_kv negative; B*H over 65535; N over 2^30; H_kv not dividing H */
+#define FA_ERR_SHAPE 2   /* B, H, N or H_kv negative; B*H over 65535; N over 2^30 (gradient calls: 2^28);
+                            H_kv not dividing H */
 #define FA_ERR_HEADDIM 3 /* d is not 64 or 128 */
 #define FA_ERR_ALIGN 4   /* a tensor or the workspace not 16-byte aligned, or lse / kv_len not 4-byte aligned */
 #define FA_ERR_ARG 5     /* scale not finite or not > 0, or causal not 0/1 */
@@ -153,7 +154,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *                16-byte aligned, overwritten (no contents needed on entry
  *                or kept on return); calls that share a workspace must be
  *                ordered on one stream
- *   B, H, H_kv, N, d, causal, scale : as fa_fwd_gqa (same values as the forward call)
+ *   B, H, H_kv, N, d, causal, scale : as fa_fwd_gqa (same values as the forward call);
+ *                N at most 2^28 (FA_ERR_SHAPE otherwise)
  * Enqueues two kernels on `stream` (dq, then dk and dv); no atomics, so the
  * same inputs give bitwise-identical gradients. p and dS are rounded to bf16
  * before their matrix products, the gradients once at the end. D_i is taken
@@ -195,7 +197,8 @@ int fa_bwd_kpad(const void* q, const void* k, const void* v, const void* o, cons
  *   workspace      : fa_bwd_workspace_bytes(B, H, max_seqlen) bytes, 16-byte
  *                    aligned, as for fa_bwd
  *   cu_seqlens, B, H, H_kv, total, max_seqlen, d, causal, scale : as
- *                    fa_fwd_varlen (offsets clamped on the device the same way)
+ *                    fa_fwd_varlen (offsets clamped on the device the same way);
+ *                    max_seqlen at most 2^28 (FA_ERR_SHAPE otherwise)
  * Errors as fa_fwd_varlen, with every tensor, lse, cu_seqlens and the
  * workspace checked (NULL, alignment) and no output (dq, dk, dv, workspace)
  * allowed to overlap an input or another output (FA_ERR_ALIAS). Deterministic

@@ -156,6 +156,8 @@ def test_backward_error_codes():
     assert _bwd(d=96) == fa.FA_ERR_HEADDIM
     assert _bwd(H_kv=3) == fa.FA_ERR_SHAPE
     assert _bwd(N=-1) == fa.FA_ERR_SHAPE
+    # the workspace planes are addressed with 32-bit byte offsets: 2^28 rows at most
+    assert _bwd(N=(1 << 28) + 1) == fa.FA_ERR_SHAPE
     assert _bwd(scale=0.0) == fa.FA_ERR_ARG
     assert _bwd(causal=3) == fa.FA_ERR_ARG
     assert _bwd(dq=BWD["q"]) == fa.FA_ERR_ALIAS                  # dq is q
@@ -182,6 +184,7 @@ def test_backward_kpad_error_codes():
     assert _bwd_kpad(kv_len=BWD["dk"] + 64) == fa.FA_ERR_ALIAS     # lengths inside dk
     assert _bwd_kpad(kv_len=BWD["ws"] + 16) == fa.FA_ERR_ALIAS     # lengths inside the workspace
     assert _bwd_kpad(H_kv=3) == fa.FA_ERR_SHAPE
+    assert _bwd_kpad(N=(1 << 28) + 1) == fa.FA_ERR_SHAPE
     assert _bwd_kpad(d=80) == fa.FA_ERR_HEADDIM
     assert _bwd_kpad(causal=2) == fa.FA_ERR_ARG
     assert _bwd_kpad(N=0, kv_len=0, **{name: 0 for name in BWD}) == fa.FA_OK
@@ -220,6 +223,7 @@ def test_varlen_backward_error_codes():
         assert bv(**{name: P[name] + 8}) == fa.FA_ERR_ALIGN, name
     assert bv(cu=P["cu"] + 2) == fa.FA_ERR_ALIGN and bv(lse=P["lse"] + 2) == fa.FA_ERR_ALIGN
     assert bv(max_seqlen=101) == fa.FA_ERR_SHAPE and bv(Hkv=3) == fa.FA_ERR_SHAPE
+    assert bv(total=(1 << 28) + 5, max_seqlen=(1 << 28) + 1) == fa.FA_ERR_SHAPE
     assert bv(dq=P["q"]) == fa.FA_ERR_ALIAS and bv(ws=P["cu"] - 16) == fa.FA_ERR_ALIAS
     assert bv(dk=P["dv"] + 64) == fa.FA_ERR_ALIAS
     assert bv(total=0, **{name: 0 for name in P}) == fa.FA_OK
