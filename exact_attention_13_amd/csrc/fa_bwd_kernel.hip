@@ -474,31 +474,39 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   // the dS wave through the pair's LDS slot (sb % 2) in exactly that register layout. The role is a compile-time
   // parameter: each role runs a loop of its own (with the same barriers), so the accumulators are not merged
   // across role branches inside the loop.
-  auto sub_block = [&](int it, int S, int sb, auto role_c) __attribute__((always_inline)) {
+  // The operands a sub-block needs first, read one sub-block ahead: the A fragments of its first product (q rows
+  // for the p wave, dO rows for the dS wave) and four f32x4 of the workspace (lse2 of its rows for the p wave,
+  // -D for the dS wave; value group g <-> rows 32sb + 8h + {0..3, 4..7, 16..19, 20..23}[g]).
+  auto read_pre = [&](int S, int sb, auto role_c, bf16x8 (&a)[kDB], f32x4 (&w)[4]) __attribute__((always_inline)) {
     constexpr bool pw = decltype(role_c)::value;
-    const lds_char* qs = qst + S * T::kBytes;
-    const lds_char* os = dst + S * T::kBytes;
-    const lds_char* wsl = wst + S * kWsTileBytes;
-    lds_char* ps = pst + ((sb & 1) * 4 + pair) * kPSlotBytes;
-    const int row0 = (t0 + it % per_head) * kDkdvTile;
-    const lds_char* rows_src = pw ? qs : os;  // q rows for S, dO rows for dP
-    // all of the sub-block's A fragments are read before the first MFMA needs one; the dS wave's accumulator starts
-    // at -D of its rows (value r <-> query row 32sb + 16(r/8) + 8h + r%8), so the MFMAs leave dP - D
-    bf16x8 a[kDB];
+    const lds_char* rows_src = (pw ? qst : dst) + S * T::kBytes;
 #pragma unroll
     for (int kb = 0; kb < kDB; ++kb)
       a[kb] = *(const __attribute__((address_space(3))) bf16x8*)(rows_src + 32 * sb * T::RB + row_off[kb]);
+    const __attribute__((address_space(3))) f32x4* wp =
+        (const __attribute__((address_space(3))) f32x4*)(wst + S * kWsTileBytes + (pw ? 512 : 0) +
+                                                         (32 * sb + 8 * h) * 4);
+    w[0] = wp[0];
+    w[1] = wp[1];
+    w[2] = wp[4];
+    w[3] = wp[5];
+  };
+  auto sub_block = [&](int it, int S, int sb, auto role_c, const bf16x8 (&a)[kDB], const f32x4 (&w)[4],
+                       bf16x8 (&a_nx)[kDB], f32x4 (&w_nx)[4]) __attribute__((always_inline)) {
+    constexpr bool pw = decltype(role_c)::value;
+    const lds_char* qs = qst + S * T::kBytes;
+    const lds_char* os = dst + S * T::kBytes;
+    lds_char* ps = pst + ((sb & 1) * 4 + pair) * kPSlotBytes;
+    const int row0 = (t0 + it % per_head) * kDkdvTile;
     f32x16 x = (f32x16){};
-    if constexpr (!pw) {
-      const __attribute__((address_space(3))) f32x4* wp =
-          (const __attribute__((address_space(3))) f32x4*)(wsl + (32 * sb + 8 * h) * 4);
-      const f32x4 w0 = wp[0], w1 = wp[1], w2 = wp[4], w3 = wp[5];  // rows +0..3, +4..7, +16..19, +20..23
-      x = (f32x16){w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3],
-                   w2[0], w2[1], w2[2], w2[3], w3[0], w3[1], w3[2], w3[3]};
-    }
+    if constexpr (!pw)
+      x = (f32x16){w[0][0], w[0][1], w[0][2], w[0][3], w[1][0], w[1][1], w[1][2], w[1][3],
+                   w[2][0], w[2][1], w[2][2], w[2][3], w[3][0], w[3][1], w[3][2], w[3][3]};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < kDB; ++kb) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], kvf[kb], x, 0, 0, 0);
+    if (sb + 1 < kSub) read_pre(S, sb + 1, role_c, a_nx, w_nx);
+    __builtin_amdgcn_sched_barrier(0);
     const lds_char* tr_src = pw ? os : qs;    // dO^T for dV^T, q^T for dK^T
     if constexpr (pw) {
       const int qlo = row0 + 32 * sb;
@@ -512,17 +520,12 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        // lse2 of query rows 32sb + 16m + 8h .. +7 of the tile
-        const __attribute__((address_space(3))) f32x4* wp =
-            (const __attribute__((address_space(3))) f32x4*)(wsl + 512 + (32 * sb + 16 * m + 8 * h) * 4);
         f32x8 pv;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f32x4 w = wp[u];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            pv[4 * u + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * m + 4 * u + e], c2, -w[e]));
-        }
+            pv[4 * u + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * m + 4 * u + e], c2, -w[2 * m + u][e]));
         const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
         *(__attribute__((address_space(3))) bf16x8*)(ps + (m * 64 + lane) * 16) = pb;
         const int rbase = (32 * sb + 16 * m) * T::RB;
@@ -561,12 +564,17 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     wait_copies_and_barrier<0>();
   }
   auto run = [&](auto role_c) __attribute__((always_inline)) {
+    static_assert(kSub % 2 == 0, "sub-blocks alternate between two operand sets");
     for (int it = 0; it < n_iter; ++it) {
       const int S = it & 1;
+      bf16x8 a0[kDB], a1[kDB];
+      f32x4 w0[4], w1[4];
+      read_pre(S, 0, role_c, a0, w0);
 #pragma unroll
-      for (int sb = 0; sb < kSub; ++sb) {
-        sub_block(it, S, sb, role_c);
+      for (int sb = 0; sb < kSub; sb += 2) {
+        sub_block(it, S, sb, role_c, a0, w0, a1, w1);
         if (sb == 0) copy_iter(min(it + 1, n_iter - 1), S ^ 1);
+        sub_block(it, S, sb + 1, role_c, a1, w1, a0, w0);
       }
       wait_copies_and_barrier<0>();
     }
