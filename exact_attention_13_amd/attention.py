@@ -38,6 +38,23 @@ def _check(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
         raise ValueError("q, k, v must be on the same device")
 
 
+def _resolve_stream(stream: int | None, device: torch.device) -> tuple[int, torch.cuda.Stream | None]:
+    """The raw stream handle to launch on, and (when it is not torch's current stream) a torch handle of it for
+    record_stream: memory this module allocates belongs to the current stream, so tensors used by a kernel on
+    another stream are recorded on that stream and are not reused before the kernel has finished."""
+    with torch.cuda.device(device):
+        cur = torch.cuda.current_stream()
+        if stream is None or int(stream) == cur.cuda_stream:
+            return cur.cuda_stream, None
+        return int(stream), torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _record(foreign: torch.cuda.Stream | None, *tensors: torch.Tensor) -> None:
+    if foreign is not None:
+        for t in tensors:
+            t.record_stream(foreign)
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: float | None = None,
             out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream: int | None = None,
             kv_len: torch.Tensor | None = None):
@@ -59,9 +76,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
-    if stream is None:
-        with torch.cuda.device(q.device):
-            stream = torch.cuda.current_stream().cuda_stream
+    stream, foreign = _resolve_stream(stream, q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
     c, sc, st = int(bool(causal)), float(scale), int(stream)
     with torch.cuda.device(q.device):
@@ -75,6 +90,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
             rc = binding.fa_fwd_f32(*ptrs, B, H, N, d, c, sc, st)
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_fwd failed ({rc}): {binding.fa_strerror(rc)}")
+    _record(foreign, out, lse)
     return out, lse
 
 
@@ -108,9 +124,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     ws = torch.empty((max(binding.fa_bwd_workspace_bytes(B, H, N), 16),), dtype=torch.uint8, device=q.device)
+    stream, foreign = _resolve_stream(stream, q.device)
     with torch.cuda.device(q.device):
-        if stream is None:
-            stream = torch.cuda.current_stream().cuda_stream
         ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
         tail = (B, H, H_kv, N, d, int(bool(causal)), float(scale), int(stream))
@@ -120,6 +135,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             rc = binding.fa_bwd(*ptrs, *tail)
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_bwd failed ({rc}): {binding.fa_strerror(rc)}")
+    _record(foreign, dq, dk, dv, ws)
     return dq, dk, dv
 
 
@@ -140,14 +156,14 @@ def forward_fp8(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, q_scale: flo
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream, foreign = _resolve_stream(stream, q.device)
     with torch.cuda.device(q.device):
-        if stream is None:
-            stream = torch.cuda.current_stream().cuda_stream
         rc = binding.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                 float(q_scale), float(k_scale), float(v_scale), B, H, N, d, int(bool(causal)),
                                 float(scale), int(stream))
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_fwd_fp8 failed ({rc}): {binding.fa_strerror(rc)}")
+    _record(foreign, o, lse)
     return o, lse
 
 
@@ -174,14 +190,14 @@ def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    stream, foreign = _resolve_stream(stream, q.device)
     with torch.cuda.device(q.device):
-        if stream is None:
-            stream = torch.cuda.current_stream().cuda_stream
         rc = binding.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                    cu_seqlens.data_ptr(), B, H, k.shape[1], total, int(max_seqlen), d,
                                    int(bool(causal)), float(scale), int(stream))
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_fwd_varlen failed ({rc}): {binding.fa_strerror(rc)}")
+    _record(foreign, o, lse)
     return o, lse
 
 
@@ -196,8 +212,10 @@ def backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
             raise ValueError(f"{name} must be a contiguous bf16 3-d GPU tensor")
     total, H, d = q.shape
     if o.shape != q.shape or dout.shape != q.shape or k.shape != v.shape or k.shape[0] != total \
-            or k.shape[2] != d or H % k.shape[1] != 0:
+            or k.shape[2] != d or k.shape[1] < 1 or H % k.shape[1] != 0:
         raise ValueError("q, o, dout [total,H,d] and k, v [total,H_kv,d] disagree")
+    if any(t.device != q.device for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must be on the same device")
     if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [H, total] tensor on q's device")
     if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
@@ -209,15 +227,15 @@ def backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty((max(binding.fa_bwd_workspace_bytes(B, H, int(max_seqlen)), 16),), dtype=torch.uint8,
                      device=q.device)
+    stream, foreign = _resolve_stream(stream, q.device)
     with torch.cuda.device(q.device):
-        if stream is None:
-            stream = torch.cuda.current_stream().cuda_stream
         rc = binding.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                                    cu_seqlens.data_ptr(), B, H, k.shape[1], total, int(max_seqlen), d,
                                    int(bool(causal)), float(scale), int(stream))
     if rc != binding.FA_OK:
         raise RuntimeError(f"fa_bwd_varlen failed ({rc}): {binding.fa_strerror(rc)}")
+    _record(foreign, dq, dk, dv, ws)
     return dq, dk, dv
 
 

@@ -93,3 +93,37 @@ def test_autograd_against_fp64_definition(fa):
     for name, got, ref in (("dq", qg.grad, q64.grad), ("dk", kg.grad, k64.grad), ("dv", vg.grad, v64.grad)):
         err = (got.double().cpu() - ref).abs().max().item()
         assert err <= 2e-2 * ref.abs().max().item() + 1e-5, (name, err)
+
+
+def test_calls_on_an_explicit_stream(fa):
+    """forward/backward (and the packed variants) given another stream run there and give the current stream's
+    results bit for bit; the workspace and outputs they allocate stay reserved for that stream, so memory taken
+    on the current stream meanwhile does not disturb the running kernels."""
+    B, H, N, d = 2, 4, 300, 128
+    q, k, v, dout = (t.cuda() for t in _inputs(B, H, 2, N, d, seed=83))
+    print(f"[stream] B={B} H={H} Hkv=2 N={N} d={d} causal=True", flush=True)
+    o_ref, lse_ref = fa.forward(q, k, v, causal=True)
+    g_ref = fa.backward(q, k, v, o_ref, lse_ref, dout, causal=True)
+    lens = [300, 1, 170]
+    cu = torch.tensor([0, 300, 301, 471], dtype=torch.int32, device="cuda")
+    qv, kv, vv, dv_ = (torch.cat([t[0].transpose(0, 1), t[1].transpose(0, 1)[:sum(lens) - N]]).contiguous()
+                       for t in (q, k, v, dout))
+    ov_ref, lsev_ref = fa.forward_varlen(qv, kv, vv, cu, max(lens), causal=True)
+    gv_ref = fa.backward_varlen(qv, kv, vv, ov_ref, lsev_ref, dv_, cu, max(lens), causal=True)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    st = side.cuda_stream
+    o, lse = fa.forward(q, k, v, causal=True, stream=st)
+    g = fa.backward(q, k, v, o_ref, lse_ref, dout, causal=True, stream=st)
+    ov, lsev = fa.forward_varlen(qv, kv, vv, cu, max(lens), causal=True, stream=st)
+    gv = fa.backward_varlen(qv, kv, vv, ov_ref, lsev_ref, dv_, cu, max(lens), causal=True, stream=st)
+    junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]  # allocations on the current stream
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    assert all(torch.equal(a, b) for a, b in zip(g, g_ref))
+    assert torch.equal(ov, ov_ref) and torch.equal(lsev, lsev_ref)
+    assert all(torch.equal(a, b) for a, b in zip(gv, gv_ref))
