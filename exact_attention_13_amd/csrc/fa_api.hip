@@ -271,7 +271,8 @@ const char* fa_strerror(int code) {
     case FA_ERR_NULL: return "a tensor, lse, kv_len, cu_seqlens or workspace pointer is NULL";
     case FA_ERR_SHAPE:
       return "bad shape: B, H, N must be >= 0, B*H <= 65535, N <= 2^30, H_kv >= 1 dividing H "
-             "(fp8: N a multiple of 16, at most 2^24; packed: 1 <= max_seqlen <= total <= 2^30)";
+             "(fp8: N a multiple of 16, at most 2^24; packed: 1 <= max_seqlen <= total <= 2^30; gradient calls: "
+             "N and max_seqlen at most 2^28)";
     case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
     case FA_ERR_ALIGN:
       return "misaligned pointer: tensors and the workspace need 16-byte alignment, lse, kv_len and cu_seqlens "
