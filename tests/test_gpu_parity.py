@@ -278,3 +278,31 @@ def test_both_workgroup_shapes(fa, d, causal):
         _compare(o1[:1].float().cpu().numpy().astype(np.float64), l1[:1].cpu().numpy().astype(np.float64),
                  q[:1].cpu(), k[:1].cpu(), v[:1].cpu(), causal, ai.default_scale(d), "bf16", rows=rows,
                  label=f"{label} grid d={d} causal={causal}")
+
+
+def test_split_shape_edges(fa):
+    """The split instance (grids too small for two waves per SIMD) where the second key half of every tile sees no
+    key (kv_len 40 < 64, so that wave's partial has l = 0 and must drop out of the merge), with grouped heads and a
+    ragged tail; and one long causal head (N = 16389) at sampled rows and the tile edges."""
+    B, H, Hkv, N, d = 2, 4, 2, 777, 128
+    g = torch.Generator("cpu").manual_seed(121)
+    q = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, N, d), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, N, d), generator=g).to(torch.bfloat16)
+    lens = [40, 700]
+    print(f"[case] split grid B={B} H={H} Hkv={Hkv} N={N} d={d} kv_len={lens}", flush=True)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), scale=ai.default_scale(d),
+                        kv_len=torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    _compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), q, k, v, False,
+             ai.default_scale(d), "bf16", label="split grid, key padding", kv_len=lens)
+
+    N = 16389
+    print(f"[case] split grid one causal head N={N} d={d}", flush=True)
+    g = torch.Generator("cpu").manual_seed(122)
+    q, k, v = (torch.randn((1, 1, N, d), generator=g).to(torch.bfloat16) for _ in range(3))
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([ai.sample_rows(1, 1, N, 256, seed=122), ai.edge_rows(N, 256, 128)]))
+    _compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), q, k, v, True,
+             ai.default_scale(d), "bf16", rows=rows, label="split grid, one causal head")
