@@ -54,7 +54,8 @@ KERNEL_SRC = ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_kernel.hip"
 KERNEL_SRCS = (KERNEL_SRC, ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
 BWD_SRCS = (ROOT / "exact_attention_13_amd" / "csrc" / "fa_bwd_kernel.hip",
             ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
-BWD_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal", "kpad_bf16_b8h16n4096d128")
+BWD_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal", "kpad_bf16_b8h16n4096d128",
+                 "mqa_bf16_b1h32kv1n16384d128_causal")
 FP8_WORKLOADS = ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal")  # the same shapes, fp8 inputs
 FP8_SRCS = (ROOT / "exact_attention_13_amd" / "csrc" / "fa_fwd_fp8_kernel.hip",
             ROOT / "exact_attention_13_amd" / "csrc" / "fa_gfx950.h")
@@ -203,7 +204,7 @@ def time_backward(w, steps: int, warmup: int):
     fwd = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
     fwd()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((fa.fa_bwd_workspace_bytes(w.B, w.H, w.N),), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(w.B, w.H, w.Hk, w.N, w.d),), dtype=torch.uint8, device="cuda")
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
             dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
     tail = (w.B, w.H, w.Hk, w.N, w.d, int(w.causal), w.scale, stream.cuda_stream)
@@ -347,7 +348,7 @@ def varlen_backward_record(w, steps: int, warmup: int):
     g = torch.Generator("cpu").manual_seed(w.seed + 500)
     dout = torch.randn(tuple(q.shape), generator=g).to(torch.bfloat16).cuda()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((fa.fa_bwd_workspace_bytes(w.B, w.H, w.max_len),), dtype=torch.uint8, device="cuda")
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(w.B, w.H, w.Hk, w.max_len, w.d),), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
             dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), cu.data_ptr(), w.B, w.H, w.Hk, w.T, w.max_len, w.d,

@@ -123,7 +123,8 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    ws = torch.empty((max(binding.fa_bwd_workspace_bytes(B, H, N), 16),), dtype=torch.uint8, device=q.device)
+    ws = torch.empty((max(binding.fa_bwd_workspace_bytes(B, H, H_kv, N, d), 16),), dtype=torch.uint8,
+                     device=q.device)
     stream, foreign = _resolve_stream(stream, q.device)
     with torch.cuda.device(q.device):
         ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
@@ -225,8 +226,8 @@ def backward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty((max(binding.fa_bwd_workspace_bytes(B, H, int(max_seqlen)), 16),), dtype=torch.uint8,
-                     device=q.device)
+    ws_bytes = binding.fa_bwd_workspace_bytes(B, H, k.shape[1], int(max_seqlen), d)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=q.device)
     stream, foreign = _resolve_stream(stream, q.device)
     with torch.cuda.device(q.device):
         rc = binding.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),

@@ -52,7 +52,7 @@ _lib.fa_bwd_kpad.argtypes = [_P] * 11 + [_I] * 6 + [ctypes.c_float, _P]
 _lib.fa_bwd_varlen.restype = _I
 _lib.fa_bwd_varlen.argtypes = [_P] * 11 + [_I] * 7 + [ctypes.c_float, _P]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-_lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.fa_fwd_f32.restype = _I
 _lib.fa_fwd_f32.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 _lib.fa_strerror.restype = ctypes.c_char_p
@@ -99,7 +99,7 @@ def fa_fwd_fp8(q: int, k: int, vt: int, o: int, lse: int, q_scale: float, k_scal
 def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, workspace: int, B: int,
            H: int, H_kv: int, N: int, d: int, causal: int, scale: float, stream: int) -> int:
     """Raw entry point: gradients dq [B,H,N,d], dk, dv [B,H_kv,N,d] (bf16) of the forward for upstream dout;
-    workspace: fa_bwd_workspace_bytes(B, H, N) bytes of device memory."""
+    workspace: fa_bwd_workspace_bytes(B, H, H_kv, N, d) bytes of device memory."""
     return _lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H_kv, N, d, causal, scale, stream)
 
 
@@ -113,13 +113,14 @@ def fa_bwd_kpad(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk
 def fa_bwd_varlen(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, workspace: int,
                   cu_seqlens: int, B: int, H: int, H_kv: int, total: int, max_seqlen: int, d: int, causal: int,
                   scale: float, stream: int) -> int:
-    """Raw entry point: gradients of fa_fwd_varlen; workspace of fa_bwd_workspace_bytes(B, H, max_seqlen) bytes."""
+    """Raw entry point: gradients of fa_fwd_varlen; workspace of fa_bwd_workspace_bytes(B, H, H_kv, max_seqlen,
+    d) bytes."""
     return _lib.fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, B, H, H_kv, total,
                               max_seqlen, d, causal, scale, stream)
 
 
-def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
-    return int(_lib.fa_bwd_workspace_bytes(B, H, N))
+def fa_bwd_workspace_bytes(B: int, H: int, H_kv: int, N: int, d: int) -> int:
+    return int(_lib.fa_bwd_workspace_bytes(B, H, H_kv, N, d))
 
 
 def fa_fwd_f32(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int, d: int, causal: int,

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 10600;  // 1.6.0
+constexpr int kVersion = 10700;  // 1.7.0
 constexpr long long kMaxHeads = 65535;   // B*H is the grid's y extent
 constexpr long long kMaxN = 1LL << 30;
 // The gradient kernels read the workspace's two planes of one head through a 32-bit byte range and offset
@@ -105,7 +105,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   // byte ranges: q, o, dout, dq are [B,H,N,d]; k, v, dk, dv are [B,H_kv,N,d]; lse [B,H,N]; kv_len [B]; the
   // workspace
   const size_t tq = (size_t)B * H * N * d * 2, tk = (size_t)B * H_kv * N * d * 2, tl = (size_t)B * H * N * 4;
-  const size_t tw = fa::bwd_workspace_bytes(B, H, N);
+  const size_t tw = fa::bwd_workspace_bytes(B, H, H_kv, N, d);
   const void* rin[] = {q, k, v, o, dout, lse, kv_len};
   const size_t nin[] = {tq, tk, tk, tq, tq, tl, with_len ? (size_t)B * sizeof(int) : 0};
   void* rout[] = {dq, dk, dv, workspace};
@@ -165,7 +165,7 @@ int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
   if (!lse || !cu_seqlens) return FA_ERR_NULL;
   if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return FA_ERR_ALIGN;
   const size_t tq = (size_t)total * H * d * 2, tk = (size_t)total * Hkv * d * 2, tl = (size_t)total * H * 4;
-  const size_t tw = fa::bwd_workspace_bytes(B, H, max_seqlen), tc = (size_t)(B + 1) * sizeof(int);
+  const size_t tw = fa::bwd_workspace_bytes(B, H, Hkv, max_seqlen, d), tc = (size_t)(B + 1) * sizeof(int);
   const void* rin[] = {q, k, v, o, dout, lse, cu_seqlens};
   const size_t nin[] = {tq, tk, tk, tq, tq, tl, tc};
   void* rout[] = {dq, dk, dv, workspace};
@@ -226,9 +226,9 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
                         causal, scale, stream);
 }
 
-size_t fa_bwd_workspace_bytes(int B, int H, int N) {
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return fa::bwd_workspace_bytes(B, H, N);
+size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || H_kv <= 0 || H % H_kv != 0 || (d != 64 && d != 128)) return 0;
+  return fa::bwd_workspace_bytes(B, H, H_kv, N, d);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, float q_scale, float k_scale,

@@ -349,12 +349,16 @@ constexpr int kPSlotBytes = 2 * 64 * 16;  // p of one 32 x 32 sub-block, bf16, a
 // Waves w and w+4 run on the same SIMD and own the same 32 keys: the p wave (w < 4) computes S = Q K^T, p and
 // dV^T += dO^T P; the dS wave computes dP = dO V^T, then (after the sub-block's barrier) dS = p (dP - D) from the
 // p the other wave left in LDS, and dK^T += Q^T dS. Each holds half the accumulators, so two waves share a SIMD.
+// With nsplit > 1, the grid's y extent is BHkv * nsplit: workgroup part z of a key block visits only query heads
+// z*group/nsplit .. (z+1)*group/nsplit - 1 of the group and writes its dk and dv in fp32 to part
+// ([2][nsplit][BHkv][N][D]: dk, then dv) for fa_bwd_reduce_kernel. The parts of one key block are handed out
+// together, so the longest-first order of causal blocks holds over all of them.
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ ws, __bf16* __restrict__ dk,
     __bf16* __restrict__ dv, int N, int BHkv, float scale, int group, int Hkv, const int* __restrict__ kv_len,
-    const int* __restrict__ cu_seqlens, int T_total) {
+    const int* __restrict__ cu_seqlens, int T_total, float* __restrict__ part, int nsplit) {
   using T = BwdTile<D, kDkdvTile>;
   constexpr int NW = kDkdvWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   constexpr int kSub = kDkdvTile / kBwdRows;  // 32-row sub-blocks per query tile
@@ -370,20 +374,24 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const bool pw = wave < 4;
   const int pair = wave & 3;
   const int nk = gridDim.x;
-  int bkv, kblk;
+  int bkv, kblk, zs;
   const int nbatch = BHkv / Hkv;
   if (VARLEN && nbatch <= 64) {
-    // packed batches: consecutive workgroups are the Hkv heads of one (sequence, key block) item (so a head stays
-    // on one XCD when Hkv is a multiple of 8), items in longest-first order
+    // packed batches: consecutive workgroups are the Hkv heads (times the nsplit parts) of one (sequence, key
+    // block) item (so a head stays on one XCD when Hkv is a multiple of 8), items in longest-first order
     const int nb = packed_blocks(cu_seqlens, nbatch, T_total, N, kBwdBlock);
     const int lin = blockIdx.x + nk * blockIdx.y;
     int b, kb;
-    if (!longest_first_item(lin / Hkv, nb, CAUSAL, b, kb)) return;  // the whole workgroup: no item left
-    bkv = __builtin_amdgcn_readfirstlane(b * Hkv + lin % Hkv);
+    if (!longest_first_item(lin / (Hkv * nsplit), nb, CAUSAL, b, kb)) return;  // the whole workgroup: no item left
+    const int u = lin % (Hkv * nsplit);
+    bkv = __builtin_amdgcn_readfirstlane(b * Hkv + u % Hkv);
+    zs = __builtin_amdgcn_readfirstlane(u / Hkv);
     kblk = __builtin_amdgcn_readfirstlane(kb);
   } else {
-    int t;
-    map_workgroup(blockIdx.x + nk * blockIdx.y, nk, BHkv, 1, CAUSAL, bkv, t);
+    int t, u;
+    map_workgroup(blockIdx.x + nk * blockIdx.y, nk, BHkv * nsplit, 1, CAUSAL, u, t);
+    bkv = u % BHkv;
+    zs = u / BHkv;
     // causal: the first key blocks see the most query rows; map_workgroup hands out the last index first
     kblk = CAUSAL ? nk - 1 - t : t;
   }
@@ -401,7 +409,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const int kpitch = VARLEN ? Hkv * D : D;  // ... of k, v, dk and dv
   const int qpitch_b = 2 * qpitch;
   const size_t kv_off = VARLEN ? ((size_t)start * Hkv + bkv % Hkv) * D : (size_t)bkv * (size_t)N * D;
-  const int bh0 = bkv * group;  // first query head (of B*H) of this key/value head's group
+  const int gsub = group / nsplit;                      // query heads this workgroup visits
+  const int bh0 = bkv * group + zs * gsub;  // the first of them (of B*H)
   const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bkv / Hkv], 0), N)) : Ns;
 
   const int kw0 = k0 + pair * kBwdRows;
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const int nqt = (Ns + kDkdvTile - 1) / kDkdvTile;
   const int t0 = CAUSAL ? kblk : 0;
   const int per_head = nqt - t0;
-  const int n_iter = (k0 < Nk) ? group * per_head : 0;  // a block of padded keys only writes zeros
+  const int n_iter = (k0 < Nk) ? gsub * per_head : 0;  // a block of padded keys only writes zeros
   const int npad = ws_rows(N);
   auto copy_iter = [&](int it, int S) __attribute__((always_inline)) {
     const int hq = bh0 + it / per_head;
@@ -587,15 +596,65 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
 
   // dk_j = scale * dK^T, dv_j = dV^T; [cb][4g + i] is column 32cb + 8g + 4h + i of key row my_k (0 past Nk)
   if (my_k < Ns) {
-    __bf16* row = (pw ? dv : dk) + kv_off + (size_t)my_k * kpitch;
     const float f = (my_k < Nk) ? (pw ? 1.f : scale) : 0.f;
+    if (nsplit == 1) {
+      __bf16* row = (pw ? dv : dk) + kv_off + (size_t)my_k * kpitch;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
+      for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 a = {acc[cb][4 * g] * f, acc[cb][4 * g + 1] * f, acc[cb][4 * g + 2] * f, acc[cb][4 * g + 3] * f};
-        *(bf16x4*)(row + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(a, bf16x4);
-      }
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 a = {acc[cb][4 * g] * f, acc[cb][4 * g + 1] * f, acc[cb][4 * g + 2] * f,
+                           acc[cb][4 * g + 3] * f};
+          *(bf16x4*)(row + 32 * cb + 8 * g + 4 * h) = __builtin_convertvector(a, bf16x4);
+        }
+    } else {
+      float* row = part + ((((size_t)(pw ? 1 : 0) * nsplit + zs) * BHkv + bkv) * N + my_k) * D;
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(row + 32 * cb + 8 * g + 4 * h) = (f32x4){acc[cb][4 * g] * f, acc[cb][4 * g + 1] * f,
+                                                             acc[cb][4 * g + 2] * f, acc[cb][4 * g + 3] * f};
+    }
+  }
+}
+
+// Sums the nsplit partial dk and dv of a head-split dk/dv launch in split order and writes them in bf16: one thread
+// per 8 columns of one key row of one key/value head (rows past a packed sequence's end are not written, as in the
+// unsplit kernel).
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* __restrict__ part, int nsplit,
+                                                           __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N,
+                                                           int BHkv, int Hkv, const int* __restrict__ cu_seqlens,
+                                                           int T_total) {
+  constexpr int kTpr = D / 8;  // threads per row
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t rows = (size_t)BHkv * N;
+  if (t >= rows * kTpr) return;
+  const size_t r = t / kTpr;
+  const int c0 = (int)(t % kTpr) * 8;
+  const int bkv = (int)(r / N), i = (int)(r % N);
+  size_t out;
+  if constexpr (VARLEN) {
+    const int lo = min(max(cu_seqlens[bkv / Hkv], 0), T_total);
+    const int hi = min(max(cu_seqlens[bkv / Hkv + 1], lo), T_total);
+    if (i >= min(hi - lo, N)) return;
+    out = ((size_t)(lo + i) * Hkv + bkv % Hkv) * D + c0;
+  } else {
+    out = r * D + c0;
+  }
+  const size_t stride = rows * D;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const float* src = part + (size_t)which * nsplit * stride + r * D + c0;
+    f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+    for (int sp = 1; sp < nsplit; ++sp) {
+      a += *(const f32x4*)(src + sp * stride);
+      b += *(const f32x4*)(src + sp * stride + 4);
+    }
+    __bf16* dst = (which ? dv : dk) + out;
+    *(bf16x4*)dst = __builtin_convertvector(a, bf16x4);
+    *(bf16x4*)(dst + 4) = __builtin_convertvector(b, bf16x4);
   }
 }
 
@@ -623,9 +682,18 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
                      N, B * H, scale, group, H, kv_len, cu_seqlens, T_total);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv)), dim3(64 * kDkdvWaves), lds_b, stream, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const float*)ws, (__bf16*)dk,
-                     (__bf16*)dv, N, B * Hkv, scale, group, Hkv, kv_len, cu_seqlens, T_total);
+  const int nsplit = bwd_head_split(B, H, Hkv, N);
+  float* part = nsplit > 1 ? (float*)((char*)ws + bwd_planes_bytes(B, H, N)) : nullptr;
+  hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv * nsplit)), dim3(64 * kDkdvWaves), lds_b, stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const float*)ws,
+                     (__bf16*)dk, (__bf16*)dv, N, B * Hkv, scale, group, Hkv, kv_len, cu_seqlens, T_total, part,
+                     nsplit);
+  if (nsplit == 1) return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t threads = (size_t)B * Hkv * N * (D / 8);
+  hipLaunchKernelGGL((fa_bwd_reduce_kernel<D, VARLEN>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     (const float*)part, nsplit, (__bf16*)dk, (__bf16*)dv, N, B * Hkv, Hkv, cu_seqlens, T_total);
   return hipGetLastError();
 }
 

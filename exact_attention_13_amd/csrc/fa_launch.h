@@ -21,20 +21,37 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           bool causal, float scale, hipStream_t stream);
 // Enqueue the two gradient kernels (dq and the workspace values, then dk and dv). Arguments must already be valid
 // (d is 64 or 128, B, H, N >= 1, Hkv >= 1 dividing H, pointers device-resident and aligned, ws of
-// bwd_workspace_bytes(B, H, N) bytes); kv_len as launch_fwd_bf16 (the forward's lengths); returns the launch
+// bwd_workspace_bytes(B, H, Hkv, N, d) bytes); kv_len as launch_fwd_bf16 (the forward's lengths); returns the launch
 // status.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int H, int Hkv, int N,
                            int d, bool causal, float scale, const int* kv_len, hipStream_t stream);
 // The gradient kernels on packed variable-length batches (layout of launch_fwd_varlen_bf16; dq as q, dk and dv
-// as k); ws of bwd_workspace_bytes(B, H, max_seqlen) bytes.
+// as k); ws of bwd_workspace_bytes(B, H, Hkv, max_seqlen, d) bytes.
 hipError_t launch_bwd_varlen_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                   const void* dout, void* dq, void* dk, void* dv, float* ws, const int* cu_seqlens,
                                   int B, int H, int Hkv, int T_total, int max_seqlen, int d, bool causal, float scale,
                                   hipStream_t stream);
-// Workspace of the gradient kernels: -D_i and lse_i*log2e planes, [B*H][2][N rounded up to 128] float.
-inline size_t bwd_workspace_bytes(int B, int H, int N) {
+// The dk/dv kernel runs one workgroup per (128-key block, key/value head) and visits the H/Hkv query heads of the
+// head's group in turn. When that grid would give fewer than two workgroups per CU (256 CUs), the group's query
+// heads are divided over `split` workgroups (the smallest divisor of the group that reaches 512 workgroups, else
+// the whole group): each writes fp32 partial dk and dv, and a reduction kernel sums them in split order.
+inline int bwd_head_split(int B, int H, int Hkv, int N) {
+  const int group = H / Hkv;
+  const long long wgs = (long long)((N + 127) / 128) * B * Hkv;
+  for (int s = 1; s < group; ++s)
+    if (group % s == 0 && wgs * s >= 512) return s;
+  return group;
+}
+// Workspace of the gradient kernels: -D_i and lse_i*log2e planes, [B*H][2][N rounded up to 128] float; then,
+// with a head split s > 1, the partial dk and dv, [2][s][B*Hkv][N][d] float.
+inline size_t bwd_planes_bytes(int B, int H, int N) {
   return (size_t)B * (size_t)H * (size_t)((N + 127) / 128 * 128) * 2 * sizeof(float);
+}
+inline size_t bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  const int s = bwd_head_split(B, H, Hkv, N);
+  const size_t parts = s > 1 ? 2 * (size_t)s * B * Hkv * (size_t)N * d * sizeof(float) : 0;
+  return bwd_planes_bytes(B, H, N) + parts;
 }
 }  // namespace fa
 #endif

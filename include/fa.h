@@ -150,13 +150,14 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *   lse        : const float [B,H,N] (device), fa_fwd's lse for the same call
  *   dq         : bf16 [B,H,N,d] (device, written)
  *   dk, dv     : bf16 [B,H_kv,N,d] (device, written)
- *   workspace  : device memory of fa_bwd_workspace_bytes(B, H, N) bytes,
+ *   workspace  : device memory of fa_bwd_workspace_bytes(B, H, H_kv, N, d) bytes,
  *                16-byte aligned, overwritten (no contents needed on entry
  *                or kept on return); calls that share a workspace must be
  *                ordered on one stream
  *   B, H, H_kv, N, d, causal, scale : as fa_fwd_gqa (same values as the forward call);
  *                N at most 2^28 (FA_ERR_SHAPE otherwise)
- * Enqueues two kernels on `stream` (dq, then dk and dv); no atomics, so the
+ * Enqueues two kernels on `stream` (dq, then dk and dv; a third that sums
+ * partial dk and dv when the workspace holds them); no atomics, so the
  * same inputs give bitwise-identical gradients. p and dS are rounded to bf16
  * before their matrix products, the gradients once at the end. D_i is taken
  * from the o given (bf16): its rounding moves dq_i by at most
@@ -194,7 +195,7 @@ int fa_bwd_kpad(const void* q, const void* k, const void* v, const void* o, cons
  *   q, o, dout, dq : [total, H, d] bf16 (dq written); k, v, dk, dv :
  *                    [total, H_kv, d] bf16 (dk, dv written); lse : float
  *                    [H, total] from fa_fwd_varlen with the same arguments
- *   workspace      : fa_bwd_workspace_bytes(B, H, max_seqlen) bytes, 16-byte
+ *   workspace      : fa_bwd_workspace_bytes(B, H, H_kv, max_seqlen, d) bytes, 16-byte
  *                    aligned, as for fa_bwd
  *   cu_seqlens, B, H, H_kv, total, max_seqlen, d, causal, scale : as
  *                    fa_fwd_varlen (offsets clamped on the device the same way);
@@ -208,9 +209,13 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
                   void* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens, int B, int H, int H_kv,
                   int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream);
 
-/* fa_bwd_workspace_bytes -- bytes of the fa_bwd / fa_bwd_kpad workspace for N (fa_bwd_varlen: N = max_seqlen);
- * 0 for an empty problem. */
-size_t fa_bwd_workspace_bytes(int B, int H, int N);
+/* fa_bwd_workspace_bytes -- bytes of the fa_bwd / fa_bwd_kpad workspace (fa_bwd_varlen: N = max_seqlen); 0 for
+ * an empty problem or arguments the gradient calls reject (H_kv not dividing H, d not 64 or 128). It holds two
+ * float planes per query row (-D_i and lse_i log2 e; 8 bytes a row), and, when the key/value heads alone give
+ * the dk/dv kernel fewer than two workgroups per compute unit (few heads of a grouped-query call), the fp32
+ * partial dk and dv of the workgroups that share a group's query heads between them (2 x s x B x H_kv x N x d
+ * floats, s dividing H / H_kv), summed in a fixed order by a third kernel. */
+size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d);
 
 /*
  * fa_fwd_fp8 -- the attention forward of fp8 inputs with per-tensor scales

@@ -55,7 +55,7 @@ def test_probe_library_exports_what_its_header_declares():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() == 10600
+    assert fa.fa_version() == 10700
     for code in range(8):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
@@ -246,11 +246,20 @@ def test_fp8_error_codes():
 
 
 def test_backward_workspace_bytes():
+    ws = fa.fa_bwd_workspace_bytes
     # (D, lse*log2e) float pairs per query row, rows rounded up to 128 per head
-    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 128 * 8
-    assert fa.fa_bwd_workspace_bytes(1, 1, 64) == 128 * 8
-    assert fa.fa_bwd_workspace_bytes(1, 32, 16384) == 32 * 16384 * 8
-    assert fa.fa_bwd_workspace_bytes(0, 3, 100) == 0 and fa.fa_bwd_workspace_bytes(1, 1, -5) == 0
+    assert ws(2, 3, 3, 100, 64) == 2 * 3 * 128 * 8
+    assert ws(1, 1, 1, 64, 128) == 128 * 8
+    assert ws(1, 32, 32, 16384, 128) == 32 * 16384 * 8
+    # grouped heads whose key/value heads already give 512 dk/dv workgroups (2 x 8 heads x 32 key blocks): no split
+    assert ws(2, 32, 8, 4096, 128) == 2 * 32 * 4096 * 8
+    # one key/value head of 16384 keys: 128 workgroups, so the 32 query heads split 4 ways (the smallest divisor
+    # reaching 512), each way with fp32 partial dk and dv of every key row
+    assert ws(1, 32, 1, 16384, 128) == 32 * 16384 * 8 + 2 * 4 * 16384 * 128 * 4
+    # a tiny grid splits the whole group (2 heads per key/value head): 2 partials
+    assert ws(1, 4, 2, 100, 64) == 4 * 128 * 8 + 2 * 2 * 2 * 100 * 64 * 4
+    assert ws(0, 3, 3, 100, 64) == 0 and ws(1, 1, 1, -5, 64) == 0
+    assert ws(1, 4, 3, 100, 64) == 0 and ws(1, 4, 0, 100, 64) == 0 and ws(1, 4, 4, 100, 96) == 0
 
 
 def test_python_wrapper_rejects_cpu_tensors():

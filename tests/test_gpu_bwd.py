@@ -86,7 +86,7 @@ def test_backward_grouped_heads(fa, Hkv, d, causal):
     _full(fa, 2, 8, Hkv, 333, d, causal, 450 + Hkv, label)
 
 
-@pytest.mark.parametrize("H,Hkv,causal", [(16, 16, False), (16, 16, True), (16, 4, True)])
+@pytest.mark.parametrize("H,Hkv,causal", [(16, 16, False), (16, 16, True), (16, 4, True), (16, 1, True)])
 def test_backward_large_sampled_rows(fa, H, Hkv, causal):
     """B2 N2048 d128: 192 dq rows and 192 dk/dv rows of four heads, plus the first and last rows."""
     B, N, d = 2, 2048, 128
@@ -108,6 +108,29 @@ def test_backward_large_sampled_rows(fa, H, Hkv, causal):
     _check(f"{label} dq", dq.reshape(-1, d)[torch.from_numpy(qr).to(dq.device)], rq)
     _check(f"{label} dk", dk.reshape(-1, d)[torch.from_numpy(kr).to(dk.device)], rk)
     _check(f"{label} dv", dv.reshape(-1, d)[torch.from_numpy(kr).to(dv.device)], rv)
+
+
+def test_backward_multi_query_full_size_sampled_rows(fa):
+    """The multi-query workload (B1 H32 H_kv1 N16384 d128 causal), whose 128 key blocks split the 32 query heads
+    four ways in the dk/dv kernel (fp32 partials summed by the reduction kernel): sampled dq and dk/dv rows and the
+    first and last rows, against the oracle; and deterministic run to run."""
+    w = ai.WORKLOADS["mqa_bf16_b1h32kv1n16384d128_causal"]
+    label = f"bwd {w.name}"
+    print(f"[case] {label}", flush=True)
+    q, k, v = ai.make_workload(w)
+    dout = _dout(w.B, w.H, w.N, w.d, 760)
+    dq, dk, dv = _run(fa, q, k, v, dout, True, w.scale)
+    again = _run(fa, q, k, v, dout, True, w.scale)
+    assert torch.equal(dq, again[0]) and torch.equal(dk, again[1]) and torch.equal(dv, again[2])
+    g = torch.Generator("cpu").manual_seed(761)
+    N = w.N
+    qr = np.unique(np.concatenate([[0, N - 1, 31 * N, 32 * N - 1],
+                                   torch.randint(0, w.B * w.H * N, (40,), generator=g).numpy()]))
+    kr = np.unique(np.concatenate([[0, 1, 127, 128, N - 1], torch.randint(0, N, (27,), generator=g).numpy()]))
+    rq, rk, rv = oracle.attention_bwd_rows(q, k, v, dout, True, w.scale, q_rows=qr, kv_rows=kr)
+    _check(f"{label} dq", dq.reshape(-1, w.d)[torch.from_numpy(qr).to(dq.device)], rq)
+    _check(f"{label} dk", dk.reshape(-1, w.d)[torch.from_numpy(kr).to(dk.device)], rk)
+    _check(f"{label} dv", dv.reshape(-1, w.d)[torch.from_numpy(kr).to(dv.device)], rv)
 
 
 def test_backward_is_deterministic(fa):
@@ -176,7 +199,7 @@ def test_backward_raw_entry_point_and_errors(fa):
     B, H, Hkv, N, d = 1, 4, 2, 100, 64
     q, k, v, dout = (t.to("cuda:0") for t in _inputs(B, H, Hkv, N, d, 490))
     o, lse = fa.forward(q, k, v, causal=True)
-    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, N),), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d),), dtype=torch.uint8, device="cuda:0")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     sc = ai.default_scale(d)
     stream = torch.cuda.current_stream().cuda_stream
@@ -200,7 +223,7 @@ def test_backward_writes_nothing_outside_its_outputs(fa):
     pad = 4096
     buf = torch.full((3 * n + 4 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda:0")
     views = [buf[pad + i * (n + pad): pad + i * (n + pad) + n].view(B, H, N, d) for i in range(3)]
-    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, N),), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, H, N, d),), dtype=torch.uint8, device="cuda:0")
     rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                    views[0].data_ptr(), views[1].data_ptr(), views[2].data_ptr(), ws.data_ptr(), B, H, H, N, d, 0,
                    ai.default_scale(d), torch.cuda.current_stream().cuda_stream)
@@ -310,7 +333,7 @@ def test_backward_kpad_raw_entry_point(fa):
     q, k, v, dout = (t.to("cuda:0") for t in _inputs(B, H, Hkv, N, d, 750))
     kl = torch.tensor([37, 100], dtype=torch.int32, device="cuda:0")
     o, lse = fa.forward(q, k, v, causal=True, kv_len=kl)
-    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, N),), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(B, H, Hkv, N, d),), dtype=torch.uint8, device="cuda:0")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     sc = ai.default_scale(d)
     stream = torch.cuda.current_stream().cuda_stream

@@ -225,7 +225,8 @@ def test_varlen_backward_writes_nothing_outside_its_outputs(fa):
     buf = torch.full((sum(sizes) + 4 * pad,), 1234.0, dtype=torch.bfloat16, device="cuda:0")
     offs = [pad, 2 * pad + sizes[0], 3 * pad + sizes[0] + sizes[1]]
     views = [buf[offs[i]: offs[i] + sizes[i]] for i in range(3)]
-    ws = torch.empty((fa.fa_bwd_workspace_bytes(len(lens), H, max(lens)),), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty((fa.fa_bwd_workspace_bytes(len(lens), H, Hkv, max(lens), d),), dtype=torch.uint8,
+                     device="cuda:0")
     rc = fa.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                           views[0].data_ptr(), views[1].data_ptr(), views[2].data_ptr(), ws.data_ptr(), cu.data_ptr(),
                           len(lens), H, Hkv, T, max(lens), d, 1, ai.default_scale(d),
