@@ -771,7 +771,7 @@ Attention TFLOP/s at the traced average: {tf:.1f} ({100 * tf / PEAK_BF16_TFLOPS:
 
 
 def write_profiles_bwd(w):
-    """Summary of the BWD_PROFILE_COMMANDS outputs: profiles/bwd_<workload>_rocprof.md (both gradient kernels)."""
+    """Summary of the BWD_PROFILE_COMMANDS outputs: profiles/bwd_<workload>_rocprof.md (the gradient kernels)."""
     dirs = {k: f"gpurun_out/prof_bwd_{w.name}_{k}" for k in BWD_PROFILE_COMMANDS}
     stats = _stats(dirs["trace"])
     fetch, write, sq = _counters(dirs["fetch"]), _counters(dirs["write"]), _counters(dirs["sq"])
@@ -781,8 +781,11 @@ def write_profiles_bwd(w):
     f_write = known_kib / _pick(write, "WRITE_SIZE", copy)
     n_simd = 256 * 4
     rows, total_us = [], 0.0
-    for kname in ("fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"):
+    # the reduction kernel runs only where the dk/dv kernel splits a group's query heads
+    for kname in ("fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel", "fa_bwd_reduce_kernel"):
         t = [r for r in stats if kname in r["Name"]]
+        if not t and kname == "fa_bwd_reduce_kernel":
+            continue
         if not t:
             raise RuntimeError(f"no kernel statistics for {kname}")
         avg_us = float(t[0]["AverageNs"]) / 1e3
