@@ -349,10 +349,11 @@ constexpr int kPSlotBytes = 2 * 64 * 16;  // p of one 32 x 32 sub-block, bf16, a
 // Waves w and w+4 run on the same SIMD and own the same 32 keys: the p wave (w < 4) computes S = Q K^T, p and
 // dV^T += dO^T P; the dS wave computes dP = dO V^T, then (after the sub-block's barrier) dS = p (dP - D) from the
 // p the other wave left in LDS, and dK^T += Q^T dS. Each holds half the accumulators, so two waves share a SIMD.
-// With nsplit > 1, the grid's y extent is BHkv * nsplit: workgroup part z of a key block visits only query heads
-// z*group/nsplit .. (z+1)*group/nsplit - 1 of the group and writes its dk and dv in fp32 to part
-// ([2][nsplit][BHkv][N][D]: dk, then dv) for fa_bwd_reduce_kernel. The parts of one key block are handed out
-// together, so the longest-first order of causal blocks holds over all of them.
+// A key block's work is a list of iterations, one per (query head of the group, query tile), head by head. With
+// nsplit > 1, the grid's y extent is BHkv * nsplit: workgroup part z of a key block takes iterations
+// n*z/nsplit .. n*(z+1)/nsplit - 1 of the n and writes its dk and dv in fp32 to part ([2][nsplit][BHkv][N][D]:
+// dk, then dv) for fa_bwd_reduce_kernel. The parts of one key block are handed out together, so the
+// longest-first order of causal blocks holds over all of them.
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -409,8 +410,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const int kpitch = VARLEN ? Hkv * D : D;  // ... of k, v, dk and dv
   const int qpitch_b = 2 * qpitch;
   const size_t kv_off = VARLEN ? ((size_t)start * Hkv + bkv % Hkv) * D : (size_t)bkv * (size_t)N * D;
-  const int gsub = group / nsplit;                      // query heads this workgroup visits
-  const int bh0 = bkv * group + zs * gsub;  // the first of them (of B*H)
+  const int bh0 = bkv * group;  // first query head (of B*H) of this key/value head's group
   const int Nk = kv_len ? __builtin_amdgcn_readfirstlane(min(max(kv_len[bkv / Hkv], 0), N)) : Ns;
 
   const int kw0 = k0 + pair * kBwdRows;
@@ -436,7 +436,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   const int nqt = (Ns + kDkdvTile - 1) / kDkdvTile;
   const int t0 = CAUSAL ? kblk : 0;
   const int per_head = nqt - t0;
-  const int n_iter = (k0 < Nk) ? gsub * per_head : 0;  // a block of padded keys only writes zeros
+  const int n_all = (k0 < Nk) ? group * per_head : 0;  // a block of padded keys only writes zeros
+  const int it_lo = (int)((long long)n_all * zs / nsplit), it_hi = (int)((long long)n_all * (zs + 1) / nsplit);
   const int npad = ws_rows(N);
   auto copy_iter = [&](int it, int S) __attribute__((always_inline)) {
     const int hq = bh0 + it / per_head;
@@ -568,21 +569,21 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   // finished reading that stage (tile it-1) before the barrier that ended tile it-1, and the barrier that ends
   // tile it also waits for the copies. The last tile copies itself again (harmless, in bounds), so the copy is
   // unconditional.
-  if (n_iter > 0) {
-    copy_iter(0, 0);
+  if (it_hi > it_lo) {
+    copy_iter(it_lo, 0);
     wait_copies_and_barrier<0>();
   }
   auto run = [&](auto role_c) __attribute__((always_inline)) {
     static_assert(kSub % 2 == 0, "sub-blocks alternate between two operand sets");
-    for (int it = 0; it < n_iter; ++it) {
-      const int S = it & 1;
+    for (int it = it_lo; it < it_hi; ++it) {
+      const int S = (it - it_lo) & 1;
       bf16x8 a0[kDB], a1[kDB];
       f32x4 w0[4], w1[4];
       read_pre(S, 0, role_c, a0, w0);
 #pragma unroll
       for (int sb = 0; sb < kSub; sb += 2) {
         sub_block(it, S, sb, role_c, a0, w0, a1, w1);
-        if (sb == 0) copy_iter(min(it + 1, n_iter - 1), S ^ 1);
+        if (sb == 0) copy_iter(min(it + 1, it_hi - 1), S ^ 1);
         sub_block(it, S, sb + 1, role_c, a1, w1, a0, w0);
       }
       wait_copies_and_barrier<0>();

@@ -32,16 +32,17 @@ hipError_t launch_bwd_varlen_bf16(const void* q, const void* k, const void* v, c
                                   const void* dout, void* dq, void* dk, void* dv, float* ws, const int* cu_seqlens,
                                   int B, int H, int Hkv, int T_total, int max_seqlen, int d, bool causal, float scale,
                                   hipStream_t stream);
-// The dk/dv kernel runs one workgroup per (128-key block, key/value head) and visits the H/Hkv query heads of the
-// head's group in turn. When that grid would give fewer than two workgroups per CU (256 CUs), the group's query
-// heads are divided over `split` workgroups (the smallest divisor of the group that reaches 512 workgroups, else
-// the whole group): each writes fp32 partial dk and dv, and a reduction kernel sums them in split order.
+// The dk/dv kernel runs one workgroup per (128-key block, key/value head) and visits every (query head of the
+// head's group, 128-row query tile) in turn. When that grid would give fewer than two workgroups per CU (256 CUs),
+// each block's visits are divided over `split` workgroups: the fewest that reach 512 workgroups, at most one per
+// visit of the longest block and at most 64. Each writes fp32 partial dk and dv, and a reduction kernel sums
+// them in split order.
 inline int bwd_head_split(int B, int H, int Hkv, int N) {
-  const int group = H / Hkv;
-  const long long wgs = (long long)((N + 127) / 128) * B * Hkv;
-  for (int s = 1; s < group; ++s)
-    if (group % s == 0 && wgs * s >= 512) return s;
-  return group;
+  const long long tiles = (N + 127) / 128, wgs = tiles * B * Hkv;
+  if (wgs >= 512) return 1;
+  long long s = (512 + wgs - 1) / wgs;
+  if (s > (long long)(H / Hkv) * tiles) s = (long long)(H / Hkv) * tiles;
+  return (int)(s < 64 ? s : 64);
 }
 // Workspace of the gradient kernels: -D_i and lse_i*log2e planes, [B*H][2][N rounded up to 128] float; then,
 // with a head split s > 1, the partial dk and dv, [2][s][B*Hkv][N][d] float.

@@ -256,8 +256,13 @@ def test_backward_workspace_bytes():
     # one key/value head of 16384 keys: 128 workgroups, so the 32 query heads split 4 ways (the smallest divisor
     # reaching 512), each way with fp32 partial dk and dv of every key row
     assert ws(1, 32, 1, 16384, 128) == 32 * 16384 * 8 + 2 * 4 * 16384 * 128 * 4
-    # a tiny grid splits the whole group (2 heads per key/value head): 2 partials
+    # a tiny grid: 2 workgroups would need 256 parts, but a block has only 2 visits (2 heads x 1 query tile)
     assert ws(1, 4, 2, 100, 64) == 4 * 128 * 8 + 2 * 2 * 2 * 100 * 64 * 4
+    # one head of 32768 keys: 256 key blocks, so each block's query tiles split 2 ways
+    assert ws(1, 1, 1, 32768, 128) == 32768 * 8 + 2 * 2 * 32768 * 128 * 4
+    # 8 heads of 1000 keys: 8 blocks x 8 heads = 64 workgroups, 8 parts; at most 64 parts however small the grid
+    assert ws(1, 8, 8, 1000, 64) == 8 * 1024 * 8 + 2 * 8 * 8 * 1000 * 64 * 4
+    assert ws(1, 64, 1, 128, 64) == 64 * 128 * 8 + 2 * 64 * 128 * 64 * 4
     assert ws(0, 3, 3, 100, 64) == 0 and ws(1, 1, 1, -5, 64) == 0
     assert ws(1, 4, 3, 100, 64) == 0 and ws(1, 4, 0, 100, 64) == 0 and ws(1, 4, 4, 100, 96) == 0
 

@@ -133,6 +133,29 @@ def test_backward_multi_query_full_size_sampled_rows(fa):
     _check(f"{label} dv", dv.reshape(-1, w.d)[torch.from_numpy(kr).to(dv.device)], rv)
 
 
+@pytest.mark.parametrize("N,causal", [(8192, True), (3000, False)])
+def test_backward_one_long_head(fa, N, causal):
+    """One head (B1 H1 d128): too few key blocks for the GPU, so each block's query tiles are divided over several
+    dk/dv workgroups (fp32 partials, fixed-order sum). Sampled dq and dk/dv rows and the tile edges against the
+    oracle, and deterministic run to run."""
+    d = 128
+    label = f"bwd B1 H1 N{N} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v, dout = _inputs(1, 1, 1, N, d, 790)
+    scale = ai.default_scale(d)
+    dq, dk, dv = _run(fa, q, k, v, dout, causal, scale)
+    again = _run(fa, q, k, v, dout, causal, scale)
+    assert torch.equal(dq, again[0]) and torch.equal(dk, again[1]) and torch.equal(dv, again[2])
+    g = torch.Generator("cpu").manual_seed(791)
+    edges = np.array([0, 1, 127, 128, N // 2, N - 2, N - 1])
+    rows = np.unique(np.concatenate([edges, torch.randint(0, N, (120,), generator=g).numpy()]))
+    rq, rk, rv = oracle.attention_bwd_rows(q, k, v, dout, causal, scale, q_rows=rows, kv_rows=rows)
+    idx = torch.from_numpy(rows).to(dq.device)
+    _check(f"{label} dq", dq.reshape(-1, d)[idx], rq)
+    _check(f"{label} dk", dk.reshape(-1, d)[idx], rk)
+    _check(f"{label} dv", dv.reshape(-1, d)[idx], rv)
+
+
 def test_backward_is_deterministic(fa):
     q, k, v, dout = _inputs(2, 8, 2, 1000, 128, 480)
     a = _run(fa, q, k, v, dout, True, ai.default_scale(128))
