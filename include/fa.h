@@ -211,10 +211,10 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
 
 /* fa_bwd_workspace_bytes -- bytes of the fa_bwd / fa_bwd_kpad workspace (fa_bwd_varlen: N = max_seqlen); 0 for
  * an empty problem or arguments the gradient calls reject (H_kv not dividing H, d not 64 or 128). It holds two
- * float planes per query row (-D_i and lse_i log2 e; 8 bytes a row), and, when the key/value heads alone give
- * the dk/dv kernel fewer than two workgroups per compute unit (few heads of a grouped-query call), the fp32
- * partial dk and dv of the workgroups that share a group's query heads between them (2 x s x B x H_kv x N x d
- * floats, s dividing H / H_kv), summed in a fixed order by a third kernel. */
+ * float planes per query row (-D_i and lse_i log2 e; 8 bytes a row), and, when the key blocks of the key/value
+ * heads give the dk/dv kernel fewer than two workgroups per compute unit (few or long heads), the fp32 partial dk
+ * and dv of the s <= 64 workgroups that share each key block's query heads and tiles between them
+ * (2 x s x B x H_kv x N x d floats), summed in a fixed order by a third kernel. */
 size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d);
 
 /*
