@@ -5,8 +5,8 @@
 One step = one fa_fwd call (the whole hot path: Q/K/V read, S = QK^T, online softmax, PV, 1/l, o and lse
 written) over the workload's synthetic inputs, already resident in device memory. Prints ONE JSON line:
 value = attention-forward TFLOP/s (4*B*H*N^2*d, halved when causal) over the timed steps; roofline = the
-kernel's MFMA roofline from HIP-event launch durations; cpu_baseline = the fp64 oracle timed on a bounded
-sample of the same workload on this host's cores.
+kernel's MFMA roofline from HIP-event launch durations; cpu_baseline = the fp64 oracle timed on every query
+row of the same workload on this host's cores (about 4 s of CPU work on 16 threads for the headline workload).
 
 The line also carries `backward`: the gradient call fa_bwd (dq, then dk and dv) on the headline workload and on
 the long causal one, timed the same way, in the usual FLOP convention 2.5 x the forward's (five matrix products:
@@ -119,18 +119,13 @@ def kernel_src_hash(srcs=KERNEL_SRCS) -> str:
 
 
 def kernel_name(w) -> str:
-    """The kernel instance the library launches for workload w (mirrors the launcher's choice)."""
-    c = "true" if w.causal else "false"
+    """The kernel instance the library launches for workload w, as the library itself reports it (fa_fwd_instance;
+    the fp32 forward has one instance per head dim and causal flag)."""
+    import exact_attention_13_amd as fa
+
     if w.dtype != "bf16":
-        return f"fa_fwd_f32_kernel<{w.d}, {c}>"
-    bh = w.B * w.H
-    if ((w.N + 255) // 256) * bh >= 512:
-        shape = "8, 2, 2, false, 1"   # wide
-    elif ((w.N + 127) // 128) * bh >= 512:
-        shape = "4, 2, 1, false, 1"   # narrow
-    else:
-        shape = "8, 2, 2, false, 2"   # split keys
-    return f"fa_fwd_bf16_kernel<{w.d}, {c}, {shape}>"
+        return f"fa_fwd_f32_kernel<{w.d}, {'true' if w.causal else 'false'}>"
+    return fa.fa_fwd_instance(w.B, w.H, w.N, w.d, int(w.causal), 0)
 
 
 def _device_inputs(w):
@@ -438,7 +433,11 @@ def cpu_baseline(w, n_rows: int):
 
     q, k, v = ai.make_workload(w)
     lens = ai.kv_len_of(w)
-    rows = ai.sample_rows(w.B, w.H, w.N, n_rows, seed=w.seed + 7)
+    total = w.B * w.H * w.N
+    if n_rows <= 0 or n_rows >= total:
+        rows = np.arange(total, dtype=np.int64)  # every query row of the workload
+    else:
+        rows = ai.sample_rows(w.B, w.H, w.N, n_rows, seed=w.seed + 7)
     threads = oracle.default_threads()
     oracle.attention_rows(q, k, v, w.causal, w.scale, rows=rows[:threads], threads=threads, kv_len=lens)  # warm
     t0 = time.perf_counter()
@@ -463,8 +462,9 @@ def cpu_baseline(w, n_rows: int):
     except OSError:
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} seeded random query rows of {w.name} ({len(rows) / (w.B * w.H * w.N):.1%} of "
-                      f"the rows), fp64, {dt:.2f} s wall on {threads} threads; FLOPs counted as 4*d per visible key",
+            "sample": (f"all {total} query rows of {w.name}" if len(rows) == total else
+                       f"{len(rows)} seeded random query rows of {w.name} ({len(rows) / total:.1%} of the rows)")
+                      + f", fp64, {dt:.2f} s wall on {threads} threads; FLOPs counted as 4*d per visible key",
             "single_thread": {"value": sample_flops(rows1) / dt1 / 1e12, "rows": len(rows1),
                               "seconds": round(dt1, 3)},
             "cpu_model": cpu, "host_cpus": os.cpu_count(), "seconds": dt}
@@ -847,7 +847,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(ai.WORKLOADS))
-    ap.add_argument("--cpu-rows", type=int, default=32768, help="query rows in the oracle's CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows in the oracle's CPU sample (0: every row of the workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")

@@ -26,7 +26,7 @@ FA_ERR_ALIAS = 6
 FA_ERR_HIP = 7
 
 EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_kpad",
-           "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_strerror", "fa_version")
+           "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_fwd_instance", "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python exact_attention_13_amd/build.py` "
@@ -55,6 +55,8 @@ _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.fa_fwd_f32.restype = _I
 _lib.fa_fwd_f32.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+_lib.fa_fwd_instance.restype = ctypes.c_char_p
+_lib.fa_fwd_instance.argtypes = [_I] * 6
 _lib.fa_strerror.restype = ctypes.c_char_p
 _lib.fa_strerror.argtypes = [_I]
 _lib.fa_version.restype = _I
@@ -127,6 +129,12 @@ def fa_fwd_f32(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, N: int,
                scale: float, stream: int) -> int:
     """Raw entry point: device pointers as ints, fp32 q/k/v/o and lse. Returns the FA_* code."""
     return _lib.fa_fwd_f32(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+
+
+def fa_fwd_instance(B: int, H: int, N: int, d: int, causal: int, packed: int = 0) -> str | None:
+    """Name of the bf16 forward kernel instance the library launches for these sizes (None if they are invalid)."""
+    r = _lib.fa_fwd_instance(B, H, N, d, causal, packed)
+    return None if r is None else r.decode()
 
 
 def fa_strerror(code: int) -> str:

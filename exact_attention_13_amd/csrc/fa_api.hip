@@ -228,6 +228,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
 
 size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || H_kv <= 0 || H % H_kv != 0 || (d != 64 && d != 128)) return 0;
+  if ((long long)B * H > kMaxHeads || N > kMaxNBwd) return 0;  // sizes the gradient calls reject
   return fa::bwd_workspace_bytes(B, H, H_kv, N, d);
 }
 
@@ -263,6 +264,12 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   if (rc != FA_OK || empty) return rc;
   const hipError_t e = fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, causal != 0, scale, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_fwd_instance(int B, int H, int N, int d, int causal, int packed) {
+  if (B < 1 || H < 1 || N < 1 || (long long)B * H > kMaxHeads || N > kMaxN) return nullptr;
+  if ((d != 64 && d != 128) || (causal != 0 && causal != 1) || (packed != 0 && packed != 1)) return nullptr;
+  return fa::fwd_instance_bf16(B * H, N, d, causal != 0, packed != 0);
 }
 
 const char* fa_strerror(int code) {

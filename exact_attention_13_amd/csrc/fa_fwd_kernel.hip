@@ -646,27 +646,33 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
 // The three differ in where the exponent reference may move and in the order of the sums, so their outputs can
 // differ in the last bit; each is deterministic, and the packed entry point chooses the same way from max_seqlen.
 constexpr long long kTwoPerCu = 512;
-enum class Shape { kWide, kNarrow, kSplit };
+enum class Shape { kWide = 0, kNarrow = 1, kSplit = 2 };
 static Shape fwd_shape(int N, int BH) {
   if ((long long)((N + 255) / 256) * BH >= kTwoPerCu) return Shape::kWide;
   if ((long long)((N + 127) / 128) * BH >= kTwoPerCu) return Shape::kNarrow;
   return Shape::kSplit;
 }
+// (NW, KT, SPL) of each shape; the ring always has 2 stages.
+#define FA_WIDE 8, 2, 1
+#define FA_NARROW 4, 1, 1
+#define FA_SPLIT 8, 2, 2
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                            int N, int d, bool causal, float scale, const int* kv_len, hipStream_t stream) {
   const int BH = B * H, group = H / Hkv;
 #define FA_LAUNCH(D, C, NW, KT, SPL) \
   launch_bf16<D, C, NW, 2, KT, false, SPL>(q, k, v, o, lse, BH, N, scale, H, group, kv_len, stream)
-#define FA_D(NW, KT, SPL)                                                                        \
+#define FA_D2(NW, KT, SPL)                                                                       \
   (d == 64 ? (causal ? FA_LAUNCH(64, true, NW, KT, SPL) : FA_LAUNCH(64, false, NW, KT, SPL)) \
            : (causal ? FA_LAUNCH(128, true, NW, KT, SPL) : FA_LAUNCH(128, false, NW, KT, SPL)))
+#define FA_D(...) FA_D2(__VA_ARGS__)
   switch (fwd_shape(N, BH)) {
-    case Shape::kWide: return FA_D(8, 2, 1);
-    case Shape::kNarrow: return FA_D(4, 1, 1);
-    default: return FA_D(8, 2, 2);
+    case Shape::kWide: return FA_D(FA_WIDE);
+    case Shape::kNarrow: return FA_D(FA_NARROW);
+    default: return FA_D(FA_SPLIT);
   }
 #undef FA_D
+#undef FA_D2
 #undef FA_LAUNCH
 }
 
@@ -677,17 +683,38 @@ hipError_t launch_fwd_varlen_bf16(const void* q, const void* k, const void* v, v
 #define FA_LAUNCH(D, C, NW, KT, SPL)                                                                                 \
   launch_bf16<D, C, NW, 2, KT, true, SPL>(q, k, v, o, lse, BH, N, scale, H, group, nullptr, stream, cu_seqlens, \
                                           T_total)
-#define FA_D(NW, KT, SPL)                                                                        \
+#define FA_D2(NW, KT, SPL)                                                                       \
   (d == 64 ? (causal ? FA_LAUNCH(64, true, NW, KT, SPL) : FA_LAUNCH(64, false, NW, KT, SPL)) \
            : (causal ? FA_LAUNCH(128, true, NW, KT, SPL) : FA_LAUNCH(128, false, NW, KT, SPL)))
+#define FA_D(...) FA_D2(__VA_ARGS__)
   switch (fwd_shape(N, BH)) {
-    case Shape::kWide: return FA_D(8, 2, 1);
-    case Shape::kNarrow: return FA_D(4, 1, 1);
-    default: return FA_D(8, 2, 2);
+    case Shape::kWide: return FA_D(FA_WIDE);
+    case Shape::kNarrow: return FA_D(FA_NARROW);
+    default: return FA_D(FA_SPLIT);
   }
 #undef FA_D
+#undef FA_D2
 #undef FA_LAUNCH
 }
+
+// The name of the instance the two launchers above pick, as the kernel's template arguments spell it.
+const char* fwd_instance_bf16(int BH, int N, int d, bool causal, bool packed) {
+#define FA_NAME2(D, C, V, NW, KT, SPL) "fa_fwd_bf16_kernel<" #D ", " #C ", " #NW ", 2, " #KT ", " #V ", " #SPL ">"
+#define FA_NAME(D, C, V, ...) FA_NAME2(D, C, V, __VA_ARGS__)
+#define FA_NAMES(S)                                                                              \
+  {{{FA_NAME(64, false, false, S), FA_NAME(64, false, true, S)},                                 \
+    {FA_NAME(64, true, false, S), FA_NAME(64, true, true, S)}},                                  \
+   {{FA_NAME(128, false, false, S), FA_NAME(128, false, true, S)},                               \
+    {FA_NAME(128, true, false, S), FA_NAME(128, true, true, S)}}}
+  static const char* const names[3][2][2][2] = {FA_NAMES(FA_WIDE), FA_NAMES(FA_NARROW), FA_NAMES(FA_SPLIT)};
+#undef FA_NAMES
+#undef FA_NAME
+#undef FA_NAME2
+  return names[(int)fwd_shape(N, BH)][d == 128][causal][packed];
+}
+#undef FA_WIDE
+#undef FA_NARROW
+#undef FA_SPLIT
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, hipStream_t stream) {

@@ -17,6 +17,9 @@ hipError_t launch_fwd_varlen_bf16(const void* q, const void* k, const void* v, v
 // fp8 (float8_e4m3fn) q, k [B*H, N, d] and v^T [B*H, d, N] with per-tensor scales; bf16 o. N % 16 == 0.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, float q_scale, float k_scale, float v_scale, hipStream_t stream);
+// Name of the bf16 forward kernel instance launch_fwd_bf16 (packed false) or launch_fwd_varlen_bf16 (packed true,
+// N = max_seqlen) enqueues for B*H = BH heads of N rows and head dim d (64 or 128).
+const char* fwd_instance_bf16(int BH, int N, int d, bool causal, bool packed);
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, hipStream_t stream);
 // Enqueue the two gradient kernels (dq and the workspace values, then dk and dv). Arguments must already be valid

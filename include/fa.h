@@ -26,17 +26,23 @@
  * fa_bwd's workspace) and keeps it alive until the stream has run the work.
  * The library allocates nothing, keeps no state between calls, and never
  * synchronises: it validates the arguments on the host, enqueues its kernels
- * on `stream` (0 = null stream; one kernel for a forward call, two for fa_bwd)
- * and returns. Results are valid once the caller synchronises the stream.
- * Inputs are only read; outputs are only written. Calls are thread-safe, and
- * the same inputs give bitwise-identical outputs on every call (no atomics, no
- * split over keys).
+ * on `stream` (0 = null stream) and returns. A forward call enqueues one
+ * kernel; a gradient call two (dq, then dk and dv), or three when the dk/dv
+ * visits of each key block are divided over several workgroups and a third
+ * kernel sums their fp32 partials. Results are valid once the caller
+ * synchronises the stream. Inputs are only read; outputs are only written.
+ * Calls are thread-safe, and the same inputs give bitwise-identical outputs on
+ * every call: no kernel uses atomics, and where the work of one output row is
+ * divided -- the forward's small-grid shape gives the two 64-key halves of
+ * every key tile to two waves, each with its own running maximum and sum; the
+ * gradient call may give a key block's query tiles to several workgroups --
+ * the partial results are merged in a fixed order.
  *
  * Errors. 0 on success; otherwise one of the FA_ERR_* codes below, and nothing
  * is enqueued. Every check except FA_ERR_HIP runs before any HIP call. Faults
  * inside the kernel surface at the caller's next synchronisation.
  * B, H or N equal to 0 is an empty problem: the call returns 0, enqueues
- * nothing and does not look at the pointers.
+ * nothing and does not look at the pointers (sizes below 0 are FA_ERR_SHAPE).
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
@@ -210,7 +216,8 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
                   int total, int max_seqlen, int d, int causal, float scale, hipStream_t stream);
 
 /* fa_bwd_workspace_bytes -- bytes of the fa_bwd / fa_bwd_kpad workspace (fa_bwd_varlen: N = max_seqlen); 0 for
- * an empty problem or arguments the gradient calls reject (H_kv not dividing H, d not 64 or 128). It holds two
+ * an empty problem or arguments the gradient calls reject (H_kv not dividing H, d not 64 or 128, B*H above
+ * 65535, N above 2^28). It holds two
  * float planes per query row (-D_i and lse_i log2 e; 8 bytes a row), and, when the key blocks of the key/value
  * heads give the dk/dv kernel fewer than two workgroups per compute unit (few or long heads), the fp32 partial dk
  * and dv of the s <= 64 workgroups that share each key block's query heads and tiles between them
@@ -244,6 +251,21 @@ int fa_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse
  */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d,
                int causal, float scale, hipStream_t stream);
+
+/*
+ * fa_fwd_instance -- which bf16 forward kernel instance fa_fwd, fa_fwd_gqa
+ * and fa_fwd_kpad (packed = 0), or fa_fwd_varlen (packed = 1, N =
+ * max_seqlen), enqueue for B*H heads of N query rows, head dim d and the
+ * causal flag: a static string spelling the kernel's template arguments, the
+ * name profilers list, e.g. "fa_fwd_bf16_kernel<128, false, 8, 2, 2, false, 1>"
+ * (<d, causal, waves per workgroup, ring stages, 64-key parts per key tile,
+ * packed, waves per 32-row group>). The workgroup shape is chosen from the
+ * grid size alone (grouped heads and key lengths do not change it). NULL when
+ * the sizes are not a valid non-empty problem (B, H or N below 1, B*H above
+ * 65535, N above 2^30, d not 64 or 128, causal or packed not 0 or 1). Makes no
+ * HIP call.
+ */
+const char* fa_fwd_instance(int B, int H, int N, int d, int causal, int packed);
 
 /* fa_strerror -- static, NUL-terminated description of an FA_* code. */
 const char* fa_strerror(int code);

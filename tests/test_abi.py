@@ -61,6 +61,25 @@ def test_version_and_strerror():
     assert fa.fa_strerror(99) == "unknown error code"
 
 
+def test_instance_query():
+    """fa_fwd_instance names the kernel instance the bf16 forward launches, from the grid size alone: 256-row
+    workgroups when they give the 256 CUs two each, else 128-row ones when those do, else the split-key shape."""
+    assert fa.fa_fwd_instance(2, 16, 4096, 128, 0, 0) == "fa_fwd_bf16_kernel<128, false, 8, 2, 2, false, 1>"
+    assert fa.fa_fwd_instance(1, 32, 16384, 128, 1, 0) == "fa_fwd_bf16_kernel<128, true, 8, 2, 2, false, 1>"
+    assert fa.fa_fwd_instance(2, 32, 1000, 64, 1, 0) == "fa_fwd_bf16_kernel<64, true, 4, 2, 1, false, 1>"
+    assert fa.fa_fwd_instance(4, 8, 1024, 64, 0, 0) == "fa_fwd_bf16_kernel<64, false, 8, 2, 2, false, 2>"
+    assert fa.fa_fwd_instance(4, 32, 1000, 128, 0, 1) == "fa_fwd_bf16_kernel<128, false, 8, 2, 2, true, 1>"
+    # the boundaries: 128 heads of 1024 rows (4 x 128 = 512 wide workgroups), 127 of them (8 x 127 narrow ones),
+    # 63 (8 x 63 = 504 narrow ones: split)
+    assert fa.fa_fwd_instance(1, 128, 1024, 64, 0, 0).endswith("8, 2, 2, false, 1>")
+    assert fa.fa_fwd_instance(1, 127, 1024, 64, 0, 0).endswith("4, 2, 1, false, 1>")
+    assert fa.fa_fwd_instance(1, 64, 1024, 64, 0, 0).endswith("4, 2, 1, false, 1>")
+    assert fa.fa_fwd_instance(1, 63, 1024, 64, 0, 0).endswith("8, 2, 2, false, 2>")
+    for bad in ((0, 1, 64, 64, 0, 0), (1, 0, 64, 64, 0, 0), (1, 1, 0, 64, 0, 0), (1, 1, 64, 96, 0, 0),
+                (1, 1, 64, 64, 2, 0), (1, 1, 64, 64, 0, 2), (70000, 1, 64, 64, 0, 0), (1, 1, (1 << 30) + 1, 64, 0, 0)):
+        assert fa.fa_fwd_instance(*bad) is None, bad
+
+
 LEN = A + 0x5000000  # fake device address of kv_len
 
 

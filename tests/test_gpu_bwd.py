@@ -169,12 +169,21 @@ def test_backward_is_deterministic(fa):
     (2, 2, 9, 64, True, 0.3, 1.7, 7154), (2, 2, 130, 128, False, 0.2, 1.7, 8428)])
 def test_backward_peaked_rows_carry_the_rounding_of_o(fa, B, H, N, d, causal, scale, amp, seed):
     """Peaked rows with small gradients (q and k drawn N(0, amp^2), few keys). The gradient kernels take
-    D_i = dO_i . o_i from the o they are given, which the forward rounded to bf16; an error e_i = dO_i . (o_i -
-    o_exact_i) in D moves dS_ij by -p_ij e_i, so dq_i by at most scale |e_i| max_j |k_j| and dk_j by at most
-    scale sum_i p_ij |e_i| |q_i| (elementwise over d; dv does not use D). Where the gradients are small against
-    that term (two keys with one dominant: dq and dk scale with p_0 p_1) it exceeds 2e-2 of their largest value,
-    so here the bound is the plain one plus that term, with |e_i| <= sum_d |dO_id| |o_id - o_exact_id| measured
-    from the o the backward was given and the oracle's o."""
+    D_i = dO_i . o_i from the o they are given, which the forward rounded to bf16; an error e_i in D moves dS_ij by
+    -p_ij e_i, so dq_i by at most scale |e_i| max_j |k_j| and dk_j by at most scale sum_i p_ij |e_i| |q_i|
+    (elementwise over d; dv does not use D). Where the gradients are small against that term (two keys with one
+    dominant: dq and dk scale with p_0 p_1) it exceeds 2e-2 of their largest value, so the bound here is the plain
+    one plus that term, with e_i taken from a bound on the forward's error that uses only the oracle's quantities:
+
+      the weights are rounded to bf16 before the product with v and l sums exactly those rounded weights, so before
+      its own rounding o_i is the weighted mean of v under weights p_ij (1 + delta_j), |delta_j| <= E_i, and
+      |o_ic - o_exact_ic| <= E_i / (1 - E_i) max_j |v_jc - o_exact_ic|; rounding o to bf16 adds 2^-8 |o_ic|.
+      E_i = 2^-8 (bf16 rounding of a weight) + scale (2 d 2^-24 + 2^-21) max_j sum_c |q_ic k_jc| (fp32 scores
+      and the fp32 scale factor, both ends of a weight ratio) + 2^-20 (the exponential); the fp32 sums of the n_i
+      visible terms add 2 n_i 2^-24 max_j |v_jc|.
+
+    The test first checks the forward's o against that per-element bound, then the gradients against the bound
+    built from it (e_i = sum_c |dO_ic| bound_ic + the fp32 dot product's own error)."""
     g = torch.Generator("cpu").manual_seed(seed)
     q, k, v, dout = ((torch.randn((B, H, N, d), generator=g) * f).to(torch.bfloat16) for f in (amp, amp, 1.0, 1.0))
     print(f"[bwd] peaked rows B={B} H={H} N={N} d={d} causal={causal} scale={scale} amp={amp}", flush=True)
@@ -184,12 +193,25 @@ def test_backward_peaked_rows_carry_the_rounding_of_o(fa, B, H, N, d, causal, sc
     torch.cuda.synchronize()
     o_ex, lse_ex = oracle.attention(q, k, v, causal, scale)
     rq, rk, rv = oracle.attention_bwd(q, k, v, dout, causal, scale)
-    q64, k64, d64 = (t.double().numpy() for t in (q, k, dout))
-    e = (np.abs(d64) * np.abs(o.double().cpu().numpy() - o_ex)).sum(-1)             # [B, H, N]
+    q64, k64, v64, d64 = (t.double().numpy() for t in (q, k, v, dout))
     sc = float(np.float32(scale))
-    p = np.exp(np.einsum("bhid,bhjd->bhij", q64, k64) * sc - lse_ex[..., None])
-    if causal:
-        p = np.where(np.tril(np.ones((N, N), dtype=bool)), p, 0.0)
+    vis = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+    # a-priori bound on |o - o_exact| per element, from the oracle's o and the inputs only
+    qk_abs = np.einsum("bhic,bhjc->bhij", np.abs(q64), np.abs(k64))
+    E = 2.0 ** -8 + sc * (2 * d * 2.0 ** -24 + 2.0 ** -21) * np.where(vis, qk_abs, 0).max(-1) + 2.0 ** -20
+    spread = np.where(vis[None, None, :, :, None], np.abs(v64[:, :, None, :, :] - o_ex[:, :, :, None, :]),
+                      0).max(3)                                                                # [B, H, N, d]
+    v_max = np.where(vis[None, None, :, :, None], np.abs(v64)[:, :, None, :, :], 0).max(3)      # [B, H, N, d]
+    n_vis = vis.sum(-1)[None, None, :, None]
+    o_bound = ((E / (1 - E))[..., None] * spread + 2 * n_vis * 2.0 ** -24 * v_max) * (1 + 2.0 ** -8) \
+        + (2.0 ** -8 + 2.0 ** -22) * np.abs(o_ex)
+    o_err = np.abs(o.double().cpu().numpy() - o_ex)
+    print(f"[parity] o max|err|={o_err.max():.3e}, worst err/a-priori bound {np.max(o_err / o_bound):.3f}",
+          flush=True)
+    assert np.all(o_err <= o_bound), "forward o outside its a-priori bound"
+    assert np.abs(lse.double().cpu().numpy() - lse_ex).max() <= RTOL
+    e = (np.abs(d64) * o_bound).sum(-1) + d * 2.0 ** -24 * (np.abs(d64) * (np.abs(o_ex) + o_bound)).sum(-1)
+    p = np.where(vis, np.exp(np.einsum("bhid,bhjd->bhij", q64, k64) * sc - lse_ex[..., None]), 0.0)
     t_dq = sc * e[..., None] * np.abs(k64).max(axis=2, keepdims=True)                # [B, H, N, d]
     t_dk = sc * np.einsum("bhij,bhi,bhid->bhjd", p, e, np.abs(q64))                  # [B, H, N, d]
     for label, got, ref, term in (("dq", dq, rq, t_dq), ("dk", dk, rk, t_dk), ("dv", dv, rv, 0.0)):

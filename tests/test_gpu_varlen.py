@@ -82,8 +82,13 @@ def test_varlen_workload_sampled_rows(fa, name):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("T,H,Hkv", [(333, 4, 4), (4096, 4, 2), (4096, 32, 8)])
 def test_one_packed_sequence_equals_the_padded_forward(fa, T, H, Hkv, causal):
-    """The same data as one [1, H, T, d] problem through fa_fwd_gqa gives the same bits (same tiles, same order;
-    the last shape takes the 8-wave workgroups, the others the 4-wave ones)."""
+    """The same data as one [1, H, T, d] problem through fa_fwd_gqa gives the same bits (same tiles, same order).
+    The packed and padded launches choose the workgroup shape by the same rule (fa_fwd_instance): the 32-head case
+    takes the wide instance (16 x 32 = 512 workgroups of 256 rows), the others the split-key one."""
+    split = 2 if H == 4 else 1
+    for packed in (0, 1):
+        assert fa.fa_fwd_instance(1, H, T, 128, int(causal), packed).endswith("8, 2, 2, %s, %d>" % (
+            "true" if packed else "false", split))
     d = 128
     q, k, v = ai.make_qkv_varlen((T,), H, d, seed=850, Hkv=Hkv)
     o, lse = _run(fa, q, k, v, (T,), causal, ai.default_scale(d))

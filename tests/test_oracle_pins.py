@@ -290,3 +290,59 @@ def test_bad_rows_rejected():
     q, k, v = ai.make_qkv(1, 1, 8, 64, seed=1, dtype="bf16")
     with pytest.raises(RuntimeError):
         oracle.attention_rows(q, k, v, False, 0.125, rows=np.array([8]))
+
+
+# --- the page's blockwise recurrence (reading R6) -----------------------------------------------------------------
+
+def _page_blockwise(q, k, v, scale, block, keep_old_sum):
+    """The recurrence of the unite.ai page's "Implementation Details" code, restated in numpy fp64 (the page's
+    tensors are (batch, seq, d_model); batch x heads serve as its batch here). For every block of `block` query rows
+    and then every block of `block` keys it forms the block's scores, moves the running row maximum M to
+    M' = max(M, row max), rescales by a = exp(M - M'), updates the running sum L' = a L + sum exp(S - M') and the
+    output. As printed, the output update is O' = (a O + exp(S - M') V) / L', which treats the previous O, already
+    divided by L, as if it were not (keep_old_sum=False); the reading followed everywhere else multiplies the old
+    O by L as well, O' = (a L O + exp(S - M') V) / L' (keep_old_sum=True)."""
+    qa, ka, va = (np.asarray(x.to(torch.float64).reshape(-1, x.shape[-2], x.shape[-1])) for x in (q, k, v))
+    nb, n, d = qa.shape
+    out = np.zeros_like(qa)
+    for r0 in range(0, n, block):
+        qb = qa[:, r0:r0 + block]
+        rows = qb.shape[1]
+        m_run = np.full((nb, rows, 1), -np.inf)
+        l_run = np.zeros((nb, rows, 1))
+        o_run = np.zeros((nb, rows, d))
+        for c0 in range(0, n, block):
+            s = np.matmul(qb, np.swapaxes(ka[:, c0:c0 + block], 1, 2)) * scale
+            m_new = np.maximum(m_run, s.max(axis=-1, keepdims=True))
+            w = np.exp(s - m_new)
+            a = np.exp(m_run - m_new)
+            l_new = a * l_run + w.sum(axis=-1, keepdims=True)
+            old = a * l_run * o_run if keep_old_sum else a * o_run
+            o_run = (old + np.matmul(w, va[:, c0:c0 + block])) / l_new
+            m_run, l_run = m_new, l_new
+        out[:, r0:r0 + block] = o_run
+    return out.reshape(q.shape)
+
+
+@pytest.mark.parametrize("N", [100, 256])
+def test_page_blockwise_code_is_exact_with_one_key_block(N):
+    """With every key in one block (N <= block size 256) the page's recurrence is the plain softmax and equals the
+    oracle to rounding."""
+    q, k, v = ai.make_qkv(2, 2, N, 64, seed=40 + N, dtype="f32")
+    sc = ai.default_scale(64)
+    o_ref, _ = oracle.attention(q, k, v, False, sc, threads=2)
+    np.testing.assert_allclose(_page_blockwise(q, k, v, sc, 256, keep_old_sum=False), o_ref, rtol=0, atol=1e-12)
+
+
+def test_page_blockwise_code_needs_the_old_sum_with_several_key_blocks():
+    """With three key blocks the printed update drifts from the oracle by far more than rounding, while the same
+    recurrence with the old sum kept (the reading followed by the oracle and the kernels) equals it."""
+    q, k, v = ai.make_qkv(2, 2, 700, 64, seed=47, dtype="f32")
+    sc = ai.default_scale(64)
+    o_ref, _ = oracle.attention(q, k, v, False, sc, threads=2)
+    printed = _page_blockwise(q, k, v, sc, 256, keep_old_sum=False)
+    corrected = _page_blockwise(q, k, v, sc, 256, keep_old_sum=True)
+    assert np.abs(printed - o_ref).max() > 1e-3
+    np.testing.assert_allclose(corrected, o_ref, rtol=0, atol=1e-12)
+    # rows of the first query block see all three key blocks; the printed result is off there too
+    assert np.abs(printed[:, :, :256] - o_ref[:, :, :256]).max() > 1e-3
