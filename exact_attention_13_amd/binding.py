@@ -24,8 +24,9 @@ FA_ERR_ALIGN = 4
 FA_ERR_ARG = 5
 FA_ERR_ALIAS = 6
 FA_ERR_HIP = 7
+FA_ERR_SCRATCH = 8
 
-EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_kpad",
+EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_kpad", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_kpad",
            "fa_bwd_varlen", "fa_bwd_workspace_bytes", "fa_fwd_f32", "fa_fwd_instance", "fa_strerror", "fa_version")
 
 if not _LIB_PATH.exists():
@@ -47,6 +48,8 @@ _lib.fa_fwd_fp8.restype = _I
 _lib.fa_fwd_fp8.argtypes = [_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _P]
 _lib.fa_bwd.restype = _I
 _lib.fa_bwd.argtypes = [_P] * 10 + [_I] * 6 + [ctypes.c_float, _P]
+_lib.fa_bwd_noalloc.restype = _I
+_lib.fa_bwd_noalloc.argtypes = [_P] * 9 + [_I] * 6 + [ctypes.c_float, _P]
 _lib.fa_bwd_kpad.restype = _I
 _lib.fa_bwd_kpad.argtypes = [_P] * 11 + [_I] * 6 + [ctypes.c_float, _P]
 _lib.fa_bwd_varlen.restype = _I
@@ -103,6 +106,12 @@ def fa_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int
     """Raw entry point: gradients dq [B,H,N,d], dk, dv [B,H_kv,N,d] (bf16) of the forward for upstream dout;
     workspace: fa_bwd_workspace_bytes(B, H, H_kv, N, d) bytes of device memory."""
     return _lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H_kv, N, d, causal, scale, stream)
+
+
+def fa_bwd_noalloc(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, B: int, H: int,
+                   H_kv: int, N: int, d: int, causal: int, scale: float, stream: int) -> int:
+    """Raw entry point: fa_bwd with the library's own scratch buffer as the workspace. Returns the FA_* code."""
+    return _lib.fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, causal, scale, stream)
 
 
 def fa_bwd_kpad(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int, workspace: int,

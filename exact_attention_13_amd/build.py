@@ -18,7 +18,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libfa.so"
 SOURCES = [CSRC / "fa_fwd_kernel.hip", CSRC / "fa_fwd_fp8_kernel.hip", CSRC / "fa_bwd_kernel.hip",
-           CSRC / "fa_api.hip"]
+           CSRC / "fa_scratch.hip", CSRC / "fa_api.hip"]
 PROBE_LIB = PKG / "libfa_probe.so"
 PROBE_SOURCES = [CSRC / "fa_probe.hip"]
 ARCH = "gfx950"

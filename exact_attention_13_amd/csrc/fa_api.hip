@@ -67,7 +67,7 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, c
 
 // Checks of the gradient call: the forward's shape rules, then the nine tensors and the workspace.
 int validate_bwd(const void* const* in, int n_in, void* const* out, int n_out, const float* lse, const float* ws,
-                 int B, int H, int Hkv, int N, int d, int causal, float scale, bool* empty) {
+                 bool with_ws, int B, int H, int Hkv, int N, int d, int causal, float scale, bool* empty) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0 || Hkv < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
@@ -83,22 +83,23 @@ int validate_bwd(const void* const* in, int n_in, void* const* out, int n_out, c
     if (!in[i]) return FA_ERR_NULL;
   for (int i = 0; i < n_out; ++i)
     if (!out[i]) return FA_ERR_NULL;
-  if (!lse || !ws) return FA_ERR_NULL;
+  if (!lse || (with_ws && !ws)) return FA_ERR_NULL;
   for (int i = 0; i < n_in; ++i)
     if ((uintptr_t)in[i] & 15) return FA_ERR_ALIGN;
   for (int i = 0; i < n_out; ++i)
     if ((uintptr_t)out[i] & 15) return FA_ERR_ALIGN;
-  if (((uintptr_t)lse & 3) || ((uintptr_t)ws & 15)) return FA_ERR_ALIGN;
+  if (((uintptr_t)lse & 3) || (with_ws && ((uintptr_t)ws & 15))) return FA_ERR_ALIGN;
   return FA_OK;
 }
 
+// with_ws false: the workspace is the library's scratch buffer (fa_bwd_noalloc), looked up after every check.
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
-            void* dk, void* dv, float* workspace, const int* kv_len, bool with_len, int B, int H, int H_kv, int N,
-            int d, int causal, float scale, hipStream_t stream) {
+            void* dk, void* dv, float* workspace, bool with_ws, const int* kv_len, bool with_len, int B, int H,
+            int H_kv, int N, int d, int causal, float scale, hipStream_t stream) {
   const void* in[] = {q, k, v, o, dout};
   void* out[] = {dq, dk, dv};
   bool empty = false;
-  int rc = validate_bwd(in, 5, out, 3, lse, workspace, B, H, H_kv, N, d, causal, scale, &empty);
+  int rc = validate_bwd(in, 5, out, 3, lse, workspace, with_ws, B, H, H_kv, N, d, causal, scale, &empty);
   if (rc != FA_OK || empty) return rc;
   if (with_len && !kv_len) return FA_ERR_NULL;
   if (with_len && ((uintptr_t)kv_len & 3)) return FA_ERR_ALIGN;
@@ -106,15 +107,21 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   // workspace
   const size_t tq = (size_t)B * H * N * d * 2, tk = (size_t)B * H_kv * N * d * 2, tl = (size_t)B * H * N * 4;
   const size_t tw = fa::bwd_workspace_bytes(B, H, H_kv, N, d);
+  if (!with_ws && tw > fa::kScratchBytes) return FA_ERR_SCRATCH;
   const void* rin[] = {q, k, v, o, dout, lse, kv_len};
   const size_t nin[] = {tq, tk, tk, tq, tq, tl, with_len ? (size_t)B * sizeof(int) : 0};
   void* rout[] = {dq, dk, dv, workspace};
-  const size_t nout[] = {tq, tk, tk, tw};
+  const size_t nout[] = {tq, tk, tk, with_ws ? tw : 0};  // the scratch buffer is the library's own memory
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 7; ++j)
       if (overlaps(rout[i], nout[i], rin[j], nin[j])) return FA_ERR_ALIAS;
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(rout[i], nout[i], rout[j], nout[j])) return FA_ERR_ALIAS;
+  }
+  if (!with_ws) {
+    void* p = nullptr;
+    if (fa::scratch_address(stream, &p) != hipSuccess) return FA_ERR_HIP;
+    workspace = (float*)p;
   }
   const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H_kv, N, d,
                                            causal != 0, scale, with_len ? kv_len : nullptr, stream);
@@ -208,14 +215,21 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* workspace, int B, int H, int H_kv, int N, int d, int causal, float scale,
            hipStream_t stream) {
-  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, nullptr, false, B, H, H_kv, N, d, causal, scale,
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, true, nullptr, false, B, H, H_kv, N, d, causal, scale,
+                 stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, int causal, float scale,
+                   hipStream_t stream) {
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, false, nullptr, false, B, H, H_kv, N, d, causal, scale,
                  stream);
 }
 
 int fa_bwd_kpad(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                 void* dq, void* dk, void* dv, float* workspace, const int* kv_len, int B, int H, int H_kv, int N, int d,
                 int causal, float scale, hipStream_t stream) {
-  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, kv_len, true, B, H, H_kv, N, d, causal, scale,
+  return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, true, kv_len, true, B, H, H_kv, N, d, causal, scale,
                  stream);
 }
 
@@ -287,6 +301,9 @@ const char* fa_strerror(int code) {
     case FA_ERR_ARG: return "bad argument: scales must be finite and > 0, causal must be 0 or 1";
     case FA_ERR_ALIAS: return "an output (o, lse, dq, dk, dv, workspace) overlaps an input or another output";
     case FA_ERR_HIP: return "the HIP runtime reported an error when launching the kernel";
+    case FA_ERR_SCRATCH:
+      return "fa_bwd_noalloc: the gradient workspace of this problem exceeds the library's 64 MiB scratch buffer "
+             "(use fa_bwd with a caller-allocated workspace)";
     default: return "unknown error code";
   }
 }

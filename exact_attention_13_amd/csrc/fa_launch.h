@@ -52,6 +52,12 @@ inline int bwd_head_split(int B, int H, int Hkv, int N) {
 inline size_t bwd_planes_bytes(int B, int H, int N) {
   return (size_t)B * (size_t)H * (size_t)((N + 127) / 128 * 128) * 2 * sizeof(float);
 }
+// The library's own device scratch buffer (fa_scratch.hip): the gradient workspace of fa_bwd_noalloc, for callers
+// that cannot allocate. One copy per device, kept until the process ends.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+// Device address of the scratch buffer on the device `stream` belongs to (the current device for the null stream),
+// looked up once per device with that device current.
+hipError_t scratch_address(hipStream_t stream, void** out);
 inline size_t bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
   const int s = bwd_head_split(B, H, Hkv, N);
   const size_t parts = s > 1 ? 2 * (size_t)s * B * Hkv * (size_t)N * d * sizeof(float) : 0;

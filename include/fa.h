@@ -63,6 +63,7 @@ extern "C" {
 #define FA_ERR_ARG 5     /* scale not finite or not > 0, or causal not 0/1 */
 #define FA_ERR_ALIAS 6   /* an output overlaps an input or another output */
 #define FA_ERR_HIP 7     /* the HIP runtime reported an error at launch */
+#define FA_ERR_SCRATCH 8 /* fa_bwd_noalloc: the problem's workspace exceeds the library's scratch buffer */
 
 /*
  * fa_fwd -- bf16 inputs and output, fp32 accumulation and fp32 lse.
@@ -176,6 +177,33 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* workspace, int B, int H, int H_kv, int N, int d, int causal, float scale,
            hipStream_t stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code recorded into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * static device buffer of the library instead of an argument.
+ *   Arguments as fa_bwd, without workspace.
+ *   Limit: the workspace fa_bwd_workspace_bytes(B, H, H_kv, N, d) would
+ *   report must fit in 64 MiB (67108864 bytes); larger problems return
+ *   FA_ERR_SCRATCH before any HIP call (e.g. B*H*N up to ~8.4M query rows
+ *   when the dk/dv work needs no split; one key/value head serving 32 query
+ *   heads of N = 16384 at d = 128 needs 68 MiB and is refused).
+ * The buffer is a file-scope device array: every GPU the library runs on holds
+ * its own 64 MiB copy from the library's first kernel launch on that GPU until
+ * the process ends. Its device address is looked up once per GPU (on the
+ * first fa_bwd_noalloc call for a stream of that GPU, a HIP call that can
+ * fail with FA_ERR_HIP); nothing is allocated, and the call never frees or
+ * allocates memory. All calls on one GPU share the buffer, which keeps the
+ * last call's contents (no kernel needs it cleared: every value the kernels
+ * read is written earlier in the same call): calls that can overlap on one
+ * GPU -- on different streams, or from several host threads without ordering
+ * -- race on it and give wrong results. Order them on one stream, or use
+ * fa_bwd with a workspace per stream. Errors otherwise as fa_bwd.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, int causal, float scale,
+                   hipStream_t stream);
 
 /*
  * fa_bwd_kpad -- fa_bwd for a forward call made with fa_fwd_kpad: the

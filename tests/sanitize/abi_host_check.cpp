@@ -50,8 +50,11 @@ int main() {
                     64, 0, sc, nullptr) == FA_OK);
   CHECK(fa_bwd_varlen(at(0), at(1), at(2), at(3), atf(4), at(5), at(6), at(7), at(8), atf(9), ati(10), 2, 4, 1, 500,
                       300, 128, 1, sc, nullptr) == FA_OK);
+  CHECK(fa_bwd_noalloc(at(0), at(1), at(2), at(3), atf(4), at(5), at(6), at(7), at(8), 2, 16, 16, 4096, 128, 0, sc,
+                       nullptr) == FA_OK);
+  CHECK(fa::g_last[0] == 32 && fa::g_last[1] == 4096);
   const int calls = fa::g_calls;
-  CHECK(calls == 9);
+  CHECK(calls == 10);
 
   // ---- the largest accepted sizes, and one past them
   CHECK(fwd(65535, 1, 1 << 30, 128, 1, sc) == FA_OK);
@@ -116,6 +119,15 @@ int main() {
   CHECK(fa_bwd_varlen(at(0), at(1), at(2), at(3), atf(4), at(5), at(6), at(7), at(8), atf(9), ati(10), 2, 4, 1, 500,
                       (1 << 28) + 1, 128, 1, sc, nullptr) == FA_ERR_SHAPE);
   CHECK(fa_fwd_fp8(at(0), at(1), at(2), at(3), atf(4), 0.f, 1.f, 1.f, 1, 2, 64, 128, 1, sc, nullptr) == FA_ERR_ARG);
+  // the no-allocation gradient call: the scratch limit, then the checks of fa_bwd
+  CHECK(fa_bwd_noalloc(at(0), at(1), at(2), at(3), atf(4), at(5), at(6), at(7), at(8), 1, 32, 1, 16384, 128, 1, sc,
+                       nullptr) == FA_ERR_SCRATCH);
+  CHECK(fa_bwd_noalloc(at(0), at(1), at(2), at(3), atf(4), at(5), nullptr, at(7), at(8), 1, 4, 4, 64, 64, 0, sc,
+                       nullptr) == FA_ERR_NULL);
+  CHECK(fa_bwd_noalloc(at(0), at(1), at(2), at(3), atf(4), at(5), at(1), at(7), at(8), 1, 4, 4, 64, 64, 0, sc,
+                       nullptr) == FA_ERR_ALIAS);
+  CHECK(fa_bwd_noalloc(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 4, 4, 64,
+                       64, 0, sc, nullptr) == FA_OK);
   // no rejected call reached a launcher
   CHECK(fa::g_calls == calls + 1);  // + the largest accepted forward above
 

@@ -1,6 +1,8 @@
 // launch_stubs.cpp -- host-only stand-ins for the kernel launchers of fa_launch.h, for the sanitizer build of the
 // C ABI (fa_api.hip compiled with g++ -fsanitize=address,undefined and no GPU code). Each records the call and
 // its sizes and returns hipSuccess; nothing touches a device.
+#include <stdint.h>
+
 #include "fa_launch.h"
 
 namespace fa {
@@ -40,4 +42,12 @@ hipError_t launch_bwd_varlen_bf16(const void*, const void*, const void*, const v
   return record(B * H, T_total, d, causal, Hkv, max_seqlen);
 }
 const char* fwd_instance_bf16(int, int, int, bool, bool) { return "stub"; }
+}  // namespace fa
+
+namespace fa {
+// stand-in for the scratch buffer's device address (never dereferenced on the host)
+hipError_t scratch_address(hipStream_t, void** out) {
+  *out = (void*)(uintptr_t)(uint64_t(0x3f) << 56);
+  return hipSuccess;
+}
 }  // namespace fa

@@ -56,9 +56,23 @@ def test_probe_library_exports_what_its_header_declares():
 
 def test_version_and_strerror():
     assert fa.fa_version() == 10700
-    for code in range(8):
+    for code in range(9):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
     assert fa.fa_strerror(99) == "unknown error code"
+
+
+def test_noalloc_gradient_refuses_problems_beyond_its_scratch_buffer():
+    """fa_bwd_noalloc checks everything fa_bwd checks, then that the workspace fits the library's 64 MiB buffer,
+    all before any HIP call."""
+    args = (A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x5000000, B_, B_ + 0x10000000,
+            B_ + 0x20000000)
+    assert fa.fa_bwd_workspace_bytes(1, 32, 1, 16384, 128) > 64 << 20  # one key/value head: split dk/dv partials
+    assert fa.fa_bwd_noalloc(*args, 1, 32, 1, 16384, 128, 1, 0.088, 0) == fa.FA_ERR_SCRATCH
+    assert "scratch" in fa.fa_strerror(fa.FA_ERR_SCRATCH)
+    assert fa.fa_bwd_noalloc(*args[:6], 0, *args[7:], 1, 4, 4, 64, 64, 0, 0.125, 0) == fa.FA_ERR_NULL
+    assert fa.fa_bwd_noalloc(*args, 1, 4, 4, 64, 96, 0, 0.125, 0) == fa.FA_ERR_HEADDIM
+    assert fa.fa_bwd_noalloc(*args, 1, 4, 4, 64, 64, 0, 0.0, 0) == fa.FA_ERR_ARG
+    assert fa.fa_bwd_noalloc(*args, 0, 4, 4, 64, 64, 0, 0.125, 0) == fa.FA_OK  # empty: nothing enqueued
 
 
 def test_instance_query():
