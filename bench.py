@@ -75,6 +75,14 @@ PROFILE_COMMANDS = {
     "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA "
           "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
           "-d gpurun_out/prof_{w}_sq -o run -- python bench.py --workload {w} --pmc-pass",
+    # where the wave-cycles go: waiting, issuing, co-issue of vector instructions with busy matrix cores
+    "stall": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+             "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+             "-d gpurun_out/prof_{w}_stall -o run -- python bench.py --workload {w} --pmc-pass",
+    # L2 hit rate, dual-issued vector cycles, transcendental instructions, LDS data-queue pressure
+    "l2": "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum SQ_ACTIVE_INST_VALU2 SQ_INSTS_VALU_TRANS_F32 SQ_LDS_DATA_FIFO_FULL "
+          "SQ_INSTS_LDS SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+          "-d gpurun_out/prof_{w}_l2 -o run -- python bench.py --workload {w} --pmc-pass",
 }
 
 
@@ -650,9 +658,51 @@ MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (traced average x 2.4 GHz) = 
 over GRBM_GUI_ACTIVE / 8 (the GPU cycles counted during the kernel, summed over the 8 XCDs) = {100 * mfma_busy / n_simd / (gui / 8):.1f} %.
 Clock during the kernel, GRBM_GUI_ACTIVE / 8 / traced average: {gui / 8 / (avg_us * 1e-6) / 1e9:.2f} GHz.
 LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active, 1):.1f} %.
-"""
+""" + _cycle_breakdown(w, dirs, kname, avg_us)
     (PROFILES / f"{w.name}_rocprof.md").write_text(md)
     print(md)
+
+
+def _cycle_breakdown(w, dirs, kname, avg_us):
+    """Where the wave-cycles of the kernel go (the "stall" and "l2" passes), as markdown; empty if not run."""
+    if not (glob.glob(os.path.join(dirs["stall"], "**", "*counter_collection.csv"), recursive=True) and
+            glob.glob(os.path.join(dirs["l2"], "**", "*counter_collection.csv"), recursive=True)):
+        return ""
+    st, l2 = _counters(dirs["stall"]), _counters(dirs["l2"])
+    g = lambda c, src=st: _pick(src, c, kname)  # noqa: E731
+    wave_cyc = 4 * g("SQ_WAVE_CYCLES")          # quad-cycles, summed over waves
+    wait_any, wait_inst = 4 * g("SQ_WAIT_ANY"), 4 * g("SQ_WAIT_INST_ANY")
+    act_any, act_valu, act_lds = 4 * g("SQ_ACTIVE_INST_ANY"), 4 * g("SQ_ACTIVE_INST_VALU"), 4 * g("SQ_ACTIVE_INST_LDS")
+    coexec = g("SQ_VALU_MFMA_COEXEC_CYCLES")
+    busy = g("SQ_VALU_MFMA_BUSY_CYCLES", l2)
+    gui = g("GRBM_GUI_ACTIVE", l2)
+    hit, miss = g("TCC_HIT_sum", l2), g("TCC_MISS_sum", l2)
+    valu2 = 4 * g("SQ_ACTIVE_INST_VALU2", l2)
+    trans = g("SQ_INSTS_VALU_TRANS_F32", l2)
+    fifo = g("SQ_LDS_DATA_FIFO_FULL", l2)
+    simd_cyc = gui / 8 * 1024   # SIMD-cycles during the kernel (GPU cycles per XCD x 1024 SIMDs)
+    rows = [("SQ_WAVE_CYCLES x4 (wave-cycles)", wave_cyc, ""),
+            ("SQ_WAIT_ANY x4", wait_any, f"{100 * wait_any / wave_cyc:.1f} % of wave-cycles waiting (s_waitcnt, barrier)"),
+            ("SQ_WAIT_INST_ANY x4", wait_inst, f"{100 * wait_inst / wave_cyc:.1f} % of wave-cycles waiting to issue"),
+            ("SQ_ACTIVE_INST_ANY x4", act_any, f"{100 * act_any / wave_cyc:.1f} % of wave-cycles issuing"),
+            ("SQ_ACTIVE_INST_VALU x4", act_valu, f"{100 * act_valu / wave_cyc:.1f} % of wave-cycles on vector/matrix instructions"),
+            ("SQ_ACTIVE_INST_LDS x4", act_lds, f"{100 * act_lds / wave_cyc:.1f} % of wave-cycles on LDS instructions"),
+            ("SQ_VALU_MFMA_BUSY_CYCLES", busy, f"{100 * busy / simd_cyc:.1f} % of SIMD-cycles"),
+            ("SQ_VALU_MFMA_COEXEC_CYCLES", coexec, f"{100 * coexec / busy:.1f} % of the matrix-busy cycles also issue a vector instruction"),
+            ("SQ_ACTIVE_INST_VALU2 x4", valu2, f"{100 * valu2 / simd_cyc:.1f} % of SIMD-cycles issue two vector instructions"),
+            ("SQ_INSTS_VALU_TRANS_F32", trans, "transcendental (exp2, log, rcp) instructions"),
+            ("SQ_LDS_DATA_FIFO_FULL", fifo, f"{100 * fifo / (gui / 8 * 256):.2f} % of CU-cycles with the LDS data queue full"),
+            ("TCC_HIT_sum / TCC_MISS_sum", f"{hit:.4g} / {miss:.4g}", f"L2 hit rate {100 * hit / max(hit + miss, 1):.1f} %")]
+    body = "\n".join(f"| {n} | {v if isinstance(v, str) else f'{v:.4g}'} | {d} |" for n, v, d in rows)
+    return f"""
+## Where the cycles go (SQ and TCC counters, per dispatch)
+
+Wave-cycles are summed over every wave (two waves share each SIMD); SIMD-cycles = GRBM_GUI_ACTIVE / 8 x 1024 SIMDs.
+
+| counter | value | share |
+|---|---|---|
+{body}
+"""
 
 
 def write_profiles_fp8(w):
