@@ -140,6 +140,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     qb = __builtin_amdgcn_readfirstlane(CAUSAL ? __shfl(nb, b) - 1 - kb : kb);
   } else {
     map_workgroup(blockIdx.x + nq * blockIdx.y, nq, BH, group, CAUSAL, bh, qb);
+    if constexpr (CAUSAL && NW == 4 && SPL == 2) {
+      // The 64-row causal shape runs its whole grid at once, two workgroups per CU; a CU receives the workgroups
+      // at dispatch positions L and L + total/2. The second half of the longest-first order is reversed, so those
+      // two take complementary query blocks (qb and nq-1-qb) and every CU gets about the same work.
+      if (qb < nq / 2) qb = nq / 2 - 1 - qb;
+    }
   }
 
   // Packed sequences: this head's sequence starts at token `start` and has Ns tokens (offsets clamped to
@@ -643,19 +649,26 @@ static hipError_t launch_f32(const float* q, const float* k, const float* v, flo
 //  * split: otherwise (too few rows to give every SIMD two waves of 32 rows): 8 waves x 128 rows, the two waves
 //    of each 32-row group taking the two 64-key halves of every 128-key tile and merging their partial (m, l, O)
 //    at the end. Short sequences of few heads (and long ones of very few) get two waves per SIMD this way.
-// The three differ in where the exponent reference may move and in the order of the sums, so their outputs can
-// differ in the last bit; each is deterministic, and the packed entry point chooses the same way from max_seqlen.
+//  * split64 (causal, d = 64, not for packed batches): the split shape on 64 rows and 4 waves, when its grid fits
+//    on the chip at two workgroups per CU (at most 512): every 64-row block is resident at once and each CU pairs a
+//    long causal block with a short one (see the mapping in the kernel). Same arithmetic per row as the split
+//    shape, so the same bits.
+// Wide, narrow and split differ in where the exponent reference may move and in the order of the sums, so their
+// outputs can differ in the last bit; each is deterministic, and the packed entry point chooses among them the same
+// way from max_seqlen.
 constexpr long long kTwoPerCu = 512;
-enum class Shape { kWide = 0, kNarrow = 1, kSplit = 2 };
-static Shape fwd_shape(int N, int BH) {
+enum class Shape { kWide = 0, kNarrow = 1, kSplit = 2, kSplit64 = 3 };
+static Shape fwd_shape(int N, int BH, int d, bool causal, bool packed) {
   if ((long long)((N + 255) / 256) * BH >= kTwoPerCu) return Shape::kWide;
   if ((long long)((N + 127) / 128) * BH >= kTwoPerCu) return Shape::kNarrow;
+  if (causal && d == 64 && !packed && (long long)((N + 63) / 64) * BH <= kTwoPerCu) return Shape::kSplit64;
   return Shape::kSplit;
 }
 // (NW, KT, SPL) of each shape; the ring always has 2 stages.
 #define FA_WIDE 8, 2, 1
 #define FA_NARROW 4, 1, 1
 #define FA_SPLIT 8, 2, 2
+#define FA_SPLIT64 4, 2, 2
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
                            int N, int d, bool causal, float scale, const int* kv_len, hipStream_t stream) {
@@ -666,9 +679,11 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   (d == 64 ? (causal ? FA_LAUNCH(64, true, NW, KT, SPL) : FA_LAUNCH(64, false, NW, KT, SPL)) \
            : (causal ? FA_LAUNCH(128, true, NW, KT, SPL) : FA_LAUNCH(128, false, NW, KT, SPL)))
 #define FA_D(...) FA_D2(__VA_ARGS__)
-  switch (fwd_shape(N, BH)) {
+  switch (fwd_shape(N, BH, d, causal, false)) {
     case Shape::kWide: return FA_D(FA_WIDE);
     case Shape::kNarrow: return FA_D(FA_NARROW);
+    case Shape::kSplit64: return launch_bf16<64, true, 4, 2, 2, false, 2>(q, k, v, o, lse, BH, N, scale, H, group,
+                                                                         kv_len, stream);
     default: return FA_D(FA_SPLIT);
   }
 #undef FA_D
@@ -687,7 +702,7 @@ hipError_t launch_fwd_varlen_bf16(const void* q, const void* k, const void* v, v
   (d == 64 ? (causal ? FA_LAUNCH(64, true, NW, KT, SPL) : FA_LAUNCH(64, false, NW, KT, SPL)) \
            : (causal ? FA_LAUNCH(128, true, NW, KT, SPL) : FA_LAUNCH(128, false, NW, KT, SPL)))
 #define FA_D(...) FA_D2(__VA_ARGS__)
-  switch (fwd_shape(N, BH)) {
+  switch (fwd_shape(N, BH, d, causal, true)) {
     case Shape::kWide: return FA_D(FA_WIDE);
     case Shape::kNarrow: return FA_D(FA_NARROW);
     default: return FA_D(FA_SPLIT);
@@ -707,14 +722,17 @@ const char* fwd_instance_bf16(int BH, int N, int d, bool causal, bool packed) {
    {{FA_NAME(128, false, false, S), FA_NAME(128, false, true, S)},                               \
     {FA_NAME(128, true, false, S), FA_NAME(128, true, true, S)}}}
   static const char* const names[3][2][2][2] = {FA_NAMES(FA_WIDE), FA_NAMES(FA_NARROW), FA_NAMES(FA_SPLIT)};
+  const Shape shape = fwd_shape(N, BH, d, causal, packed);
+  if (shape == Shape::kSplit64) return FA_NAME(64, true, false, FA_SPLIT64);
 #undef FA_NAMES
 #undef FA_NAME
 #undef FA_NAME2
-  return names[(int)fwd_shape(N, BH)][d == 128][causal][packed];
+  return names[(int)shape][d == 128][causal][packed];
 }
 #undef FA_WIDE
 #undef FA_NARROW
 #undef FA_SPLIT
+#undef FA_SPLIT64
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, hipStream_t stream) {

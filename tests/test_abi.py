@@ -89,6 +89,12 @@ def test_instance_query():
     assert fa.fa_fwd_instance(1, 127, 1024, 64, 0, 0).endswith("4, 2, 1, false, 1>")
     assert fa.fa_fwd_instance(1, 64, 1024, 64, 0, 0).endswith("4, 2, 1, false, 1>")
     assert fa.fa_fwd_instance(1, 63, 1024, 64, 0, 0).endswith("8, 2, 2, false, 2>")
+    # causal d = 64 grids whose 64-row blocks fit two per CU (16 x 32 = 512): the 64-row split shape; not at d = 128,
+    # not past 512 such blocks, not for packed batches
+    assert fa.fa_fwd_instance(4, 8, 1024, 64, 1, 0) == "fa_fwd_bf16_kernel<64, true, 4, 2, 2, false, 2>"
+    assert fa.fa_fwd_instance(4, 8, 1024, 128, 1, 0).endswith("8, 2, 2, false, 2>")
+    assert fa.fa_fwd_instance(1, 33, 1024, 64, 1, 0).endswith("8, 2, 2, false, 2>")
+    assert fa.fa_fwd_instance(4, 8, 1024, 64, 1, 1).endswith("8, 2, 2, true, 2>")
     for bad in ((0, 1, 64, 64, 0, 0), (1, 0, 64, 64, 0, 0), (1, 1, 0, 64, 0, 0), (1, 1, 64, 96, 0, 0),
                 (1, 1, 64, 64, 2, 0), (1, 1, 64, 64, 0, 2), (70000, 1, 64, 64, 0, 0), (1, 1, (1 << 30) + 1, 64, 0, 0)):
         assert fa.fa_fwd_instance(*bad) is None, bad

@@ -4,7 +4,9 @@ The library picks one of three shapes from the grid size alone (fa_fwd_instance 
   * wide:   8 waves x 32 rows, 128-key tiles, when ceil(N/256) * B*H >= 512;
   * narrow: 4 waves x 32 rows, 64-key tiles, when ceil(N/128) * B*H >= 512 but the wide grid is smaller;
   * split:  8 waves on 128 rows, the two waves of each 32-row group taking the two 64-key halves of every
-            128-key tile and merging their partial (m, l, o) at the end, otherwise.
+            128-key tile and merging their partial (m, l, o) at the end, otherwise;
+  * split64: causal d = 64 grids whose 64-row blocks fit at two workgroups per CU (ceil(N/64) * B*H <= 512): the
+            split shape on 64 rows and 4 waves, complementary query blocks paired on each CU.
 Each test asks the library which instance it launches for its sizes, so a change of the rule cannot silently move
 a case to another shape. Every shape runs at d in {64, 128}, causal and not, with N = 1000 (not a multiple of any
 tile), and with key padding, grouped heads and packed sequences. Bar: max |o - o_oracle| and max |lse -
@@ -21,9 +23,22 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
 N = 1000
-# (B, H) that put B*H heads of N = 1000 rows on each shape: ceil(1000/256) = 4, ceil(1000/128) = 8
-HEADS = {"wide": (2, 64), "narrow": (2, 32), "split": (2, 4)}
-SIGNATURE = {"wide": "8, 2, 2, {p}, 1>", "narrow": "4, 2, 1, {p}, 1>", "split": "8, 2, 2, {p}, 2>"}
+# (B, H) that put B*H heads of N = 1000 rows on each shape: ceil(1000/256) = 4, ceil(1000/128) = 8,
+# ceil(1000/64) = 16; causal d = 64 takes split64 while 16 * B*H <= 512, so its split cases use 48 heads
+HEADS = {"wide": (2, 64), "narrow": (2, 32), "split": (2, 4), "split64": (2, 4)}
+SIGNATURE = {"wide": "8, 2, 2, {p}, 1>", "narrow": "4, 2, 1, {p}, 1>", "split": "8, 2, 2, {p}, 2>",
+             "split64": "4, 2, 2, {p}, 2>"}
+
+
+def _heads(shape, d, causal):
+    if shape == "split" and d == 64 and causal:
+        return (2, 24)
+    return HEADS[shape]
+
+
+# (shape, d, causal) of every instance a non-packed call can launch
+CASES = [(sh, d, c) for sh in ("wide", "narrow", "split") for d in (64, 128) for c in (False, True)] + \
+    [("split64", 64, True)]
 
 
 @pytest.fixture(scope="module")
@@ -56,11 +71,9 @@ def _compare(label, o, lse, q, k, v, causal, scale, kv_len=None):
     assert el <= TOL, f"{label}: lse error {el}"
 
 
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("shape", ["wide", "narrow", "split"])
+@pytest.mark.parametrize("shape,d,causal", CASES)
 def test_every_shape_every_row(fa, shape, d, causal):
-    B, H = HEADS[shape]
+    B, H = _heads(shape, d, causal)
     _expect_shape(fa, shape, B, H, N, d, causal)
     q, k, v = ai.make_qkv(B, H, N, d, seed=900 + 10 * d + causal, dtype="bf16")
     scale = ai.default_scale(d)
@@ -69,13 +82,13 @@ def test_every_shape_every_row(fa, shape, d, causal):
     _compare(f"{shape} d={d} causal={causal}", o, lse, q, k, v, causal, scale)
 
 
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", ["wide", "narrow", "split"])
-def test_every_shape_with_key_padding_and_grouped_heads(fa, shape, causal):
+@pytest.mark.parametrize("shape,d,causal", [(sh, 128, c) for sh in ("wide", "narrow", "split") for c in (False, True)]
+                         + [("split64", 64, True)])
+def test_every_shape_with_key_padding_and_grouped_heads(fa, shape, d, causal):
     """Per-batch key lengths (one that ends inside a 64-key part, one past the first tile) together with 4 query
     heads per key/value head."""
-    B, H = HEADS[shape]
-    Hkv, d = H // 4, 128
+    B, H = _heads(shape, d, causal)
+    Hkv = H // 4
     _expect_shape(fa, shape, B, H, N, d, causal)
     q, k, v = ai.make_qkv(B, H, N, d, seed=940 + causal, dtype="bf16", Hkv=Hkv)
     lens = [517, 40]
@@ -86,12 +99,12 @@ def test_every_shape_with_key_padding_and_grouped_heads(fa, shape, causal):
     _compare(f"{shape} kv_len={lens} H={H} Hkv={Hkv} causal={causal}", o, lse, q, k, v, causal, scale, kv_len=lens)
 
 
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", ["wide", "narrow", "split"])
+@pytest.mark.parametrize("shape,causal", [(sh, c) for sh in ("wide", "narrow", "split") for c in (False, True)]
+                         + [("split64", True)])
 def test_every_shape_multi_query(fa, shape, causal):
     """One key/value head for every query head of a batch (d = 64)."""
-    B, H = HEADS[shape]
     d = 64
+    B, H = _heads(shape, d, causal)
     _expect_shape(fa, shape, B, H, N, d, causal)
     q, k, v = ai.make_qkv(B, H, N, d, seed=950 + causal, dtype="bf16", Hkv=1)
     scale = ai.default_scale(d)
@@ -101,7 +114,7 @@ def test_every_shape_multi_query(fa, shape, causal):
 
 
 # Packed batches of 4 sequences, the longest 1000 tokens: max_seqlen = 1000 and B*H = 128, 64 or 8 heads pick the
-# shape.
+# shape (packed calls never take split64).
 VARLEN_H = {"wide": 32, "narrow": 16, "split": 2}
 
 
