@@ -188,16 +188,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
       const int kv0 = j * kBcT;
       if ((kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
+        // key kv0 + 32h + o (o = 64t + 16b + r) is visible iff key < N and (causal) key <= my_q, i.e. iff o <= lim
+        const int lim = (CAUSAL ? min(N - 1, my_q) : N - 1) - kv0 - 32 * h;
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kv0 + 64 * t + 32 * h + 16 * b + r;
-              const bool vis = (key < N) && (!CAUSAL || key <= my_q);
-              s[2 * t + b][r] = vis ? s[2 * t + b][r] : -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+              s[2 * t + b][r] = (64 * t + 16 * b + r <= lim) ? s[2 * t + b][r] : -INFINITY;
       }
       float mx = s[0][0];
 #pragma unroll
@@ -228,7 +227,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 1], c2, nb));
           const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 2], c2, nb));
           const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 3], c2, nb));
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          // the first conversion writes the low half of the word, the second the high half; the word starts as
+          // p0's bits (any value would do), so no register has to be cleared first
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
           word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
           pf[w] = word;
         }

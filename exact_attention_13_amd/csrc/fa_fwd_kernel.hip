@@ -298,14 +298,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto stats = [&](f32x16(&s)[2 * kWKT], int j) __attribute__((always_inline)) {
     const int kv0 = j * kBcT + kofs;  // first key of this wave's part of tile j
     if ((kv0 + kWKT * kBc > Nk) || (CAUSAL && kv0 + kWKT * kBc - 1 > q0w)) {
+      // key kv0 + 8h + o (o = 32b + 16(r/8) + r%8) is visible iff key < Nk and (causal) key <= my_q, i.e. iff
+      // o <= lim: one compare against a constant per score
+      const int lim = (CAUSAL ? min(Nk - 1, my_q) : Nk - 1) - kv0 - 8 * h;
 #pragma unroll
       for (int b = 0; b < 2 * kWKT; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * b + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool vis = (key < Nk) && (!CAUSAL || key <= my_q);
-          s[b][r] = vis ? s[b][r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) s[b][r] = (32 * b + 16 * (r >> 3) + (r & 7) <= lim) ? s[b][r] : -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
