@@ -656,7 +656,10 @@ HBM bandwidth at the traced average: {(k_read + k_write) / (avg_us * 1e-6) / 1e9
 
 MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (traced average x 2.4 GHz) = {100 * util:.1f} %;
 over GRBM_GUI_ACTIVE / 8 (the GPU cycles counted during the kernel, summed over the 8 XCDs) = {100 * mfma_busy / n_simd / (gui / 8):.1f} %.
-Clock during the kernel, GRBM_GUI_ACTIVE / 8 / traced average: {gui / 8 / (avg_us * 1e-6) / 1e9:.2f} GHz.
+Clock during the kernel, GRBM_GUI_ACTIVE / 8 / traced average: {gui / 8 / (avg_us * 1e-6) / 1e9:.2f} GHz.{
+    "" if gui / 8 / (avg_us * 1e-6) <= 2.45e9 else " Above the 2.4 GHz maximum: for a launch this short GRBM_GUI_ACTIVE"
+    " counts more than the kernel's own cycles (the counter run's dispatch and drain), so the shares over"
+    " GRBM_GUI_ACTIVE and over SIMD-cycles below understate it; the 2.4 GHz-based utilisation is the one to read."}
 LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active, 1):.1f} %.
 """ + _cycle_breakdown(w, dirs, kname, avg_us)
     (PROFILES / f"{w.name}_rocprof.md").write_text(md)
