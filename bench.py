@@ -169,13 +169,28 @@ def _caller(w, q, k, v, o, lse, lens, stream_handle):
     return call
 
 
-def time_workload(w, steps: int, warmup: int):
-    """Returns (wall_s for `steps` calls, per-launch durations in ms from HIP events on the launch stream)."""
+SETTLE_S = 0.3  # seconds of untimed back-to-back calls before a leg's warm-up
+
+
+def _time_calls(call, stream, steps: int, warmup: int, settle_s: float = 0.0):
+    """`warmup` untimed calls, then `steps` calls each bracketed by HIP events on `stream`, with a device
+    synchronisation before and after the timed ones. Returns (wall_s for the `steps` calls, per-call durations in ms).
+
+    With settle_s > 0 the call first runs back to back, untimed, for settle_s seconds. After an idle spell (the
+    seconds the host spends making a workload's inputs) the GPU's clock needs about a hundred launches of the
+    headline kernel (≈ 30 ms of load) to reach the level it then holds; the launches in between run up to 30 %
+    slower, and a few warm-up steps end inside that transient."""
     import torch
 
-    q, k, v, o, lse, lens = _device_inputs(w)
-    stream = torch.cuda.current_stream()
-    call = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
+    if settle_s > 0:
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + settle_s
+        batch = 1
+        while time.perf_counter() < t_end:
+            for _ in range(batch):
+                call()
+            torch.cuda.synchronize()
+            batch = min(2 * batch, 64)
     for _ in range(warmup):
         call()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -188,12 +203,41 @@ def time_workload(w, steps: int, warmup: int):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, [a.elapsed_time(b) for a, b in zip(starts, ends)]
+
+
+def clock_settle(w, launches: int = 300, idle_s: float = 2.0, trials: int = 2):
+    """Per-launch kernel times of workload w after `idle_s` seconds with the GPU idle: the means of each 20 launches
+    in order and the first 10 launches, per trial. Shows how long the clock takes to settle under load."""
+    import torch
+
+    q, k, v, o, lse, lens = _device_inputs(w)
+    stream = torch.cuda.current_stream()
+    call = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
+    out = []
+    for trial in range(trials):
+        torch.cuda.synchronize()
+        time.sleep(idle_s)
+        _, durs = _time_calls(call, stream, launches, 0)
+        out.append({"trial": trial, "idle_s": idle_s,
+                    "mean_ms_per_20": [round(statistics.fmean(durs[i:i + 20]), 4) for i in range(0, launches, 20)],
+                    "first10_ms": [round(d, 4) for d in durs[:10]]})
+    return out
+
+
+def time_workload(w, steps: int, warmup: int, settle_s: float = 0.0):
+    """Returns (wall_s for `steps` calls, per-launch durations in ms from HIP events on the launch stream)."""
+    import torch
+
+    q, k, v, o, lse, lens = _device_inputs(w)
+    stream = torch.cuda.current_stream()
+    call = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
+    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
     del q, k, v, o, lse, lens
     return wall, durs
 
 
-def time_backward(w, steps: int, warmup: int):
+def time_backward(w, steps: int, warmup: int, settle_s: float = 0.0):
     """Gradient call of workload w (bf16): (wall_s for `steps` calls, per-call durations in ms from HIP events).
     The forward runs once first to provide o and lse; dout is seeded N(0, 1)."""
     import torch
@@ -217,25 +261,13 @@ def time_backward(w, steps: int, warmup: int):
         rc = entry(*args)
         if rc != 0:
             raise RuntimeError(f"fa_bwd failed: {fa.fa_strerror(rc)}")
-    for _ in range(warmup):
-        call()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    durs = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
     del q, k, v, o, lse, dout, dq, dk, dv, ws
     return wall, durs
 
 
-def backward_record(w, steps: int, warmup: int):
-    wall, durs = time_backward(w, steps, warmup)
+def backward_record(w, steps: int, warmup: int, settle_s: float = 0.0):
+    wall, durs = time_backward(w, steps, warmup, settle_s)
     flops = 2.5 * w.flops
     mean = statistics.fmean(durs)
     return {"workload": w.name, "tflops": round(flops * steps / wall / 1e12, 2),
@@ -249,7 +281,7 @@ def backward_record(w, steps: int, warmup: int):
             "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}
 
 
-def fp8_record(w, steps: int, warmup: int):
+def fp8_record(w, steps: int, warmup: int, settle_s: float = 0.0):
     """fa_fwd_fp8 on workload w's shape with the seeded inputs quantized per tensor to float8_e4m3fn."""
     import torch
 
@@ -268,19 +300,7 @@ def fp8_record(w, steps: int, warmup: int):
         rc = fa.fa_fwd_fp8(*args)
         if rc != 0:
             raise RuntimeError(f"fa_fwd_fp8 failed: {fa.fa_strerror(rc)}")
-    for _ in range(warmup):
-        call()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
     mean = statistics.fmean(durs)
     return {"workload": w.name.replace("_bf16_", "_fp8_"), "dtype": "fp8 e4m3 (bf16 o)",
             "tflops": round(w.flops * steps / wall / 1e12, 2),
@@ -294,7 +314,7 @@ def fp8_record(w, steps: int, warmup: int):
             "kernel_src_sha256_16": kernel_src_hash(FP8_SRCS)}
 
 
-def varlen_record(w, steps: int, warmup: int):
+def varlen_record(w, steps: int, warmup: int, settle_s: float = 0.0):
     """fa_fwd_varlen on a packed variable-length workload (inputs resident on the device)."""
     import torch
 
@@ -313,19 +333,7 @@ def varlen_record(w, steps: int, warmup: int):
         rc = fa.fa_fwd_varlen(*args)
         if rc != 0:
             raise RuntimeError(f"fa_fwd_varlen failed: {fa.fa_strerror(rc)}")
-    for _ in range(warmup):
-        call()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
     mean = statistics.fmean(durs)
     return {"workload": w.name, "lens": list(w.lens), "H": w.H, "H_kv": w.Hk, "d": w.d, "causal": w.causal,
             "tflops": round(w.flops * steps / wall / 1e12, 2),
@@ -338,7 +346,7 @@ def varlen_record(w, steps: int, warmup: int):
             "kernel": "fa_fwd_bf16_kernel (VARLEN)", "kernel_src_sha256_16": kernel_src_hash()}
 
 
-def varlen_backward_record(w, steps: int, warmup: int):
+def varlen_backward_record(w, steps: int, warmup: int, settle_s: float = 0.0):
     """fa_bwd_varlen on a packed workload (o and lse from one fa_fwd_varlen call), FLOPs 2.5 x the forward's."""
     import torch
 
@@ -361,19 +369,7 @@ def varlen_backward_record(w, steps: int, warmup: int):
         rc = fa.fa_bwd_varlen(*args)
         if rc != 0:
             raise RuntimeError(f"fa_bwd_varlen failed: {fa.fa_strerror(rc)}")
-    for _ in range(warmup):
-        call()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
     mean = statistics.fmean(durs)
     flops = 2.5 * w.flops
     return {"workload": w.name, "call": "fa_bwd_varlen", "tflops": round(flops * steps / wall / 1e12, 2),
@@ -918,6 +914,10 @@ def main():
     ap.add_argument("--write-profiles-varlen", metavar="WORKLOAD", choices=sorted(ai.VARLEN_WORKLOADS))
     ap.add_argument("--write-profiles-fp8", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true")
+    ap.add_argument("--clock-settle", action="store_true",
+                    help="per-launch times of --workload after 2 s idle (300 launches, twice)")
+    ap.add_argument("--settle", type=float, default=SETTLE_S, metavar="SECONDS",
+                    help="untimed back-to-back calls before each leg's warm-up (0: time the leg as it comes)")
     args = ap.parse_args()
 
     if args.summarize:
@@ -953,10 +953,10 @@ def main():
         pmc_pass(w, reps=5)
         return 0
     if args.varlen_only:
-        print(json.dumps(varlen_record(ai.VARLEN_WORKLOADS[args.varlen_only], args.steps, args.warmup)), flush=True)
+        print(json.dumps(varlen_record(ai.VARLEN_WORKLOADS[args.varlen_only], args.steps, args.warmup, args.settle)), flush=True)
         return 0
     if args.fp8_only:
-        print(json.dumps(fp8_record(w, args.steps, args.warmup)), flush=True)
+        print(json.dumps(fp8_record(w, args.steps, args.warmup, args.settle)), flush=True)
         return 0
     if args.bwd_pmc_pass:
         bwd_pmc_pass(w, reps=3)
@@ -964,11 +964,19 @@ def main():
     if args.fp8_pmc_pass:
         fp8_pmc_pass(w, reps=5)
         return 0
+    if args.clock_settle:
+        for rec in clock_settle(w):
+            print(json.dumps({"workload": w.name, **rec}), flush=True)
+        return 0
     if args.bwd_only:
-        print(json.dumps(backward_record(w, args.steps, args.warmup)), flush=True)
+        print(json.dumps(backward_record(w, args.steps, args.warmup, args.settle)), flush=True)
         return 0
 
-    wall, durs = time_workload(w, args.steps, args.warmup)
+    # The headline leg is timed twice on the same shape: as it comes (the W warm-up steps straight after the host
+    # has made the inputs, the GPU idle until then), reported as "cold_start", and after `--settle` seconds of
+    # untimed back-to-back calls, which gives `value`: the throughput of a GPU kept busy.
+    cold_wall, cold_durs = time_workload(w, args.steps, args.warmup)
+    wall, durs = time_workload(w, args.steps, args.warmup, args.settle)
     ms_step = wall / args.steps * 1e3
     value = w.flops * args.steps / wall / 1e12
     k_mean = statistics.fmean(durs)
@@ -991,6 +999,10 @@ def main():
                      "kernel": kernel_name(w), "flops_per_launch": w.flops,
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
         "kernel_src_sha256_16": kernel_src_hash(),
+        "settle_s": args.settle,
+        "cold_start": {"value": round(w.flops * args.steps / cold_wall / 1e12, 2),
+                       "ms_per_step": round(cold_wall / args.steps * 1e3, 4),
+                       "kernel_ms_mean": round(statistics.fmean(cold_durs), 4)},
     }
     if not args.no_mfma_probe:
         # the same kernel time against what this GPU's matrix cores sustain (data-sheet peak: 2516.6 at 2.4 GHz)
@@ -1002,16 +1014,17 @@ def main():
         for name, ow in ai.WORKLOADS.items():
             if name == w.name or ow.dtype != "bf16":
                 continue
-            _, od = time_workload(ow, steps=20, warmup=3)
+            _, od = time_workload(ow, steps=20, warmup=3, settle_s=args.settle)
             om = statistics.fmean(od)
             others[name] = {"kernel_ms_mean": round(om, 4), "tflops": round(ow.flops / (om * 1e-3) / 1e12, 2),
                             "pct_of_peak": round(100 * ow.flops / (om * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
         line["other_workloads"] = others
     if not args.no_backward:
-        line["backward"] = [backward_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in BWD_WORKLOADS]
-        line["fp8"] = [fp8_record(ai.WORKLOADS[n], steps=20, warmup=3) for n in FP8_WORKLOADS]
-        line["varlen"] = [varlen_record(vw, steps=20, warmup=3) for vw in ai.VARLEN_WORKLOADS.values()]
-        line["varlen_backward"] = [varlen_backward_record(vw, steps=10, warmup=2)
+        st = args.settle
+        line["backward"] = [backward_record(ai.WORKLOADS[n], steps=20, warmup=3, settle_s=st) for n in BWD_WORKLOADS]
+        line["fp8"] = [fp8_record(ai.WORKLOADS[n], steps=20, warmup=3, settle_s=st) for n in FP8_WORKLOADS]
+        line["varlen"] = [varlen_record(vw, steps=20, warmup=3, settle_s=st) for vw in ai.VARLEN_WORKLOADS.values()]
+        line["varlen_backward"] = [varlen_backward_record(vw, steps=10, warmup=2, settle_s=st)
                                    for vw in ai.VARLEN_WORKLOADS.values()]
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_rows)
