@@ -36,6 +36,7 @@ import csv
 import glob
 import hashlib
 import json
+import re
 import os
 import statistics
 import sys
@@ -542,6 +543,24 @@ def summarize(d: str):
     print(json.dumps(out, indent=1))
 
 
+def _timed_avg_us(trace_dir, name, cmd):
+    """Mean duration (us) of the last K dispatches of kernel `name` in a --kernel-trace run of `cmd` (K = its
+    --steps): the leg's timed steps, which follow its settle phase and warm-up. None without a per-dispatch trace."""
+    m = re.search(r"--steps (\d+)", cmd)
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not m or not files:
+        return None
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Kernel_Name"] == name]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    tail = rows[-int(m.group(1)):]
+    if not tail:
+        return None
+    return statistics.fmean((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tail)
+
+
 def _stats(d):
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
@@ -579,7 +598,8 @@ def write_profiles(w):
     if not trace:
         raise RuntimeError("no kernel statistics for the attention kernel")
     t = trace[0]
-    avg_us = float(t["AverageNs"]) / 1e3
+    avg_all = float(t["AverageNs"]) / 1e3
+    avg_us = _timed_avg_us(dirs["trace"], t["Name"], PROFILE_COMMANDS["trace"]) or avg_all
     fetch, write = _counters(dirs["fetch"]), _counters(dirs["write"])
     copy = "neg_kernel"
     copy_read_kib = _pick(fetch, "FETCH_SIZE", copy)
@@ -617,11 +637,14 @@ Commands (run from the repository root; outputs under gpurun_out/, summarised by
 
 ## Kernel trace (--kernel-trace --stats)
 
-| kernel | calls | avg us | min us | max us |
-|---|---|---|---|---|
-| {t['Name'][:90]} | {t['Calls']} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
+| kernel | calls | avg us, all calls | avg us, timed steps | min us | max us |
+|---|---|---|---|---|---|
+| {t['Name'][:90]} | {t['Calls']} | {avg_all:.1f} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
 
-Attention TFLOP/s at the traced average: {w.flops / (avg_us * 1e-6) / 1e12:.1f}
+"Timed steps": the last --steps dispatches of the run, after its settle phase and warm-up (what bench.py's HIP-event
+mean covers); the figures below use that average.
+
+Attention TFLOP/s at the timed-step average: {w.flops / (avg_us * 1e-6) / 1e12:.1f}
 ({100 * w.flops / (avg_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
 
 ## HBM traffic (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
@@ -634,7 +657,7 @@ FETCH_SIZE reads {copy_read_kib:.1f} KiB (scale {f_fetch:.4f}), WRITE_SIZE reads
 | read | {k_read / f_fetch / 1024:.1f} | {k_read:.0f} | {(w.B * w.H * w.N + 2 * w.kv_rows) * w.d * w.elt_bytes} (q, k, v) |
 | write | {k_write / f_write / 1024:.1f} | {k_write:.0f} | {w.B * w.H * w.N * (w.d * w.elt_bytes + 4)} (o, lse) |
 
-HBM bandwidth at the traced average: {(k_read + k_write) / (avg_us * 1e-6) / 1e9:.0f} GB/s.
+HBM bandwidth at the timed-step average: {(k_read + k_write) / (avg_us * 1e-6) / 1e9:.0f} GB/s.
 
 ## Matrix cores and LDS (SQ counters, per dispatch)
 
@@ -650,9 +673,9 @@ HBM bandwidth at the traced average: {(k_read + k_write) / (avg_us * 1e-6) / 1e9
 | SQ_WAVE_CYCLES | {_pick(sq, 'SQ_WAVE_CYCLES', kname):.4g} |
 | GRBM_GUI_ACTIVE | {gui:.4g} |
 
-MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (traced average x 2.4 GHz) = {100 * util:.1f} %;
+MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (timed-step average x 2.4 GHz) = {100 * util:.1f} %;
 over GRBM_GUI_ACTIVE / 8 (the GPU cycles counted during the kernel, summed over the 8 XCDs) = {100 * mfma_busy / n_simd / (gui / 8):.1f} %.
-Clock during the kernel, GRBM_GUI_ACTIVE / 8 / traced average: {gui / 8 / (avg_us * 1e-6) / 1e9:.2f} GHz.{
+Clock during the kernel, GRBM_GUI_ACTIVE / 8 / timed-step average: {gui / 8 / (avg_us * 1e-6) / 1e9:.2f} GHz.{
     "" if gui / 8 / (avg_us * 1e-6) <= 2.45e9 else " Above the 2.4 GHz maximum: for a launch this short GRBM_GUI_ACTIVE"
     " counts more than the kernel's own cycles (the counter run's dispatch and drain), so the shares over"
     " GRBM_GUI_ACTIVE and over SIMD-cycles below understate it; the 2.4 GHz-based utilisation is the one to read."}
@@ -712,7 +735,8 @@ def write_profiles_fp8(w):
     if not trace:
         raise RuntimeError("no kernel statistics for the fp8 attention kernel")
     t = trace[0]
-    avg_us = float(t["AverageNs"]) / 1e3
+    avg_all = float(t["AverageNs"]) / 1e3
+    avg_us = _timed_avg_us(dirs["trace"], t["Name"], FP8_PROFILE_COMMANDS["trace"]) or avg_all
     fetch, write, sq = _counters(dirs["fetch"]), _counters(dirs["write"]), _counters(dirs["sq"])
     known_kib = 2 * (1 << 28) / 1024
     copy_read_kib = _pick(fetch, "FETCH_SIZE", "neg_kernel")
@@ -751,11 +775,14 @@ Commands (run from the repository root; outputs under gpurun_out/, summarised by
 
 ## Kernel trace (--kernel-trace --stats)
 
-| kernel | calls | avg us | min us | max us |
-|---|---|---|---|---|
-| {t['Name'][:90]} | {t['Calls']} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
+| kernel | calls | avg us, all calls | avg us, timed steps | min us | max us |
+|---|---|---|---|---|---|
+| {t['Name'][:90]} | {t['Calls']} | {avg_all:.1f} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
 
-Attention TFLOP/s at the traced average: {tf:.1f} ({100 * tf / PEAK_FP8_TFLOPS:.1f} % of {PEAK_FP8_TFLOPS} dense fp8,
+"Timed steps": the last --steps dispatches of the run, after its settle phase and warm-up (what bench.py's HIP-event
+mean covers); the figures below use that average.
+
+Attention TFLOP/s at the timed-step average: {tf:.1f} ({100 * tf / PEAK_FP8_TFLOPS:.1f} % of {PEAK_FP8_TFLOPS} dense fp8,
 {100 * tf / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
 
 ## HBM traffic (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
@@ -781,7 +808,7 @@ FETCH_SIZE reads {copy_read_kib:.1f} KiB (scale {f_fetch:.4f}), WRITE_SIZE reads
 | SQ_WAVE_CYCLES | {_pick(sq, 'SQ_WAVE_CYCLES', kname):.4g} |
 | GRBM_GUI_ACTIVE | {gui:.4g} |
 
-MFMA busy = busy cycles / 1024 SIMDs over the traced average at 2.4 GHz: {100 * busy / n_simd / (avg_us * 1e-6 * 2.4e9):.1f} %;
+MFMA busy = busy cycles / 1024 SIMDs over the timed-step average at 2.4 GHz: {100 * busy / n_simd / (avg_us * 1e-6 * 2.4e9):.1f} %;
 over GRBM_GUI_ACTIVE / 8 (the clock measured during the kernel): {100 * busy / n_simd / (gui / 8):.1f} %.
 LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active, 1):.1f} %.
 """
@@ -795,7 +822,8 @@ def write_profiles_varlen(w):
     if not trace:
         raise RuntimeError("no kernel statistics for the attention kernel")
     t = trace[0]
-    avg_us = float(t["AverageNs"]) / 1e3
+    avg_all = float(t["AverageNs"]) / 1e3
+    avg_us = _timed_avg_us(f"gpurun_out/prof_{w.name}_trace", t["Name"], VARLEN_PROFILE_COMMAND) or avg_all
     tf = w.flops / (avg_us * 1e-6) / 1e12
     md = f"""# rocprofv3 summary: fa_fwd_varlen on {w.name}
 
@@ -808,11 +836,14 @@ Command (run from the repository root; summarised by `python bench.py --write-pr
 
     {VARLEN_PROFILE_COMMAND.format(w=w.name)}
 
-| kernel | calls | avg us | min us | max us |
-|---|---|---|---|---|
-| {t['Name'][:100]} | {t['Calls']} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
+| kernel | calls | avg us, all calls | avg us, timed steps | min us | max us |
+|---|---|---|---|---|---|
+| {t['Name'][:100]} | {t['Calls']} | {avg_all:.1f} | {avg_us:.1f} | {float(t['MinNs']) / 1e3:.1f} | {float(t['MaxNs']) / 1e3:.1f} |
 
-Attention TFLOP/s at the traced average: {tf:.1f} ({100 * tf / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
+"Timed steps": the last --steps dispatches of the run, after its settle phase and warm-up (what bench.py's HIP-event
+mean covers); the figures below use that average.
+
+Attention TFLOP/s at the timed-step average: {tf:.1f} ({100 * tf / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
 """
     PROFILES.mkdir(exist_ok=True)
     (PROFILES / f"{w.name}_rocprof.md").write_text(md)
@@ -837,7 +868,8 @@ def write_profiles_bwd(w):
             continue
         if not t:
             raise RuntimeError(f"no kernel statistics for {kname}")
-        avg_us = float(t[0]["AverageNs"]) / 1e3
+        avg_us = (_timed_avg_us(dirs["trace"], t[0]["Name"], BWD_PROFILE_COMMANDS["trace"])
+                  or float(t[0]["AverageNs"]) / 1e3)
         total_us += avg_us
         busy = _pick(sq, "SQ_VALU_MFMA_BUSY_CYCLES", kname)
         gui = _pick(sq, "GRBM_GUI_ACTIVE", kname)
@@ -876,11 +908,11 @@ Commands (run from the repository root; outputs under gpurun_out/, summarised by
 |---|---|---|---|---|---|---|---|---|---|
 {table}
 
-Gradient call at the traced averages: {total_us:.1f} us, {flops / (total_us * 1e-6) / 1e12:.1f} TFLOP/s
+Gradient call at the timed-step averages: {total_us:.1f} us, {flops / (total_us * 1e-6) / 1e12:.1f} TFLOP/s
 ({100 * flops / (total_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f} % of {PEAK_BF16_TFLOPS} dense bf16).
 Algorithmic HBM bytes per call: read {alg_read} (q, o, dout, lse, k, v), write {alg_write} (dq, dk, dv).
 FETCH_SIZE x {f_fetch:.4f} and WRITE_SIZE x {f_write:.4f} (calibrated on a copy of 2^28 bf16).
-MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over the traced average at 2.4 GHz, and over GRBM_GUI_ACTIVE / 8
+MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over the timed-step average at 2.4 GHz, and over GRBM_GUI_ACTIVE / 8
 (the clock actually measured during the kernel).
 """
     PROFILES.mkdir(exist_ok=True)
