@@ -73,9 +73,9 @@ PROFILE_COMMANDS = {
              "python bench.py --workload {w} --pmc-pass",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_{w}_write -o run -- "
              "python bench.py --workload {w} --pmc-pass",
-    "sq": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA "
-          "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv "
-          "-d gpurun_out/prof_{w}_sq -o run -- python bench.py --workload {w} --pmc-pass",
+    "sq": "rocprofv3 --kernel-trace --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
+          "SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE "
+          "--output-format csv -d gpurun_out/prof_{w}_sq -o run -- python bench.py --workload {w} --pmc-pass",
     # where the wave-cycles go: waiting, issuing, co-issue of vector instructions with busy matrix cores
     "stall": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
              "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE --output-format csv "
@@ -600,6 +600,7 @@ def write_profiles(w):
     t = trace[0]
     avg_all = float(t["AverageNs"]) / 1e3
     avg_us = _timed_avg_us(dirs["trace"], t["Name"], PROFILE_COMMANDS["trace"]) or avg_all
+    sq_us = _timed_avg_us(dirs["sq"], t["Name"], "--steps 1000000") or avg_us  # every dispatch of the counter run
     fetch, write = _counters(dirs["fetch"]), _counters(dirs["write"])
     copy = "neg_kernel"
     copy_read_kib = _pick(fetch, "FETCH_SIZE", copy)
@@ -675,8 +676,9 @@ HBM bandwidth at the timed-step average: {(k_read + k_write) / (avg_us * 1e-6) /
 
 MFMA utilisation = MFMA busy cycles / 1024 SIMDs / (timed-step average x 2.4 GHz) = {100 * util:.1f} %;
 over GRBM_GUI_ACTIVE / 8 (the GPU cycles counted during the kernel, summed over the 8 XCDs) = {100 * mfma_busy / n_simd / (gui / 8):.1f} %.
-Clock during the kernel, GRBM_GUI_ACTIVE / 8 / timed-step average: {gui / 8 / (avg_us * 1e-6) / 1e9:.2f} GHz.{
-    "" if gui / 8 / (avg_us * 1e-6) <= 2.45e9 else " Above the 2.4 GHz maximum: for a launch this short GRBM_GUI_ACTIVE"
+Clock during the kernel in the counter run, GRBM_GUI_ACTIVE / 8 / that run's kernel time ({sq_us:.1f} us; the
+counter runs launch each dispatch on its own, after a pause, so this is not the settled clock): {gui / 8 / (sq_us * 1e-6) / 1e9:.2f} GHz.{
+    "" if gui / 8 / (sq_us * 1e-6) <= 2.45e9 else " Above the 2.4 GHz maximum: for a launch this short GRBM_GUI_ACTIVE"
     " counts more than the kernel's own cycles (the counter run's dispatch and drain), so the shares over"
     " GRBM_GUI_ACTIVE and over SIMD-cycles below understate it; the 2.4 GHz-based utilisation is the one to read."}
 LDS bank-conflict cycles / LDS active cycles = {100 * conflict / max(lds_active, 1):.1f} %.
