@@ -383,6 +383,38 @@ def varlen_backward_record(w, steps: int, warmup: int, settle_s: float = 0.0):
             "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}
 
 
+ISSUE_MIX_MODES = ("8 MFMA", "8 MFMA + 8 exp2 (same wave)", "8 MFMA + 8 exp2 + 24 FMA (same wave)",
+                   "waves 0-3: 8 MFMA; waves 4-7: 8 exp2 + 24 FMA", "8 exp2 + 24 FMA")
+
+
+def issue_mix_probe(n_wg: int = 256, iters: int = 2048):
+    """libfa_probe.so's issue-mix probe (include/fa_probe.h): per mode, the mean shader cycles per loop iteration
+    of waves 0-3 and of waves 4-7 (the two waves of each SIMD), and the matrix cores' busy share per SIMD implied
+    by the products issued (32 cycles per v_mfma_f32_32x32x16_bf16)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(str(ROOT / "exact_attention_13_amd" / "libfa_probe.so"))
+    g = lib.fa_probe_issue_mix
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    sink = torch.empty((n_wg * lib.fa_probe_issue_mix_threads(),), dtype=torch.float32, device="cuda")
+    cyc = torch.zeros((8 * n_wg,), dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream()
+    out = []
+    for mode, name in enumerate(ISSUE_MIX_MODES):
+        for _ in range(2):  # the second run is the one read
+            if g(mode, sink.data_ptr(), cyc.data_ptr(), n_wg, iters, st.cuda_stream) != 0:
+                raise RuntimeError("fa_probe_issue_mix failed")
+        torch.cuda.synchronize()
+        c = cyc.view(n_wg, 8).double()
+        lo, hi = float(c[:, :4].mean()) / iters, float(c[:, 4:].mean()) / iters
+        mfma_per_simd = {0: 16, 1: 16, 2: 16, 3: 8, 4: 0}[mode]  # products per iteration on a SIMD's two waves
+        out.append({"mode": mode, "what": name, "cycles_per_iter_waves_0_3": round(lo, 1),
+                    "cycles_per_iter_waves_4_7": round(hi, 1),
+                    "matrix_busy": round(32 * mfma_per_simd / max(lo, hi), 3)})
+    return out
+
+
 def mfma_probe(n_wg: int = 2048, iters: int = 2048, reps: int = 5):
     """The dense bf16 rate the matrix cores of this GPU sustain, and the shader clock meanwhile
     (libfa_probe.so, include/fa_probe.h: v_mfma_f32_32x32x16_bf16 back to back on random register operands)."""
@@ -948,6 +980,8 @@ def main():
     ap.add_argument("--write-profiles-varlen", metavar="WORKLOAD", choices=sorted(ai.VARLEN_WORKLOADS))
     ap.add_argument("--write-profiles-fp8", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="matrix cores against exp2/FMA work, in one wave or split over a SIMD's two waves")
     ap.add_argument("--clock-settle", action="store_true",
                     help="per-launch times of --workload after 2 s idle (300 launches, twice)")
     ap.add_argument("--settle", type=float, default=SETTLE_S, metavar="SECONDS",
@@ -997,6 +1031,10 @@ def main():
         return 0
     if args.fp8_pmc_pass:
         fp8_pmc_pass(w, reps=5)
+        return 0
+    if args.issue_probe:
+        for rec in issue_mix_probe():
+            print(json.dumps(rec), flush=True)
         return 0
     if args.clock_settle:
         for rec in clock_settle(w):

@@ -68,9 +68,77 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
+// Issue-mix probe: 8-wave workgroups (waves w and w + 4 share a SIMD), one per CU when launched 256 wide. Per loop
+// iteration a wave issues, by mode:
+//   0: 8 MFMAs (8 independent accumulators)
+//   1: 8 MFMAs and 8 exp2
+//   2: 8 MFMAs, 8 exp2 and 24 FMAs (the softmax's ratio of exponentials and other vector work to products)
+//   3: waves 0-3 the 8 MFMAs of mode 0, waves 4-7 the 8 exp2 and 24 FMAs of mode 2 (one role per wave of a SIMD)
+//   4: 8 exp2 and 24 FMAs
+// The exp2 and FMA chains are independent of the products; each wave records its shader cycles over the loop.
+constexpr int kMixThreads = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(kMixThreads) void issue_mix_kernel(float* __restrict__ sink,
+                                                                unsigned long long* __restrict__ cyc, int iters) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const uint32_t seed = (uint32_t)(blockIdx.x * kMixThreads + tid) * 64u;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)unit_random(seed + e);
+    b[e] = (__bf16)unit_random(seed + 31u + e);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = (f32x16){};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.5f + 0.25f * unit_random(seed + 97u + i);
+  const bool mfma = MODE <= 2 || (MODE == 3 && wave < 4);
+  const bool expo = MODE == 1 || MODE == 2 || MODE == 4 || (MODE == 3 && wave >= 4);
+  const bool fma = MODE == 2 || MODE == 4 || (MODE == 3 && wave >= 4);
+  __syncthreads();
+  const unsigned long long t0 = __builtin_readcyclecounter();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (mfma) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+      if (expo) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+      if (fma) {
+        x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
+        x[i] = __builtin_fmaf(x[i], 0.998f, 0.002f);
+        x[i] = __builtin_fmaf(x[i], 0.997f, 0.003f);
+      }
+    }
+  }
+  const unsigned long long t1 = __builtin_readcyclecounter();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i] + acc[i][0] + acc[i][15];
+  sink[blockIdx.x * kMixThreads + tid] = s;
+  if ((tid & 63) == 0) cyc[blockIdx.x * (kMixThreads / 64) + wave] = t1 - t0;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_probe_issue_mix(int mode, float* sink, unsigned long long* cyc, int n_wg, int iters, hipStream_t stream) {
+  if (!sink || !cyc) return 1;
+  if (mode < 0 || mode > 4 || n_wg < 1 || n_wg > (1 << 20) || iters < 1) return 2;
+  const dim3 grid((unsigned)n_wg), block(kMixThreads);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(issue_mix_kernel<0>, grid, block, 0, stream, sink, cyc, iters); break;
+    case 1: hipLaunchKernelGGL(issue_mix_kernel<1>, grid, block, 0, stream, sink, cyc, iters); break;
+    case 2: hipLaunchKernelGGL(issue_mix_kernel<2>, grid, block, 0, stream, sink, cyc, iters); break;
+    case 3: hipLaunchKernelGGL(issue_mix_kernel<3>, grid, block, 0, stream, sink, cyc, iters); break;
+    default: hipLaunchKernelGGL(issue_mix_kernel<4>, grid, block, 0, stream, sink, cyc, iters); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int fa_probe_issue_mix_threads(void) { return kMixThreads; }
 
 int fa_probe_mfma_bf16(float* sink, unsigned long long* clk, int n_wg, int iters, hipStream_t stream) {
   if (!sink || !clk) return 1;

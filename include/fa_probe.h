@@ -33,6 +33,21 @@ double fa_probe_flop_per_wg_iter(void);
 /* Threads per workgroup of the probe (the sink holds one float per thread). */
 int fa_probe_threads(void);
 
+/* Issue-mix probe: can the matrix cores run while the vector ALU computes exponentials? 8-wave workgroups
+ * (waves w and w+4 share a SIMD; launch 256 of them for one per CU); per loop iteration each wave issues
+ *   mode 0: 8 MFMAs;  1: 8 MFMAs + 8 exp2;  2: 8 MFMAs + 8 exp2 + 24 FMAs (all in the same wave);
+ *   mode 3: waves 0-3 8 MFMAs, waves 4-7 8 exp2 + 24 FMAs (one role per wave of a SIMD);  4: 8 exp2 + 24 FMAs,
+ * the vector chains independent of the products.
+ *   sink : device float[n_wg * fa_probe_issue_mix_threads()] (written; keeps the results live)
+ *   cyc  : device unsigned long long[8 * n_wg] (written: shader cycles over the loop, per wave)
+ *   n_wg : workgroups, 1 .. 2^20;  iters : loop iterations, >= 1
+ * Returns 0 once enqueued; 1 if a pointer is NULL, 2 if mode, n_wg or iters is out of range, 3 if the launch
+ * failed. Cycles per iteration = cyc / iters. */
+int fa_probe_issue_mix(int mode, float* sink, unsigned long long* cyc, int n_wg, int iters, hipStream_t stream);
+
+/* Threads per workgroup of the issue-mix probe. */
+int fa_probe_issue_mix_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,3 +39,26 @@ def test_probe_runs_and_reads_a_plausible_clock():
     assert 0.3 < ghz < 3.0, ghz
     tflops = n_wg * iters * lib.fa_probe_flop_per_wg_iter() / (a.elapsed_time(b) * 1e-3) / 1e12
     assert math.isfinite(tflops) and 0 < tflops < 2516.6 * 3.0 / 2.4, tflops
+
+
+def test_issue_mix_probe_runs_every_mode():
+    """The issue-mix probe (matrix cores against exponentials and FMAs, in the same wave or in the two waves of a
+    SIMD): every mode runs, every wave records a positive cycle count, and the results are finite."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib = ctypes.CDLL(str(LIB))
+    g = lib.fa_probe_issue_mix
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n_wg, iters = 256, 64
+    sink = torch.full((n_wg * lib.fa_probe_issue_mix_threads(),), float("nan"), dtype=torch.float32, device="cuda")
+    cyc = torch.zeros((8 * n_wg,), dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream()
+    for mode in range(5):
+        print(f"[probe] issue mix mode={mode} n_wg={n_wg} iters={iters}", flush=True)
+        sink.fill_(float("nan"))
+        cyc.zero_()
+        assert g(mode, sink.data_ptr(), cyc.data_ptr(), n_wg, iters, st.cuda_stream) == 0
+        torch.cuda.synchronize()
+        assert torch.isfinite(sink).all()
+        assert (cyc > 0).all()
