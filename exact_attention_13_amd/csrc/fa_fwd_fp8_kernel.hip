@@ -186,6 +186,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
           }
           s[2 * t + b] = acc;
         }
+      {
+        // Issue order (scheduling groups: 0x100 LDS read, 0x008 MFMA): the fragments of four products first, then
+        // each product followed by the reads of the fragment four products ahead.
+        constexpr int kN = 2 * KT * kKS;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kN < 4 ? kN : 4), 0);
+#pragma unroll
+        for (int i = 0; i + 4 < kN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kN < 4 ? kN : 4, 0);
+      }
       const int kv0 = j * kBcT;
       if ((kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
         // key kv0 + 32h + o (o = 64t + 16b + r) is visible iff key < N and (causal) key <= my_q, i.e. iff o <= lim
