@@ -214,17 +214,13 @@ def _time_calls(call, stream, steps: int, warmup: int, settle_s: float = 0.0):
     return wall, [a.elapsed_time(b) for a, b in zip(starts, ends)]
 
 
-def time_region(w, steps: int, warmup: int, settle_s: float):
-    """The headline leg. After the settle phase, `steps` calls timed one by one with HIP events (their spread:
-    median, min, p90), then `warmup` untimed calls, then the timed region: `steps` calls back to back with one HIP
-    event pair around them on the launch stream and a device synchronisation on both sides. Events between the
-    launches cost the region ≈ 5 µs of wall time per call on C3 (0.2487 against 0.2424 ms per step), so the region
-    has none. Returns (wall_s of the region, its event time in ms, the per-call durations of the first pass)."""
+def _time_region_calls(call, stream, steps: int, warmup: int, settle_s: float):
+    """The settle phase, `steps` calls timed one by one with HIP events (their spread), `warmup` untimed calls, then
+    the timed region: `steps` calls back to back with one HIP event pair around them on `stream` and a device
+    synchronisation on both sides. Returns (wall_s of the region, its event time / steps in ms, the per-call
+    durations of the first pass)."""
     import torch
 
-    q, k, v, o, lse, lens = _device_inputs(w)
-    stream = torch.cuda.current_stream()
-    call = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
     _, per_call = _time_calls(call, stream, steps, 0, settle_s)
     for _ in range(warmup):
         call()
@@ -237,9 +233,23 @@ def time_region(w, steps: int, warmup: int, settle_s: float):
     b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    region_ms = a.elapsed_time(b)
+    return wall, a.elapsed_time(b) / steps, per_call
+
+
+def time_region(w, steps: int, warmup: int, settle_s: float):
+    """The headline leg. After the settle phase, `steps` calls timed one by one with HIP events (their spread:
+    median, min, p90), then `warmup` untimed calls, then the timed region: `steps` calls back to back with one HIP
+    event pair around them on the launch stream and a device synchronisation on both sides. Events between the
+    launches cost the region ≈ 5 µs of wall time per call on C3 (0.2487 against 0.2424 ms per step), so the region
+    has none. Returns (wall_s of the region, its event time in ms, the per-call durations of the first pass)."""
+    import torch
+
+    q, k, v, o, lse, lens = _device_inputs(w)
+    stream = torch.cuda.current_stream()
+    call = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
+    wall, mean_ms, per_call = _time_region_calls(call, stream, steps, warmup, settle_s)
     del q, k, v, o, lse, lens
-    return wall, region_ms, per_call
+    return wall, mean_ms * steps, per_call
 
 
 def clock_settle(w, launches: int = 300, idle_s: float = 2.0, trials: int = 2):
@@ -261,21 +271,27 @@ def clock_settle(w, launches: int = 300, idle_s: float = 2.0, trials: int = 2):
     return out
 
 
-def time_workload(w, steps: int, warmup: int, settle_s: float = 0.0):
-    """Returns (wall_s for `steps` calls, per-launch durations in ms from HIP events on the launch stream)."""
+def time_workload(w, steps: int, warmup: int, settle_s: float = 0.0, region: bool = True):
+    """Returns (wall_s for `steps` calls, mean launch duration in ms, per-launch durations in ms), from HIP events on
+    the launch stream: with `region`, the mean over a timed region of back-to-back calls (_time_region_calls),
+    otherwise the mean of calls timed one by one."""
     import torch
 
     q, k, v, o, lse, lens = _device_inputs(w)
     stream = torch.cuda.current_stream()
     call = _caller(w, q, k, v, o, lse, lens, stream.cuda_stream)
-    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
+    if region:
+        wall, mean, durs = _time_region_calls(call, stream, steps, warmup, settle_s)
+    else:
+        wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
+        mean = statistics.fmean(durs)
     del q, k, v, o, lse, lens
-    return wall, durs
+    return wall, mean, durs
 
 
-def time_backward(w, steps: int, warmup: int, settle_s: float = 0.0):
-    """Gradient call of workload w (bf16): (wall_s for `steps` calls, per-call durations in ms from HIP events).
-    The forward runs once first to provide o and lse; dout is seeded N(0, 1)."""
+def time_backward(w, steps: int, warmup: int, settle_s: float = 0.0, region: bool = True):
+    """Gradient call of workload w (bf16): (wall_s for `steps` calls, mean call duration in ms, per-call durations in
+    ms), from HIP events as time_workload. The forward runs once first to provide o and lse; dout is seeded N(0, 1)."""
     import torch
 
     import exact_attention_13_amd as fa
@@ -297,15 +313,18 @@ def time_backward(w, steps: int, warmup: int, settle_s: float = 0.0):
         rc = entry(*args)
         if rc != 0:
             raise RuntimeError(f"fa_bwd failed: {fa.fa_strerror(rc)}")
-    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
+    if region:
+        wall, mean, durs = _time_region_calls(call, stream, steps, warmup, settle_s)
+    else:
+        wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
+        mean = statistics.fmean(durs)
     del q, k, v, o, lse, dout, dq, dk, dv, ws
-    return wall, durs
+    return wall, mean, durs
 
 
 def backward_record(w, steps: int, warmup: int, settle_s: float = 0.0):
-    wall, durs = time_backward(w, steps, warmup, settle_s)
+    wall, mean, durs = time_backward(w, steps, warmup, settle_s)
     flops = 2.5 * w.flops
-    mean = statistics.fmean(durs)
     return {"workload": w.name, "tflops": round(flops * steps / wall / 1e12, 2),
             "pct_of_peak": round(100 * flops * steps / wall / 1e12 / PEAK_BF16_TFLOPS, 2),
             "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
@@ -336,8 +355,7 @@ def fp8_record(w, steps: int, warmup: int, settle_s: float = 0.0):
         rc = fa.fa_fwd_fp8(*args)
         if rc != 0:
             raise RuntimeError(f"fa_fwd_fp8 failed: {fa.fa_strerror(rc)}")
-    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
-    mean = statistics.fmean(durs)
+    wall, mean, durs = _time_region_calls(call, stream, steps, warmup, settle_s)
     return {"workload": w.name.replace("_bf16_", "_fp8_"), "dtype": "fp8 e4m3 (bf16 o)",
             "tflops": round(w.flops * steps / wall / 1e12, 2),
             "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
@@ -369,8 +387,7 @@ def varlen_record(w, steps: int, warmup: int, settle_s: float = 0.0):
         rc = fa.fa_fwd_varlen(*args)
         if rc != 0:
             raise RuntimeError(f"fa_fwd_varlen failed: {fa.fa_strerror(rc)}")
-    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
-    mean = statistics.fmean(durs)
+    wall, mean, durs = _time_region_calls(call, stream, steps, warmup, settle_s)
     return {"workload": w.name, "lens": list(w.lens), "H": w.H, "H_kv": w.Hk, "d": w.d, "causal": w.causal,
             "tflops": round(w.flops * steps / wall / 1e12, 2),
             "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
@@ -405,8 +422,7 @@ def varlen_backward_record(w, steps: int, warmup: int, settle_s: float = 0.0):
         rc = fa.fa_bwd_varlen(*args)
         if rc != 0:
             raise RuntimeError(f"fa_bwd_varlen failed: {fa.fa_strerror(rc)}")
-    wall, durs = _time_calls(call, stream, steps, warmup, settle_s)
-    mean = statistics.fmean(durs)
+    wall, mean, durs = _time_region_calls(call, stream, steps, warmup, settle_s)
     flops = 2.5 * w.flops
     return {"workload": w.name, "call": "fa_bwd_varlen", "tflops": round(flops * steps / wall / 1e12, 2),
             "kernel_ms": {"mean": round(mean, 4), "median": round(statistics.median(durs), 4),
@@ -559,7 +575,7 @@ def _copy_kernel_pass(reps: int) -> int:
 def bwd_pmc_pass(w, reps: int):
     """Kernels for the rocprofv3 counter runs of the gradient call: the copy, then fa_bwd."""
     n = _copy_kernel_pass(reps)
-    time_backward(w, steps=reps, warmup=0)
+    time_backward(w, steps=reps, warmup=0, region=False)
     print(json.dumps({"bwd_pmc_pass": w.name, "copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "reps": reps,
                       "kernel_src_sha256_16": kernel_src_hash(BWD_SRCS)}), flush=True)
 
@@ -1084,7 +1100,7 @@ def main():
     # `--settle` seconds of untimed back-to-back calls (time_region: K calls between events for their spread, W
     # warm-up calls, then the K timed calls with one event pair around them), which gives `value` and the
     # roofline's average launch duration: the throughput of a GPU kept busy.
-    cold_wall, cold_durs = time_workload(w, args.steps, args.warmup)
+    cold_wall, _, cold_durs = time_workload(w, args.steps, args.warmup, region=False)
     wall, region_ms, durs = time_region(w, args.steps, args.warmup, args.settle)
     ms_step = wall / args.steps * 1e3
     value = w.flops * args.steps / wall / 1e12
@@ -1124,8 +1140,7 @@ def main():
         for name, ow in ai.WORKLOADS.items():
             if name == w.name or ow.dtype != "bf16":
                 continue
-            _, od = time_workload(ow, steps=20, warmup=3, settle_s=args.settle)
-            om = statistics.fmean(od)
+            _, om, _ = time_workload(ow, steps=20, warmup=3, settle_s=args.settle)
             others[name] = {"kernel_ms_mean": round(om, 4), "tflops": round(ow.flops / (om * 1e-3) / 1e12, 2),
                             "pct_of_peak": round(100 * ow.flops / (om * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
         line["other_workloads"] = others
