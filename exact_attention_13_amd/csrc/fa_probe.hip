@@ -78,10 +78,28 @@ __global__ __launch_bounds__(kProbeThreads) __attribute__((amdgpu_waves_per_eu(2
 // The exp2 and FMA chains are independent of the products; each wave records its shader cycles over the loop.
 constexpr int kMixThreads = 512;
 
+// One wave's loop: per iteration 8 products (MF), 8 exp2 (EX) and 24 FMAs (FM), each set compiled in or out.
+template <bool MF, bool EX, bool FM>
+__device__ __forceinline__ void mix_loop(f32x16 (&acc)[8], float (&x)[8], bf16x8 a, bf16x8 b, int iters) {
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (MF) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+      if constexpr (EX) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+      if constexpr (FM) {
+        x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
+        x[i] = __builtin_fmaf(x[i], 0.998f, 0.002f);
+        x[i] = __builtin_fmaf(x[i], 0.997f, 0.003f);
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kMixThreads) void issue_mix_kernel(float* __restrict__ sink,
                                                                 unsigned long long* __restrict__ cyc, int iters) {
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: a role is a whole loop
   const uint32_t seed = (uint32_t)(blockIdx.x * kMixThreads + tid) * 64u;
   bf16x8 a, b;
 #pragma unroll
@@ -95,23 +113,19 @@ __global__ __launch_bounds__(kMixThreads) void issue_mix_kernel(float* __restric
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = 0.5f + 0.25f * unit_random(seed + 97u + i);
-  const bool mfma = MODE <= 2 || (MODE == 3 && wave < 4);
-  const bool expo = MODE == 1 || MODE == 2 || MODE == 4 || (MODE == 3 && wave >= 4);
-  const bool fma = MODE == 2 || MODE == 4 || (MODE == 3 && wave >= 4);
   __syncthreads();
   const unsigned long long t0 = __builtin_readcyclecounter();
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (mfma) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
-      if (expo) x[i] = __builtin_amdgcn_exp2f(-x[i]);
-      if (fma) {
-        x[i] = __builtin_fmaf(x[i], 0.999f, 0.001f);
-        x[i] = __builtin_fmaf(x[i], 0.998f, 0.002f);
-        x[i] = __builtin_fmaf(x[i], 0.997f, 0.003f);
-      }
+  if constexpr (MODE == 0) mix_loop<true, false, false>(acc, x, a, b, iters);
+  if constexpr (MODE == 1) mix_loop<true, true, false>(acc, x, a, b, iters);
+  if constexpr (MODE == 2) mix_loop<true, true, true>(acc, x, a, b, iters);
+  if constexpr (MODE == 3) {
+    if (wave < 4) {
+      mix_loop<true, false, false>(acc, x, a, b, iters);
+    } else {
+      mix_loop<false, true, true>(acc, x, a, b, iters);
     }
   }
+  if constexpr (MODE == 4) mix_loop<false, true, true>(acc, x, a, b, iters);
   const unsigned long long t1 = __builtin_readcyclecounter();
   float s = 0.f;
 #pragma unroll
