@@ -1005,6 +1005,40 @@ MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over the timed-step average at 
     print(md)
 
 
+def headline_line(w, steps: int, warmup: int, settle_s: float, wall: float, region_ms: float, durs, cold_wall: float,
+                  cold_durs) -> dict:
+    """The headline JSON line from the timed region (wall seconds and the event time of `steps` back-to-back calls),
+    the per-call durations of the pass before it, and the cold leg; the legs added later (probe, other workloads,
+    gradients, fp8, packed batches, CPU baseline) extend it."""
+    ms_step = wall / steps * 1e3
+    value = w.flops * steps / wall / 1e12
+    k_mean = region_ms / steps  # average launch duration over the timed region (HIP events, launch stream)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = w.flops / (k_mean * 1e-3) / 1e12
+    return {
+        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (B,H,N,d,causal)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q, k, v; no dataset)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hk, "N": w.N, "d": w.d, "causal": w.causal,
+                   "kv_len": list(w.kv_len) or None, "scale": w.scale, "input_dtype": w.dtype,
+                   "accumulate": "fp32"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "kernel_ms": {"mean": round(k_mean, 4), "per_call_mean": round(statistics.fmean(durs), 4),
+                      "median": round(statistics.median(durs), 4), "min": round(min(durs), 4),
+                      "p90": round(sorted(durs)[int(0.9 * (len(durs) - 1))], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w),
+                     "kernel": kernel_name(w), "flops_per_launch": w.flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+        "kernel_src_sha256_16": kernel_src_hash(),
+        "settle_s": settle_s,
+        "cold_start": {"value": round(w.flops * steps / cold_wall / 1e12, 2),
+                       "ms_per_step": round(cold_wall / steps * 1e3, 4),
+                       "kernel_ms_mean": round(statistics.fmean(cold_durs), 4)},
+    }
+
+
 def main():
     import attn_inputs as ai
 
@@ -1102,34 +1136,8 @@ def main():
     # roofline's average launch duration: the throughput of a GPU kept busy.
     cold_wall, _, cold_durs = time_workload(w, args.steps, args.warmup, region=False)
     wall, region_ms, durs = time_region(w, args.steps, args.warmup, args.settle)
-    ms_step = wall / args.steps * 1e3
-    value = w.flops * args.steps / wall / 1e12
-    k_mean = region_ms / args.steps  # average launch duration over the timed region (HIP events, launch stream)
-    k_med = statistics.median(durs)
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = w.flops / (k_mean * 1e-3) / 1e12
-    line = {
-        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (B,H,N,d,causal)",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q, k, v; no dataset)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.Hk, "N": w.N, "d": w.d, "causal": w.causal,
-                   "kv_len": list(w.kv_len) or None, "scale": w.scale, "input_dtype": w.dtype,
-                   "accumulate": "fp32"},
-        "pct_of_peak": round(100 * value / peak, 2),
-        "kernel_ms": {"mean": round(k_mean, 4), "per_call_mean": round(statistics.fmean(durs), 4),
-                      "median": round(k_med, 4), "min": round(min(durs), 4),
-                      "p90": round(sorted(durs)[int(0.9 * (len(durs) - 1))], 4)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w),
-                     "kernel": kernel_name(w), "flops_per_launch": w.flops,
-                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
-        "kernel_src_sha256_16": kernel_src_hash(),
-        "settle_s": args.settle,
-        "cold_start": {"value": round(w.flops * args.steps / cold_wall / 1e12, 2),
-                       "ms_per_step": round(cold_wall / args.steps * 1e3, 4),
-                       "kernel_ms_mean": round(statistics.fmean(cold_durs), 4)},
-    }
+    line = headline_line(w, args.steps, args.warmup, args.settle, wall, region_ms, durs, cold_wall, cold_durs)
+    achieved = w.flops / (region_ms / args.steps * 1e-3) / 1e12
     if not args.no_mfma_probe:
         # the same kernel time against what this GPU's matrix cores sustain (data-sheet peak: 2516.6 at 2.4 GHz)
         probe = mfma_probe()

@@ -39,3 +39,40 @@ def test_timed_step_average_reads_the_last_dispatches_of_the_kernel(tmp_path):
     assert bench._timed_avg_us(str(d), "C", "python bench.py --steps 2") is None
     assert bench._timed_avg_us(str(d), "A", "python bench.py") is None  # no --steps in the command
     assert bench._timed_avg_us(str(tmp_path / "missing"), "A", "python bench.py --steps 2") is None
+
+
+def test_headline_line_keeps_the_json_contract():
+    """The headline line from synthetic timings: every key the driver reads, with the throughput, the per-step time
+    and the roofline fraction computed from the timed region (not from the per-call events), all JSON-serialisable."""
+    import json
+    import math
+
+    sys.path.insert(0, str(ROOT))
+    import bench
+    import attn_inputs as ai
+
+    w = ai.WORKLOADS[bench.HEADLINE]
+    steps, warmup = 40, 5
+    k_ms = 0.25                                      # average launch duration over the timed region
+    wall = steps * 0.26e-3                           # seconds for the K timed steps, host clock
+    durs = [0.27] * (steps - 1) + [0.40]             # per-call events of the pass before the region
+    line = bench.headline_line(w, steps, warmup, 0.3, wall, k_ms * steps, durs, 2 * wall, [0.5] * warmup)
+    json.dumps(line)
+    for key, typ in [("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int),
+                     ("warmup", int), ("ms_per_step", float), ("higher_is_better", bool), ("scaling", str),
+                     ("dtype", str), ("data", str), ("config", dict), ("roofline", dict)]:
+        assert isinstance(line[key], typ), key
+    assert line["vs_baseline"] is None
+    assert (line["n_gpus"], line["steps"], line["warmup"], line["higher_is_better"]) == (1, steps, warmup, True)
+    assert line["config"]["workload"] == w.name and "model" not in line["config"]
+    assert line["dtype"] == "bf16" and line["unit"] == "TFLOP/s"
+    assert line["ms_per_step"] == pytest.approx(0.26, abs=1e-4)
+    assert line["value"] == pytest.approx(w.flops / 0.26e-3 / 1e12, abs=0.01)
+    r = line["roofline"]
+    assert {"bound", "achieved", "peak", "unit", "frac", "traffic"} <= set(r)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == bench.PEAK_BF16_TFLOPS
+    assert r["achieved"] == pytest.approx(w.flops / (k_ms * 1e-3) / 1e12, abs=0.01)
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
+    assert r["traffic"] is None or (math.isfinite(r["traffic"]) and r["traffic"] >= w.algorithmic_bytes)
+    assert line["kernel_ms"]["mean"] == pytest.approx(k_ms) and line["kernel_ms"]["per_call_mean"] > k_ms
+    assert line["cold_start"]["ms_per_step"] == pytest.approx(0.52, abs=1e-4)
