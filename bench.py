@@ -466,6 +466,59 @@ def issue_mix_probe(n_wg: int = 256, iters: int = 2048):
     return out
 
 
+ATOMIC_MODES = ("fp32 atomic add, tiles reached from any XCD", "fp32 atomic add, each tile from one XCD only",
+                "fp32 atomic add, 32 workgroups on one tile at once", "plain stores, tiles as in mode 0")
+
+
+def dq_partial_bytes(w) -> int:
+    """fp32 bytes a single gradient pass with atomic dq updates would add into dq for workload w: one 128 x d block
+    per (128-key block, 128-row query tile) pair that the mask leaves work in, for every query head."""
+    nb = -(-w.N // 128)
+    pairs = nb * (nb + 1) // 2 if w.causal else nb * nb
+    return w.B * w.H * pairs * 128 * w.d * 4
+
+
+def atomic_add_probe(n_wg: int = 2048, rounds: int = 8, tiles: int = 1024, reps: int = 10):
+    """libfa_probe.so's atomic-add probe (include/fa_probe.h): GB/s of fp32 atomic adds into device memory in
+    64 KiB tiles, per placement, against plain stores; each atomic mode's sum is checked. Then the time the dq
+    partial blocks of the C3 and C4 shapes would take at the measured atomic rate."""
+    import ctypes
+    import torch
+
+    import attn_inputs as ai
+    lib = ctypes.CDLL(str(ROOT / "exact_attention_13_amd" / "libfa_probe.so"))
+    g = lib.fa_probe_atomic_add
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    tf = lib.fa_probe_atomic_tile_floats()
+    buf = torch.zeros((tiles * tf,), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    nbytes = n_wg * rounds * tf * 4
+    out = []
+    for mode, what in enumerate(ATOMIC_MODES):
+        buf.zero_()
+        for _ in range(2):
+            if g(mode, buf.data_ptr(), tiles, n_wg, rounds, st.cuda_stream) != 0:
+                raise RuntimeError("fa_probe_atomic_add failed")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            g(mode, buf.data_ptr(), tiles, n_wg, rounds, st.cuda_stream)
+        b.record(st)
+        b.synchronize()
+        ms = a.elapsed_time(b) / reps
+        total = float(buf.double().sum())
+        want = float(tiles * tf) if mode == 3 else float((2 + reps) * n_wg * rounds * tf)
+        out.append({"mode": mode, "what": what, "bytes_per_launch": nbytes, "ms": round(ms, 4),
+                    "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "sum_exact": total == want})
+    rate = out[0]["GBps"] * 1e9
+    for name in ("c3_bf16_b2h16n4096d128", "c4_bf16_b1h32n16384d128_causal"):
+        nb = dq_partial_bytes(ai.WORKLOADS[name])
+        out.append({"workload": name, "dq_partial_bytes": nb,
+                    "atomic_ms_at_mode0_rate": round(nb / rate * 1e3, 3)})
+    return out
+
+
 def mfma_probe(n_wg: int = 2048, iters: int = 2048, reps: int = 5):
     """The dense bf16 rate the matrix cores of this GPU sustain, and the shader clock meanwhile
     (libfa_probe.so, include/fa_probe.h: v_mfma_f32_32x32x16_bf16 back to back on random register operands)."""
@@ -1067,6 +1120,8 @@ def main():
     ap.add_argument("--no-mfma-probe", action="store_true")
     ap.add_argument("--issue-probe", action="store_true",
                     help="matrix cores against exp2/FMA work, in one wave or split over a SIMD's two waves")
+    ap.add_argument("--atomic-probe", action="store_true",
+                    help="fp32 atomic-add rate into device memory (64 KiB tiles) against plain stores")
     ap.add_argument("--clock-settle", action="store_true",
                     help="per-launch times of --workload after 2 s idle (300 launches, twice)")
     ap.add_argument("--settle", type=float, default=SETTLE_S, metavar="SECONDS",
@@ -1119,6 +1174,10 @@ def main():
         return 0
     if args.issue_probe:
         for rec in issue_mix_probe():
+            print(json.dumps(rec), flush=True)
+        return 0
+    if args.atomic_probe:
+        for rec in atomic_add_probe():
             print(json.dumps(rec), flush=True)
         return 0
     if args.clock_settle:

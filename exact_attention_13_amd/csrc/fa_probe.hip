@@ -134,6 +134,42 @@ __global__ __launch_bounds__(kMixThreads) void issue_mix_kernel(float* __restric
   if ((tid & 63) == 0) cyc[blockIdx.x * (kMixThreads / 64) + wave] = t1 - t0;
 }
 
+// Atomic-add probe: the rate of fp32 atomic adds (global_atomic_add_f32, no return) into device memory, in 64 KiB
+// tiles of 16384 floats, the size of a 128 x 128 fp32 block. 8-wave workgroups; per round a workgroup adds 1.0 to
+// every float of one tile, each lane 32 floats 512 apart (coalesced). The tile a workgroup takes in round r:
+//   0: (7 wg + r) mod T                          distinct tiles in a round, each reached from any XCD
+//   1: (wg mod 8) + 8 ((wg / 8 + r) mod (T/8))   tile t only from workgroups wg = t (mod 8), which the dispatcher
+//                                                places on one XCD (workgroups go round-robin over the 8 XCDs)
+//   2: (wg / 32 + r) mod T                       32 consecutive workgroups (every XCD) on the same tile at once
+//   3: as 0, plain stores of 1.0 instead of atomic adds (the write rate to compare with)
+constexpr int kAtomThreads = 512;
+constexpr int kAtomTileFloats = 16384;
+
+template <int MODE>
+__global__ __launch_bounds__(kAtomThreads) void atomic_add_probe_kernel(float* __restrict__ buf, int tiles,
+                                                                        int rounds) {
+  const int wg = blockIdx.x, tid = threadIdx.x;
+  for (int r = 0; r < rounds; ++r) {
+    int tile;
+    if constexpr (MODE == 1) {
+      tile = (wg & 7) + 8 * ((wg / 8 + r) % (tiles / 8));
+    } else if constexpr (MODE == 2) {
+      tile = (wg / 32 + r) % tiles;
+    } else {
+      tile = (int)(((long long)wg * 7 + r) % tiles);
+    }
+    float* p = buf + (size_t)tile * kAtomTileFloats + tid;
+#pragma unroll
+    for (int i = 0; i < kAtomTileFloats / kAtomThreads; ++i) {
+      if constexpr (MODE == 3) {
+        p[i * kAtomThreads] = 1.0f;
+      } else {
+        unsafeAtomicAdd(p + i * kAtomThreads, 1.0f);  // hardware fp32 add on device memory
+      }
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,5 +203,22 @@ double fa_probe_flop_per_wg_iter(void) {
 }
 
 int fa_probe_threads(void) { return kProbeThreads; }
+
+int fa_probe_atomic_add(int mode, float* buf, int tiles, int n_wg, int rounds, hipStream_t stream) {
+  if (!buf) return 1;
+  if (mode < 0 || mode > 3 || tiles < 8 || tiles % 8 != 0 || tiles > (1 << 16) || n_wg < 1 || n_wg > (1 << 20) ||
+      rounds < 1)
+    return 2;
+  const dim3 grid((unsigned)n_wg), block(kAtomThreads);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(atomic_add_probe_kernel<0>, grid, block, 0, stream, buf, tiles, rounds); break;
+    case 1: hipLaunchKernelGGL(atomic_add_probe_kernel<1>, grid, block, 0, stream, buf, tiles, rounds); break;
+    case 2: hipLaunchKernelGGL(atomic_add_probe_kernel<2>, grid, block, 0, stream, buf, tiles, rounds); break;
+    default: hipLaunchKernelGGL(atomic_add_probe_kernel<3>, grid, block, 0, stream, buf, tiles, rounds); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int fa_probe_atomic_tile_floats(void) { return kAtomTileFloats; }
 
 }  // extern "C"

@@ -48,6 +48,23 @@ int fa_probe_issue_mix(int mode, float* sink, unsigned long long* cyc, int n_wg,
 /* Threads per workgroup of the issue-mix probe. */
 int fa_probe_issue_mix_threads(void);
 
+/* Atomic-add probe: how fast fp32 atomic adds into device memory run, for a kernel that would sum 128 x 128 fp32
+ * partial blocks from many workgroups into one buffer. 512-thread workgroups; per round each adds 1.0 to every
+ * float of one 64 KiB tile (fa_probe_atomic_tile_floats() floats), coalesced, without return. The tile of
+ * workgroup wg in round r, by mode:
+ *   0: (7 wg + r) mod tiles, any XCD;  1: only workgroups wg = t (mod 8) touch tile t (one XCD per tile, the
+ *   dispatcher placing workgroups round-robin over the 8 XCDs);  2: 32 consecutive workgroups on one tile at once;
+ *   3: as 0 with plain stores of 1.0 (the write rate to compare with).
+ *   buf    : device float[tiles * fa_probe_atomic_tile_floats()], caller-allocated; modes 0-2 add to it (clear it
+ *            first to check the sum: n_wg * rounds * fa_probe_atomic_tile_floats() per launch), mode 3 sets it to 1
+ *   tiles  : 8 .. 65536, a multiple of 8;  n_wg : workgroups, 1 .. 2^20;  rounds : tiles per workgroup, >= 1
+ * Returns 0 once enqueued; 1 if buf is NULL, 2 if an argument is out of range, 3 if the launch failed.
+ * Bytes per launch = n_wg * rounds * 4 * fa_probe_atomic_tile_floats(). */
+int fa_probe_atomic_add(int mode, float* buf, int tiles, int n_wg, int rounds, hipStream_t stream);
+
+/* Floats per tile of the atomic-add probe (16384). */
+int fa_probe_atomic_tile_floats(void);
+
 #ifdef __cplusplus
 }
 #endif

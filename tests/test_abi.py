@@ -39,8 +39,8 @@ def test_probe_library_exports_what_its_header_declares():
     header = HEADER.parent / "fa_probe.h"
     declared = sorted(set(re.findall(r"^(?:const\s+)?\w+\s*\**\s*(fa_probe_\w+)\s*\(", header.read_text(),
                                      flags=re.M)))
-    assert declared == ["fa_probe_flop_per_wg_iter", "fa_probe_issue_mix", "fa_probe_issue_mix_threads",
-                        "fa_probe_mfma_bf16", "fa_probe_threads"]
+    assert declared == ["fa_probe_atomic_add", "fa_probe_atomic_tile_floats", "fa_probe_flop_per_wg_iter",
+                        "fa_probe_issue_mix", "fa_probe_issue_mix_threads", "fa_probe_mfma_bf16", "fa_probe_threads"]
     path = Path(fa.library_path()).parent / "libfa_probe.so"
     out = subprocess.run(["nm", "-D", "--defined-only", str(path)], capture_output=True, text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
@@ -59,6 +59,13 @@ def test_probe_library_exports_what_its_header_declares():
     assert g(0, None, A, 1, 1, None) == 1 and g(0, A, None, 1, 1, None) == 1
     assert g(-1, A, B_, 1, 1, None) == 2 and g(5, A, B_, 1, 1, None) == 2
     assert g(0, A, B_, 0, 1, None) == 2 and g(0, A, B_, 1, 0, None) == 2
+    assert lib.fa_probe_atomic_tile_floats() == 16384
+    h = lib.fa_probe_atomic_add
+    h.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert h(0, None, 8, 1, 1, None) == 1
+    assert h(-1, A, 8, 1, 1, None) == 2 and h(4, A, 8, 1, 1, None) == 2
+    assert h(1, A, 0, 1, 1, None) == 2 and h(1, A, 12, 1, 1, None) == 2 and h(1, A, 1 << 17, 1, 1, None) == 2
+    assert h(0, A, 8, 0, 1, None) == 2 and h(0, A, 8, 1, 0, None) == 2
 
 
 def test_version_and_strerror():

@@ -62,3 +62,31 @@ def test_issue_mix_probe_runs_every_mode():
         torch.cuda.synchronize()
         assert torch.isfinite(sink).all()
         assert (cyc > 0).all()
+
+
+def test_atomic_add_probe_sums_exactly_in_every_mode():
+    """The atomic-add probe: in each atomic placement every add lands (the buffer sums to the adds issued, exact in
+    fp32 at these counts), and the store mode writes every float of the tiles it reaches."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib = ctypes.CDLL(str(LIB))
+    h = lib.fa_probe_atomic_add
+    h.restype = ctypes.c_int
+    h.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    tf = lib.fa_probe_atomic_tile_floats()
+    tiles, n_wg, rounds = 64, 96, 3
+    buf = torch.zeros((tiles * tf,), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    for mode in range(4):
+        print(f"[probe] atomic add mode={mode} tiles={tiles} n_wg={n_wg} rounds={rounds}", flush=True)
+        buf.fill_(-1.0 if mode == 3 else 0.0)
+        assert h(mode, buf.data_ptr(), tiles, n_wg, rounds, st.cuda_stream) == 0
+        torch.cuda.synchronize()
+        per_tile = buf.view(tiles, tf)
+        if mode == 3:
+            # tiles (7 wg + r) mod 64 for wg < 96, r < 3 cover every residue: all set to 1
+            assert (per_tile == 1.0).all()
+        else:
+            assert float(buf.double().sum()) == n_wg * rounds * tf
+            # within a tile every float received the same number of adds
+            assert (per_tile == per_tile[:, :1]).all()
