@@ -112,7 +112,9 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
   using T = BwdTile<D>;
   constexpr int NW = kDqWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  // 2 K stages, then 2 V stages (64 KiB at d = 128). Static rather than dynamic, so that its address is known when
+  // instructions are selected and the stage offsets fold into the reads' immediate offsets.
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * T::kBytes];
   lds_char* const kst = (lds_char*)smem_raw;  // 2 K stages
   lds_char* const vst = kst + 2 * T::kBytes;  // 2 V stages
 
@@ -196,9 +198,10 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
   auto copy_tile = [&](const __bf16* src, lds_char* dst, int j) __attribute__((always_inline)) {
     const int row0 = j * kBwdTile;
     // rows past Nk arrive as zeros: the range ends with the last valid row (only tiles below Nk are copied, so
-    // Nk >= 1 here); scalar byte count and base keep the descriptor in scalar registers
-    const int rows = max(0, min(Nk - row0, kBwdTile));
-    const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * kpitch_b + T::RB : 0);
+    // Nk >= 1 here); scalar byte count and base keep the descriptor in scalar registers (readfirstlane between
+    // the min and the max keeps the pair from fusing into v_med3_i32, a vector instruction)
+    const int rows = max(0, __builtin_amdgcn_readfirstlane(min(Nk - row0, kBwdTile)));
+    const int bytes = rows > 0 ? (rows - 1) * kpitch_b + T::RB : 0;
     const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Nk - 1));
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * kpitch, bytes);
 #pragma unroll
@@ -364,7 +367,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int NW = kDkdvWaves, kDB = D / 16, kCB = D / 32, kCopies = T::kInsts / NW;
   constexpr int kSub = kDkdvTile / kBwdRows;  // 32-row sub-blocks per query tile
   static_assert(T::kInsts % NW == 0, "tile copy must split evenly over the waves");
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  // 146 KiB at d = 128; static, as in the dq kernel, so that stage offsets fold into the reads
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * (2 * T::kBytes + kWsTileBytes) + 8 * kPSlotBytes];
   lds_char* const qst = (lds_char*)smem_raw;       // 2 q stages
   lds_char* const dst = qst + 2 * T::kBytes;       // 2 dO stages
   lds_char* const wst = dst + 2 * T::kBytes;       // 2 workspace stages
@@ -444,7 +448,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) __attribute__((amdgpu_waves_per_eu
     const int row0 = (t0 + it % per_head) * kDkdvTile;
     // first element of row 0 of query head hq
     const size_t base = VARLEN ? ((size_t)start * H + hq % H) * D : (size_t)hq * N * D;
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(Ns - row0, kDkdvTile)));
+    const int rows = max(0, __builtin_amdgcn_readfirstlane(min(Ns - row0, kDkdvTile)));  // scalar, no v_med3_i32
     const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Ns - 1));
     const int bytes = rows > 0 ? (rows - 1) * qpitch_b + T::RB : 0;  // ends with the sequence's last row
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base + (size_t)row_base * qpitch, bytes);
@@ -668,24 +672,18 @@ static hipError_t launch_bwd(const void* q, const void* k, const void* v, const 
                              int N, float scale, const int* kv_len, hipStream_t stream,
                              const int* cu_seqlens = nullptr, int T_total = 0) {
   const int group = H / Hkv;
-  constexpr int lds_a = 4 * BwdTile<D>::kBytes;
-  constexpr int lds_b = 2 * (2 * BwdTile<D, kDkdvTile>::kBytes + kWsTileBytes) + 8 * kPSlotBytes;
-  auto ka = fa_bwd_dq_kernel<D, CAUSAL, VARLEN>;
+  auto ka = fa_bwd_dq_kernel<D, CAUSAL, VARLEN>;  // both kernels allocate their LDS statically
   auto kb = fa_bwd_dkdv_kernel<D, CAUSAL, VARLEN>;
-  hipError_t e = hipFuncSetAttribute((const void*)ka, hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)kb, hipFuncAttributeMaxDynamicSharedMemorySize, lds_b);
-  if (e != hipSuccess) return e;
   const unsigned nblk = (unsigned)((N + kBwdBlock - 1) / kBwdBlock);
   const unsigned nblk_dq = (unsigned)((N + kDqBlock - 1) / kDqBlock);
-  hipLaunchKernelGGL(ka, dim3(nblk_dq, (unsigned)(B * H)), dim3(64 * kDqWaves), lds_a, stream, (const __bf16*)q,
+  hipLaunchKernelGGL(ka, dim3(nblk_dq, (unsigned)(B * H)), dim3(64 * kDqWaves), 0, stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse, (const __bf16*)dout, (__bf16*)dq, ws,
                      N, B * H, scale, group, H, kv_len, cu_seqlens, T_total);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nsplit = bwd_head_split(B, H, Hkv, N);
   float* part = nsplit > 1 ? (float*)((char*)ws + bwd_planes_bytes(B, H, N)) : nullptr;
-  hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv * nsplit)), dim3(64 * kDkdvWaves), lds_b, stream,
+  hipLaunchKernelGGL(kb, dim3(nblk, (unsigned)(B * Hkv * nsplit)), dim3(64 * kDkdvWaves), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, (const float*)ws,
                      (__bf16*)dk, (__bf16*)dv, N, B * Hkv, scale, group, Hkv, kv_len, cu_seqlens, T_total, part,
                      nsplit);

@@ -73,7 +73,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int kBcT = KT * kF8Part;
   constexpr int kStage = KT * T::kBytes;
   static_assert(kTileInsts % NW == 0, "tile copy must split evenly over the waves");
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  // 2 K stages, then 2 V^T stages (at most 64 KiB). Static rather than dynamic: its address is then known when
+  // instructions are selected, so the stage and part offsets fold into the reads' immediate offsets instead of
+  // costing a vector add per fragment address and tile.
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * kStage];
   lds_char* const kst = (lds_char*)smem_raw;  // 2 K stages
   lds_char* const vst = kst + 2 * kStage;     // 2 V^T stages
 
@@ -163,8 +166,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) oacc[cb] = (f32x16){};
   f32x16 lacc = (f32x16){};  // every value: sum of the rounded weights of this lane's query row
-  const i32x8 ones = (i32x8){0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                             0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // e4m3 1.0 in every byte, made opaque so that it stays in VGPRs instead of being rebuilt from SGPRs every tile
+  i32x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int w = 0x38383838;
+    asm volatile("" : "+v"(w));
+    ones[i] = w;
+  }
 
   auto step = [&](int j, int S) __attribute__((always_inline)) {
     const bool issue = j + 1 < n_tiles;
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int i = 0; i < 2 * KT; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[i][r]);
+        for (int r = (i == 0); r < 16; ++r) mx = row_max(mx, s[i][r]);
       mx = pair_max32(mx);
       const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c2 > kF8Rescale);
       if (__any(grow)) {
@@ -284,12 +293,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 template <int D, bool CAUSAL, int NW, int KT>
 static hipError_t launch_fp8(const void* q, const void* k, const void* vt, void* o, float* lse, int BH, int N,
                              float c2, float v_scale, hipStream_t stream) {
-  constexpr int lds = 2 * 2 * KT * F8Tile<D>::kBytes;
   auto kern = fa_fwd_fp8_kernel<D, CAUSAL, NW, KT>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((N + NW * kF8Rows - 1) / (NW * kF8Rows)), (unsigned)BH);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, (const uint8_t*)q, (const uint8_t*)k,
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), 0, stream, (const uint8_t*)q, (const uint8_t*)k,
                      (const uint8_t*)vt, (__bf16*)o, lse, N, BH, c2, v_scale);
   return hipGetLastError();
 }

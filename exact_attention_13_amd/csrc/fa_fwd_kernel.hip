@@ -215,10 +215,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int t = 0; t < KT; ++t) {
       const int row0 = j * kBcT + t * kBc;
       // rows past Nk arrive as zeros: the range ends with the last valid row (rows are kpitch_b >= RB bytes
-      // apart). (The clamp would compile to a vector instruction; readfirstlane keeps the descriptor in scalar
-      // registers, otherwise every copy is wrapped in a loop over distinct descriptors.)
-      const int rows = max(0, min(Nk - row0, kBc));
-      const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (rows - 1) * kpitch_b + T::RB : 0);
+      // apart). The descriptor must stay in scalar registers (else every copy is wrapped in a loop over distinct
+      // descriptors): readfirstlane between the min and the max keeps the pair from fusing into v_med3_i32, a
+      // vector instruction, so the whole computation is scalar.
+      const int rows = max(0, __builtin_amdgcn_readfirstlane(min(Nk - row0, kBc)));
+      const int bytes = rows > 0 ? (rows - 1) * kpitch_b + T::RB : 0;
       const int row_base = __builtin_amdgcn_readfirstlane(min(row0, Nk - 1));
       const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)row_base * kpitch, bytes);
 #pragma unroll
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int b = 0; b < 2 * kWKT; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+      for (int r = (b == 0); r < 16; ++r) mx = row_max(mx, s[b][r]);
     mx = pair_max32(mx);  // row max over this tile's keys
     const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c2 > kRescaleLog2);
     if (__any(grow)) {

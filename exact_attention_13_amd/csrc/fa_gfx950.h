@@ -24,10 +24,14 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the lower 32 lanes of its second.
 // Fed x twice, every lane ends up holding {x[l], x[l ^ 32]} across the two results, in an order that depends
+// The maximum of the row-max reductions: IEEE 754-2019 maximum (v_maximum3_f32 on gfx950), which propagates a
+// NaN where fmaxf would skip it and needs no quieting instructions before each chain (fmaxf costs two).
+__device__ __forceinline__ float row_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // on the half; max and sum of the two are therefore the pair reductions for every lane.
 __device__ __forceinline__ float pair_max32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return row_max(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
