@@ -11,7 +11,8 @@
 //   * fa_bwd_dq_kernel: one workgroup per block of 256 query rows (8 waves x 32 rows), K/V tiles of 64 keys
 //     streamed through LDS exactly like the forward. S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16
 //     put one query row in each lane, so p = exp2(s*c - lse*log2e) and dS^T = p (dP^T - D) need only the lane's
-//     own lse and D; dQ^T += K^T dS^T takes dS^T from registers as the B operand and K^T by transposing LDS reads
+//     own lse and D (the dP^T accumulators start at -D, so the products leave dP^T - D); dQ^T += K^T dS^T takes
+//     dS^T from registers as the B operand and K^T by transposing LDS reads
 //     (ds_read_b64_tr_b16). It also computes D_i from the o and dO rows it loads anyway and writes (-D_i,
 //     lse_i*log2e) to the workspace.
 //   * fa_bwd_dkdv_kernel: one workgroup per block of 128 keys of one key/value head, 8 waves: each block of 32
@@ -228,6 +229,9 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
   f32x16 acc[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) acc[cb] = (f32x16){};
+  f32x16 negD;  // -D_i in every value: the starting value of the dP^T accumulators (the lane's row is i)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negD[r] = -Di;
 
   // One 64-key tile from the stage at byte `at`. Value r of block b is key j*64 + 32b + 16(r/8) + 8h + r%8.
   auto compute = [&](int j, int at) __attribute__((always_inline)) {
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       s[b] = (f32x16){};
-      dp[b] = (f32x16){};
+      dp[b] = negD;  // the products then leave dP^T - D, with no subtraction per value
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c2, -lse2));
-        ds[e] = p * (y[e] - Di);
+        ds[e] = p * y[e];
       }
       const bf16x8 dsb = __builtin_convertvector(ds, bf16x8);
       if (m < 3) read_kt(m + 1, nxt);
