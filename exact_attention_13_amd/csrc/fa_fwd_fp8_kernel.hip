@@ -162,6 +162,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 
   float m_ref = -INFINITY;
+  // A tile whose row maximum exceeds m_grow = m_ref + kF8Rescale / c2 moves the reference. Every row sees key 0 in
+  // its first tile, so the first maximum is finite and always exceeds the starting m_grow = -inf.
+  const float grow_gap = kF8Rescale / c2;
+  float m_grow = -INFINITY;
+  float nb = 0.f;  // -m_ref * c2, the exponent offset of every weight (set with the first reference)
   f32x16 oacc[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) oacc[cb] = (f32x16){};
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int r = (i == 0); r < 16; ++r) mx = row_max(mx, s[i][r]);
       mx = pair_max32(mx);
-      const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c2 > kF8Rescale);
+      const bool grow = mx > m_grow;
       if (__any(grow)) {
         const float m_new = fmaxf(m_ref, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -234,8 +239,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) oacc[cb] *= alpha;
         m_ref = m_use;
+        m_grow = m_ref + grow_gap;
+        nb = -m_ref * c2;
       }
-      const float nb = -m_ref * c2;
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         // p of the part's 64 keys: lane half h holds keys 32h + e, e = 16b' + r, as bytes e of the B operand

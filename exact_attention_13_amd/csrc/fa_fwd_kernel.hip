@@ -266,6 +266,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float c2 = scale * kLog2e;
   float m_ref = -INFINITY;  // exponent reference (raw-score units) for row my_q
   float l_run = 0.f;        // this lane's share of the running sum (the keys it holds)
+  // A tile whose row maximum exceeds m_grow = m_ref + kRescaleLog2 / c2 moves the reference; nb = -m_ref * c2 is
+  // the exponent offset of the weights. Until a key of the row has been seen (m_ref = -inf) every finite maximum
+  // exceeds m_grow, and nb = 0 leaves the weights of a fully masked tile at exactly 0.
+  const float grow_gap = kRescaleLog2 / c2;
+  float m_grow = -INFINITY, nb = 0.f;
   f32x16 oacc[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) oacc[cb] = (f32x16){};
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int r = (b == 0); r < 16; ++r) mx = row_max(mx, s[b][r]);
     mx = pair_max32(mx);  // row max over this tile's keys
-    const bool grow = (m_ref == -INFINITY) || ((mx - m_ref) * c2 > kRescaleLog2);
+    const bool grow = mx > m_grow;
     if (__any(grow)) {
       const float m_new = fmaxf(m_ref, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no visible key yet: any finite reference
@@ -322,6 +327,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) oacc[cb] *= alpha;
       m_ref = m_use;
+      m_grow = m_ref + grow_gap;
+      nb = -m_ref * c2;
     }
   };
 
@@ -329,7 +336,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // the 8 exponentials of step m+1 can run on the vector ALU while the MFMAs of step m run, and the V fragments
   // of step m+1 are read during step m. Lane slot 8h+e of step m <-> key j*64KT + 16m + 8h + e.
   auto softmax_pv = [&](f32x16(&s)[2 * kWKT], int vat) __attribute__((always_inline)) {
-    const float nb = -m_ref * c2;
     float rs[2] = {0.f, 0.f};
     auto read_v = [&](int m, bf16x8(&vf)[kCB]) __attribute__((always_inline)) {
 #pragma unroll
