@@ -91,6 +91,18 @@ def test_fp8_large_sampled_rows(fa, B, H, N, causal):
     _bound_check(label, o, lse, q8, k8, v8, sq, sk, sv, causal, scale, rows=rows)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_extreme_scales(fa, causal):
+    """1e-20 x and 8 x the default scale: near-uniform weights, and rows with one dominant key whose exponent
+    reference moves on many tiles; every row within the derived bound."""
+    N, d = 400, 128
+    q8, k8, v8, sq, sk, sv = ai.make_qkv_fp8(2, 3, N, d, seed=690)
+    for f in (1e-20, 8.0):
+        scale = ai.default_scale(d) * f
+        o, lse = _run(fa, q8, k8, v8, sq, sk, sv, causal, scale)
+        _bound_check(f"fp8 scale x{f} causal={causal}", o, lse, q8, k8, v8, sq, sk, sv, causal, scale)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp8_zero_query_is_the_prefix_mean(fa, d):
     """q = 0: every visible score is 0, the weights are exactly 1 (no rounding), o_i = mean of v_0..v_i. Allowed:

@@ -95,6 +95,19 @@ def test_heads_not_multiple_of_8_and_other_scales(fa, causal):
         _compare(o, lse, q, k, v, causal, scale, "bf16", label=f"B3H5 scale={scale} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_extreme_scales(fa, d, causal):
+    """Scales at both ends of what the entry point accepts: 1e-38 (8 / (scale * log2 e) overflows to +inf, so the
+    exponent reference is set once and never moves) and 1e-30 (uniform weights: o is the mean of the visible
+    values), and 20 (every row one dominant key; the reference moves on many tiles). Every row against the
+    oracle; B*H = 6 puts the grid on the split shape, whose second wave sees no key of the first tile's rows."""
+    q, k, v = ai.make_qkv(2, 3, 300, d, seed=106, dtype="bf16")
+    for scale in (1e-38, 1e-30, 20.0):
+        o, lse = _run(fa, q, k, v, causal, scale)
+        _compare(o, lse, q, k, v, causal, scale, "bf16", label=f"d{d} scale={scale} causal={causal}")
+
+
 # --- closed forms on the GPU ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
