@@ -1083,7 +1083,10 @@ def headline_line(w, steps: int, warmup: int, settle_s: float, wall: float, regi
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(w),
                      "kernel": kernel_name(w), "flops_per_launch": w.flops,
-                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+                     # the memory side of the same launch: algorithmic bytes over the kernel time, against HBM
+                     "hbm_gbs": round(w.algorithmic_bytes / (k_mean * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(w.algorithmic_bytes / (k_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "kernel_src_sha256_16": kernel_src_hash(),
         "settle_s": settle_s,
         "cold_start": {"value": round(w.flops * steps / cold_wall / 1e12, 2),

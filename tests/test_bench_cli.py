@@ -75,4 +75,6 @@ def test_headline_line_keeps_the_json_contract():
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
     assert r["traffic"] is None or (math.isfinite(r["traffic"]) and r["traffic"] >= w.algorithmic_bytes)
     assert line["kernel_ms"]["mean"] == pytest.approx(k_ms) and line["kernel_ms"]["per_call_mean"] > k_ms
+    assert r["hbm_gbs"] == pytest.approx(w.algorithmic_bytes / (k_ms * 1e-3) / 1e9, abs=0.1)
+    assert r["hbm_frac"] == pytest.approx(r["hbm_gbs"] / bench.PEAK_HBM_GBS, abs=1e-4) and r["hbm_frac"] < 1
     assert line["cold_start"]["ms_per_step"] == pytest.approx(0.52, abs=1e-4)
