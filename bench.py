@@ -36,8 +36,8 @@ import csv
 import glob
 import hashlib
 import json
-import re
 import os
+import re
 import statistics
 import sys
 import time
@@ -120,10 +120,16 @@ VARLEN_PROFILE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv 
                           "python bench.py --varlen-only {w} --steps 50 --warmup 10")
 
 
+_COMMENTS = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_src_hash(srcs=KERNEL_SRCS) -> str:
+    """sha256[:16] of the kernel sources' code: comments removed and whitespace collapsed, so that a profile taken
+    on the code stays valid across edits of its comments or layout, and only across those."""
     h = hashlib.sha256()
     for f in srcs:
-        h.update(f.read_bytes())
+        h.update(" ".join(_COMMENTS.sub(" ", f.read_text()).split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 
@@ -763,7 +769,7 @@ def write_profiles(w):
     cmds = "\n".join(f"    {PROFILE_COMMANDS[k].format(w=w.name)}" for k in PROFILE_COMMANDS)
     md = f"""# rocprofv3 summary: {kernel_name(w)} on {w.name}
 
-Kernel source sha256[:16]: `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip and fa_gfx950.h).
+Kernel code sha256[:16] (comments and layout excluded): `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip and fa_gfx950.h).
 Workload: B={w.B} H={w.H} H_kv={w.Hk} N={w.N} d={w.d} causal={w.causal} {w.dtype}{f' kv_len={list(w.kv_len)}' if w.kv_len else ''};
 {w.flops:.4g} FLOP per launch (4*d*H per visible query-key pair, causal triangles counted as N^2/2),
 {w.algorithmic_bytes} algorithmic HBM bytes per launch.
@@ -900,7 +906,7 @@ def write_profiles_fp8(w):
     cmds = "\n".join(f"    {FP8_PROFILE_COMMANDS[k].format(w=w.name)}" for k in FP8_PROFILE_COMMANDS)
     md = f"""# rocprofv3 summary: fa_fwd_fp8_kernel on {w.name.replace('_bf16_', '_fp8_')}
 
-Kernel source sha256[:16]: `{kernel_src_hash(FP8_SRCS)}` (exact_attention_13_amd/csrc/fa_fwd_fp8_kernel.hip and fa_gfx950.h).
+Kernel code sha256[:16] (comments and layout excluded): `{kernel_src_hash(FP8_SRCS)}` (exact_attention_13_amd/csrc/fa_fwd_fp8_kernel.hip and fa_gfx950.h).
 Workload: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}; q, k, v quantized per tensor to float8_e4m3fn from the
 seeded bf16-shaped inputs (v passed transposed), o in bf16, lse in fp32;
 {w.flops:.4g} FLOP per launch (4*d*H per visible query-key pair, causal triangles counted as N^2/2),
@@ -965,7 +971,7 @@ def write_profiles_varlen(w):
     tf = w.flops / (avg_us * 1e-6) / 1e12
     md = f"""# rocprofv3 summary: fa_fwd_varlen on {w.name}
 
-Kernel source sha256[:16]: `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip and fa_gfx950.h).
+Kernel code sha256[:16] (comments and layout excluded): `{kernel_src_hash()}` (exact_attention_13_amd/csrc/fa_fwd_kernel.hip and fa_gfx950.h).
 Workload: {w.B} packed sequences of lengths {list(w.lens)} (total {w.T} tokens), H={w.H} H_kv={w.Hk} d={w.d}
 causal={w.causal} bf16; {w.flops:.4g} FLOP per launch (4*H*d per visible query-key pair of every sequence, causal
 triangles counted as L^2/2), {w.algorithmic_bytes} algorithmic HBM bytes per launch.
@@ -1032,7 +1038,7 @@ def write_profiles_bwd(w):
         f"{r['lds_conflict']:.4g} |" for r in rows)
     md = f"""# rocprofv3 summary: gradient call (fa_bwd) on {w.name}
 
-Kernel sources sha256[:16]: `{kernel_src_hash(BWD_SRCS)}` (exact_attention_13_amd/csrc/fa_bwd_kernel.hip and fa_gfx950.h).
+Kernel code sha256[:16] (comments and layout excluded): `{kernel_src_hash(BWD_SRCS)}` (exact_attention_13_amd/csrc/fa_bwd_kernel.hip and fa_gfx950.h).
 Workload: B={w.B} H={w.H} H_kv={w.Hk} N={w.N} d={w.d} causal={w.causal} bf16; {flops:.4g} FLOP per call in the usual
 convention (2.5 x the forward's 4*B*H*N^2*d{', halved' if w.causal else ''}: five matrix products); the kernels
 execute seven (S and dP are formed in both), {7 / 5 * flops:.4g} FLOP of MFMA work.

@@ -16,8 +16,8 @@
 //     registers (p rounded to e4m3 with v_cvt_pk_fp8_f32).
 //   * The row sum l adds the rounded weights the product used, so o is a weighted average under them: one more
 //     O^T-shaped instruction per 64 keys with an all-ones A operand gives sum_j p_j for every query lane.
-//   * o = acc * s_v / l in bf16, lse in natural log as the bf16 kernel. Lazy rescaling keeps p < 2^8, inside
-//     e4m3's range (448).
+//   * o = acc * s_v / l in bf16, lse in natural log as the bf16 kernel. Lazy rescaling keeps p at most 2^8 (up to
+//     the rounding of the threshold m_ref + 8 / c), well inside e4m3's range (448).
 #include "fa_gfx950.h"
 #include "fa_launch.h"
 

@@ -78,3 +78,20 @@ def test_headline_line_keeps_the_json_contract():
     assert r["hbm_gbs"] == pytest.approx(w.algorithmic_bytes / (k_ms * 1e-3) / 1e9, abs=0.1)
     assert r["hbm_frac"] == pytest.approx(r["hbm_gbs"] / bench.PEAK_HBM_GBS, abs=1e-4) and r["hbm_frac"] < 1
     assert line["cold_start"]["ms_per_step"] == pytest.approx(0.52, abs=1e-4)
+
+
+def test_kernel_hash_ignores_comments_and_layout_only(tmp_path):
+    """A profile's source hash covers the code: editing a comment or re-indenting keeps it, changing a token or a
+    literal does not."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    f = tmp_path / "k.hip"
+    base = "// header\nint f(int x) {  /* a\n block */ return x + 1; }  // tail\n"
+    f.write_text(base)
+    h0 = bench.kernel_src_hash([f])
+    f.write_text("// another header, two lines\n// of it\nint f(int x) {\n    return x + 1;\n}\n")
+    assert bench.kernel_src_hash([f]) == h0
+    f.write_text(base.replace("x + 1", "x + 2"))
+    assert bench.kernel_src_hash([f]) != h0
+    f.write_text(base.replace("return", "return -"))
+    assert bench.kernel_src_hash([f]) != h0
