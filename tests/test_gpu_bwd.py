@@ -86,6 +86,15 @@ def test_backward_grouped_heads(fa, Hkv, d, causal):
     _full(fa, 2, 8, Hkv, 333, d, causal, 450 + Hkv, label)
 
 
+@pytest.mark.parametrize("B,H,Hkv,causal", [(2, 6, 2, False), (2, 6, 2, True), (4, 24, 8, True)])
+def test_backward_groups_of_three(fa, B, H, Hkv, causal):
+    """dk and dv summed over groups of 3 query heads (not a power of two), on a grid whose B*H_kv is a multiple of 8
+    and on one where it is not."""
+    label = f"bwd B{B} H{H} Hkv{Hkv} N200 d128 causal={causal}"
+    print(f"[case] {label}", flush=True)
+    _full(fa, B, H, Hkv, 200, 128, causal, 460 + B + H, label)
+
+
 @pytest.mark.parametrize("H,Hkv,causal", [(16, 16, False), (16, 16, True), (16, 4, True), (16, 1, True)])
 def test_backward_large_sampled_rows(fa, H, Hkv, causal):
     """B2 N2048 d128: 192 dq rows and 192 dk/dv rows of four heads, plus the first and last rows."""

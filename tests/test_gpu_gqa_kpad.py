@@ -87,6 +87,19 @@ def test_gqa_parity_wide_grid(fa, Hkv, causal):
     _compare(o, lse, q, k, v, causal, rows=rows, label=label)
 
 
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [(2, 6, 2, 300, 64, False), (2, 6, 2, 300, 64, True),
+                                                  (1, 12, 4, 1000, 128, True), (8, 6, 2, 200, 128, False),
+                                                  (4, 24, 8, 300, 128, True)])
+def test_gqa_groups_of_three(fa, B, H, Hkv, N, d, causal):
+    """Groups that are not a power of two (3 query heads per key/value head), on grids whose B*H/group is a multiple
+    of 8 (the XCD mapping then keeps a group's query heads on one XCD) and on grids where it is not; every row."""
+    label = f"gqa B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    q, k, v = _qkv(B, H, Hkv, N, d, seed=250 + B + H + N)
+    o, lse = _run(fa, q, k, v, causal)
+    _compare(o, lse, q, k, v, causal, label=label)
+
+
 @pytest.mark.parametrize("N,H,causal", [(333, 16, True), (2048, 32, False), (2048, 32, True)])
 def test_gqa_equals_plain_forward_on_repeated_heads(fa, N, H, causal):
     """Each query head reads exactly its group's key/value head: bitwise equal to fa_fwd on repeated heads."""
