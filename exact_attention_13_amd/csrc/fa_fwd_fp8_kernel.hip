@@ -18,6 +18,8 @@
 //     O^T-shaped instruction per 64 keys with an all-ones A operand gives sum_j p_j for every query lane.
 //   * o = acc * s_v / l in bf16, lse in natural log as the bf16 kernel. Lazy rescaling keeps p at most 2^8 (up to
 //     the rounding of the threshold m_ref + 8 / c), well inside e4m3's range (448).
+#include <type_traits>
+
 #include "fa_gfx950.h"
 #include "fa_launch.h"
 
@@ -28,6 +30,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kF8Rows = 32;  // query rows per wave
 constexpr int kF8Part = 64;  // keys per LDS part (one K part and one V^T part)
 constexpr float kF8Rescale = 8.f;
+constexpr float kF8SumLimit = 256.f;  // 2^kF8Rescale
 
 // K part: 64 rows of d bytes; V^T part: d rows of 64 bytes. 16-byte chunks are XOR-swizzled so that each 16-byte
 // read (16 lanes, 16 rows, one chunk) hits 16 different bank groups. A lane's 32-byte fragment is two chunks c, c+1
@@ -170,7 +173,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   f32x16 oacc[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) oacc[cb] = (f32x16){};
-  f32x16 lacc = (f32x16){};  // every value: sum of the rounded weights of this lane's query row
+  // 8-wave workgroups test each tile's row sums of the weights before forming the row maximum (below); the tile's
+  // sum is then read by the vector ALU and added to l_run. 4-wave workgroups chain the sums on the matrix core in
+  // lacc (every value: the sum of the rounded weights of this lane's query row) and never wait for them.
+  constexpr bool kSumCheck = NW == 8;
+  float l_run = 0.f;
+  f32x16 lacc = (f32x16){};
   // e4m3 1.0 in every byte, made opaque so that it stays in VGPRs instead of being rebuilt from SGPRs every tile
   i32x8 ones;
 #pragma unroll
@@ -180,93 +188,149 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     ones[i] = w;
   }
 
-  auto step = [&](int j, int S) __attribute__((always_inline)) {
+  auto step = [&](int j, int S, auto first_c) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_c)::value;  // tile 0 (j == 0)
     const bool issue = j + 1 < n_tiles;
     if (issue) copy_tile(j + 1, (S ^ 1) * kStage);
     if (j < wave_tiles) {
       const lds_char* ks_ = kst + S * kStage;
       const lds_char* vs_ = vst + S * kStage;
-      // S^T blocks: part t, block b': value r of lane half h is key j*kBcT + 64t + 32h + 16b' + r
-      f32x16 s[2 * KT];
+      // S^T blocks: part t, block b': value r of lane half h is key j*kBcT + 64t + 32h + 16b' + r; masked scores
+      // are -inf.
+      auto products = [&](f32x16(&s)[2 * KT], bool again) __attribute__((always_inline)) {
+        // A second formation of the same scores reads its fragments through offsets the compiler cannot see
+        // through; it would otherwise reuse the first one's scores and hold them in registers across the tile.
+        int ko[2][kKS];
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          f32x16 acc = (f32x16){};
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int ks = 0; ks < kKS; ++ks) {
-            const i32x8 kf = lds_read32(ks_ + t * T::kBytes, k_off[b][ks]);
-            acc = mfma_f8(kf, qf[ks], acc);
+            ko[b][ks] = k_off[b][ks];
+            if (again) asm volatile("" : "+v"(ko[b][ks]));
           }
-          s[2 * t + b] = acc;
-        }
-      {
-        // Issue order (scheduling groups: 0x100 LDS read, 0x008 MFMA): the fragments of four products first, then
-        // each product followed by the reads of the fragment four products ahead.
-        constexpr int kN = 2 * KT * kKS;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kN < 4 ? kN : 4), 0);
-#pragma unroll
-        for (int i = 0; i + 4 < kN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kN < 4 ? kN : 4, 0);
-      }
-      const int kv0 = j * kBcT;
-      if ((kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
-        // key kv0 + 32h + o (o = 64t + 16b + r) is visible iff key < N and (causal) key <= my_q, i.e. iff o <= lim
-        const int lim = (CAUSAL ? min(N - 1, my_q) : N - 1) - kv0 - 32 * h;
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int b = 0; b < 2; ++b) {
+            f32x16 acc = (f32x16){};
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              s[2 * t + b][r] = (64 * t + 16 * b + r <= lim) ? s[2 * t + b][r] : -INFINITY;
-      }
-      float mx = s[0][0];
+            for (int ks = 0; ks < kKS; ++ks) {
+              const i32x8 kf = lds_read32(ks_ + t * T::kBytes, ko[b][ks]);
+              acc = mfma_f8(kf, qf[ks], acc);
+            }
+            s[2 * t + b] = acc;
+          }
+        {
+          // Issue order (scheduling groups: 0x100 LDS read, 0x008 MFMA): the fragments of four products first,
+          // then each product followed by the reads of the fragment four products ahead.
+          constexpr int kN = 2 * KT * kKS;
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kN < 4 ? kN : 4), 0);
 #pragma unroll
-      for (int i = 0; i < 2 * KT; ++i)
+          for (int i = 0; i + 4 < kN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kN < 4 ? kN : 4, 0);
+        }
+        const int kv0 = j * kBcT;
+        if ((kv0 + kBcT > N) || (CAUSAL && kv0 + kBcT - 1 > q0w)) {
+          // key kv0 + 32h + o (o = 64t + 16b + r) is visible iff key < N and (causal) key <= my_q, i.e. iff
+          // o <= lim
+          const int lim = (CAUSAL ? min(N - 1, my_q) : N - 1) - kv0 - 32 * h;
 #pragma unroll
-        for (int r = (i == 0); r < 16; ++r) mx = row_max(mx, s[i][r]);
-      mx = pair_max32(mx);
-      const bool grow = mx > m_grow;
-      if (__any(grow)) {
+          for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                s[2 * t + b][r] = (64 * t + 16 * b + r <= lim) ? s[2 * t + b][r] : -INFINITY;
+        }
+      };
+      // Row maximum of the tile; when some row's maximum exceeds m_grow, every row's reference moves to its
+      // maximum (O and l rescaled). Returns whether it moved.
+      auto move_reference = [&](const f32x16(&s)[2 * KT]) __attribute__((always_inline)) -> bool {
+        float mx = s[0][0];
+#pragma unroll
+        for (int i = 0; i < 2 * KT; ++i)
+#pragma unroll
+          for (int r = (i == 0); r < 16; ++r) mx = row_max(mx, s[i][r]);
+        mx = pair_max32(mx);
+        const bool grow = mx > m_grow;
+        if (!__any(grow)) return false;
         const float m_new = fmaxf(m_ref, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f((m_ref - m_use) * c2);
-        lacc *= alpha;
+        if constexpr (kSumCheck) {
+          l_run *= alpha;
+        } else {
+          lacc *= alpha;
+        }
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) oacc[cb] *= alpha;
         m_ref = m_use;
         m_grow = m_ref + grow_gap;
         nb = -m_ref * c2;
+        return true;
+      };
+      // Weights of the tile's parts against the current reference (lane half h holds keys 32h + e, e = 16b' + r,
+      // as bytes e of the B operand) and their row sum on the matrix core (an all-ones A operand): every value of
+      // `ts` is the sum for this lane's query row.
+      i32x8 pf[KT];
+      f32x16 ts;
+      auto weights = [&](const f32x16(&s)[2 * KT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const f32x16& sv = s[2 * t + (w >> 2)];
+            const int r0 = 4 * (w & 3);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0], c2, nb));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 1], c2, nb));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 2], c2, nb));
+            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 3], c2, nb));
+            // the first conversion writes the low half of the word, the second the high half; the word starts
+            // as p0's bits (any value would do), so no register has to be cleared first
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+            pf[t][w] = word;
+          }
+        ts = mfma_f8(ones, pf[0], kSumCheck ? (f32x16){} : lacc);
+#pragma unroll
+        for (int t = 1; t < KT; ++t) ts = mfma_f8(ones, pf[t], ts);
+      };
+      // The row maximum matters only when the reference may have to move, i.e. when some weight would reach 2^8
+      // (kF8Rescale). Tile 0 sets every row's first reference (each row of the wave sees key 0), so it forms the
+      // maximum first. In 8-wave workgroups later tiles take the weights against the current reference first: if
+      // every row's rounded weights sum to less than 2^8 (a NaN or saturated weight fails the test), no weight
+      // reached 2^8, no row maximum exceeded m_grow (up to the rounding of the exponent argument) and the weights
+      // stand. Otherwise the scores are formed again (K is still in LDS), the maximum decides the move as on tile
+      // 0, and the weights are taken again. (4-wave workgroups, one wave per SIMD, would wait for the sum with no
+      // other wave to fill the matrix core: they form the maximum on every tile.)
+      f32x16 s[2 * KT];
+      products(s, false);
+      if constexpr (kFirst || !kSumCheck) {
+        move_reference(s);
+        weights(s);
+      } else {
+        weights(s);
+        if (!__all(ts[0] < kF8SumLimit)) {
+          products(s, true);
+          move_reference(s);
+          weights(s);
+        }
+      }
+      if constexpr (kSumCheck) {
+        l_run += ts[0];
+      } else {
+        lacc = ts;
       }
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        // p of the part's 64 keys: lane half h holds keys 32h + e, e = 16b' + r, as bytes e of the B operand
-        i32x8 pf;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const f32x16& sv = s[2 * t + (w >> 2)];
-          const int r0 = 4 * (w & 3);
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0], c2, nb));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 1], c2, nb));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 2], c2, nb));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r0 + 3], c2, nb));
-          // the first conversion writes the low half of the word, the second the high half; the word starts as
-          // p0's bits (any value would do), so no register has to be cleared first
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-          pf[w] = word;
-        }
-        lacc = mfma_f8(ones, pf, lacc);
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int cb = 0; cb < kCB; ++cb) {
           const i32x8 vf = lds_read32(vs_ + t * T::kBytes, v_off[cb]);
-          oacc[cb] = mfma_f8(vf, pf, oacc[cb]);
+          oacc[cb] = mfma_f8(vf, pf[t], oacc[cb]);
         }
-      }
     }
     wait_copies_and_barrier<0>();
   };
@@ -274,13 +338,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     copy_tile(0, 0);
     wait_copies_and_barrier<0>();
   }
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(j, 0);
-    if (j + 1 < n_tiles) step(j + 1, 1);
+  // tile 0 on its own (it sets the first reference), then the stages alternate
+  if (n_tiles > 0) step(0, 0, std::true_type{});
+  for (int j = 1; j < n_tiles; j += 2) {
+    step(j, 1, std::false_type{});
+    if (j + 1 < n_tiles) step(j + 1, 0, std::false_type{});
   }
 
   // o = acc * s_v / l, lse = m*c/log2e + ln l (c holds scale * s_q * s_k * log2 e)
-  const float l_tot = lacc[0];
+  const float l_tot = kSumCheck ? l_run : lacc[0];
   if (my_q < N) {
     const float f = v_scale / l_tot;
     __bf16* orow = o + head_off + (size_t)my_q * D;

@@ -103,6 +103,43 @@ def test_fp8_extreme_scales(fa, causal):
         _bound_check(f"fp8 scale x{f} causal={causal}", o, lse, q8, k8, v8, sq, sk, sv, causal, scale)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_reference_steps_between_tiles_in_8_wave_workgroups(fa, causal):
+    """Scores that step up and down from one 128-key tile to the next, on a grid large enough for the 8-wave
+    workgroups (ceil(N/256) B H >= 512), which first take a tile's weights against the current exponent reference
+    and form the row maximum only when some row's weights sum to 2^8 or more. With q_i = g_i (1, ..., 1) and
+    k_j = b_t (1, ..., 1) on tile t, a row's score gap to its reference is 28 g_i (b_t - b_ref) in log2 units at the
+    scale below: for g = 1 the steps give gaps of 7 (weights 2^7: the sum test fails, the maximum does not move
+    the reference), 14 (the reference moves), 3.5 (sum test fails, no move), 0 and below (sum test passes); other
+    g scale the gaps, g < 0 reverses them. Sampled rows of every kind against the derived bound."""
+    B, H, N, d = 1, 64, 2048, 128
+    steps = [1.0, 1.25, 1.5, 1.5, 1.625, 1.0, 2.0, 2.0, 2.5, 2.5, 2.25, 2.5, 1.5, 2.5, 2.5, 2.5]
+    gains = [1.0, 0.5, -1.0, 0.75]
+    kb = torch.tensor(steps, dtype=torch.float32).repeat_interleave(128)[:N]
+    k8 = kb.reshape(1, 1, N, 1).expand(B, H, N, d).contiguous().to(torch.float8_e4m3fn)
+    qg = torch.tensor(gains, dtype=torch.float32).repeat(N // len(gains))
+    q8 = qg.reshape(1, 1, N, 1).expand(B, H, N, d).contiguous().to(torch.float8_e4m3fn)
+    _, _, v8, _, _, sv = ai.make_qkv_fp8(B, H, N, d, seed=695)
+    scale = float(np.float32(7.0 / (np.log2(np.e) * d * 0.25)))
+    label = f"fp8 stepped scores B{B} H{H} N{N} d{d} causal={causal}"
+    print(f"[case] {label}", flush=True)
+    o, lse = _run(fa, q8, k8, v8, 1.0, 1.0, sv, causal, scale)
+    tile_ends = (128 * np.arange(N // 128)[:, None] + np.arange(124, 128)[None, :]).ravel()
+    cand = np.unique(np.concatenate([ai.sample_rows(B, H, N, 96, 695), np.arange(0, 8), tile_ends,
+                                     (H - 1) * N + tile_ends]))
+    # The derived bound needs E = 2^-4 + 2^-10 n / Z well below 1: a causal row that sees only the first keys of
+    # its highest tile has one dominant weight among a thousand tiny ones (Z ~ 1) and no useful bound; such rows
+    # (chosen from the inputs alone) are left out.
+    i = cand % N
+    n = i + 1 if causal else np.full_like(i, N)
+    s_row = scale * d * np.asarray(gains)[i % 4][:, None] * np.asarray(kb)[None, :]
+    s_row = np.where(np.arange(N)[None, :] < n[:, None], s_row, -np.inf)
+    Z = np.exp(s_row - s_row.max(axis=1, keepdims=True)).sum(axis=1)
+    rows = cand[n / Z <= 128]
+    assert len(rows) >= 64, len(rows)
+    _bound_check(label, o, lse, q8, k8, v8, 1.0, 1.0, sv, causal, scale, rows=rows)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp8_zero_query_is_the_prefix_mean(fa, d):
     """q = 0: every visible score is 0, the weights are exactly 1 (no rounding), o_i = mean of v_0..v_i. Allowed:
