@@ -103,16 +103,18 @@ def test_fp8_extreme_scales(fa, causal):
         _bound_check(f"fp8 scale x{f} causal={causal}", o, lse, q8, k8, v8, sq, sk, sv, causal, scale)
 
 
+@pytest.mark.parametrize("N", [2048, 1936])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_reference_steps_between_tiles_in_8_wave_workgroups(fa, causal):
+def test_fp8_reference_steps_between_tiles_in_8_wave_workgroups(fa, causal, N):
     """Scores that step up and down from one 128-key tile to the next, on a grid large enough for the 8-wave
     workgroups (ceil(N/256) B H >= 512), which first take a tile's weights against the current exponent reference
     and form the row maximum only when some row's weights sum to 2^8 or more. With q_i = g_i (1, ..., 1) and
     k_j = b_t (1, ..., 1) on tile t, a row's score gap to its reference is 28 g_i (b_t - b_ref) in log2 units at the
     scale below: for g = 1 the steps give gaps of 7 (weights 2^7: the sum test fails, the maximum does not move
     the reference), 14 (the reference moves), 3.5 (sum test fails, no move), 0 and below (sum test passes); other
-    g scale the gaps, g < 0 reverses them. Sampled rows of every kind against the derived bound."""
-    B, H, N, d = 1, 64, 2048, 128
+    g scale the gaps, g < 0 reverses them. N = 1936 ends in a tile of 16 keys. Sampled rows of every kind against
+    the derived bound."""
+    B, H, d = 1, 64, 128
     steps = [1.0, 1.25, 1.5, 1.5, 1.625, 1.0, 2.0, 2.0, 2.5, 2.5, 2.25, 2.5, 1.5, 2.5, 2.5, 2.5]
     gains = [1.0, 0.5, -1.0, 0.75]
     kb = torch.tensor(steps, dtype=torch.float32).repeat_interleave(128)[:N]
@@ -124,7 +126,8 @@ def test_fp8_reference_steps_between_tiles_in_8_wave_workgroups(fa, causal):
     label = f"fp8 stepped scores B{B} H{H} N{N} d{d} causal={causal}"
     print(f"[case] {label}", flush=True)
     o, lse = _run(fa, q8, k8, v8, 1.0, 1.0, sv, causal, scale)
-    tile_ends = (128 * np.arange(N // 128)[:, None] + np.arange(124, 128)[None, :]).ravel()
+    tile_ends = (128 * np.arange((N + 127) // 128)[:, None] + np.arange(124, 128)[None, :]).ravel()
+    tile_ends = tile_ends[tile_ends < N]
     cand = np.unique(np.concatenate([ai.sample_rows(B, H, N, 96, 695), np.arange(0, 8), tile_ends,
                                      (H - 1) * N + tile_ends]))
     # The derived bound needs E = 2^-4 + 2^-10 n / Z well below 1: a causal row that sees only the first keys of
