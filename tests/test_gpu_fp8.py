@@ -78,9 +78,12 @@ def test_fp8_ragged(fa, N, d, causal):
     _bound_check(label, o, lse, q8, k8, v8, sq, sk, sv, causal, scale)
 
 
-@pytest.mark.parametrize("B,H,N,causal", [(2, 16, 4096, False), (1, 32, 4096, True), (1, 8, 16384, True)])
-def test_fp8_large_sampled_rows(fa, B, H, N, causal):
-    d = 128
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 16, 4096, 128, False), (1, 32, 4096, 128, True),
+                                              (1, 8, 16384, 128, True), (2, 16, 4096, 64, False),
+                                              (1, 32, 4096, 64, True), (1, 64, 2000, 64, True)])
+def test_fp8_large_sampled_rows(fa, B, H, N, d, causal):
+    """Grids of at least 512 blocks of 256 rows (ceil(N/256) B H >= 512): the 8-wave instances at d = 64 and 128,
+    one of them with an 80-key last tile."""
     label = f"fp8 B{B} H{H} N{N} d{d} causal={causal}"
     print(f"[case] {label}", flush=True)
     q8, k8, v8, sq, sk, sv = ai.make_qkv_fp8(B, H, N, d, seed=650 + H)
@@ -103,9 +106,10 @@ def test_fp8_extreme_scales(fa, causal):
         _bound_check(f"fp8 scale x{f} causal={causal}", o, lse, q8, k8, v8, sq, sk, sv, causal, scale)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [2048, 1936])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_reference_steps_between_tiles_in_8_wave_workgroups(fa, causal, N):
+def test_fp8_reference_steps_between_tiles_in_8_wave_workgroups(fa, causal, N, d):
     """Scores that step up and down from one 128-key tile to the next, on a grid large enough for the 8-wave
     workgroups (ceil(N/256) B H >= 512), which first take a tile's weights against the current exponent reference
     and form the row maximum only when some row's weights sum to 2^8 or more. With q_i = g_i (1, ..., 1) and
@@ -114,7 +118,7 @@ def test_fp8_reference_steps_between_tiles_in_8_wave_workgroups(fa, causal, N):
     the reference), 14 (the reference moves), 3.5 (sum test fails, no move), 0 and below (sum test passes); other
     g scale the gaps, g < 0 reverses them. N = 1936 ends in a tile of 16 keys. Sampled rows of every kind against
     the derived bound."""
-    B, H, d = 1, 64, 128
+    B, H = 1, 64
     steps = [1.0, 1.25, 1.5, 1.5, 1.625, 1.0, 2.0, 2.0, 2.5, 2.5, 2.25, 2.5, 1.5, 2.5, 2.5, 2.5]
     gains = [1.0, 0.5, -1.0, 0.75]
     kb = torch.tensor(steps, dtype=torch.float32).repeat_interleave(128)[:N]
