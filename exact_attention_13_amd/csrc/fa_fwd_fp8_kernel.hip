@@ -18,6 +18,9 @@
 //     O^T-shaped instruction per 64 keys with an all-ones A operand gives sum_j p_j for every query lane.
 //   * o = acc * s_v / l in bf16, lse in natural log as the bf16 kernel. Lazy rescaling keeps p at most 2^8 (up to
 //     the rounding of the threshold m_ref + 8 / c), well inside e4m3's range (448).
+//   * 8-wave workgroups take a tile's weights against the current reference first and form the row maximum only
+//     when some row's weights sum to 2^8 or more, the only case in which the reference could have to move (the
+//     tile loop below); the softmax work per key is then exponential, FMA and conversion.
 #include <type_traits>
 
 #include "fa_gfx950.h"
