@@ -147,8 +147,9 @@ def attention_varlen(q, k, v, cu_seqlens, causal: bool, scale: float, rows=None,
     """Attention of packed variable-length sequences: every sequence is its own attention problem.
 
     q: [T, H, d], k and v: [T, Hkv, d] (tokens of all sequences back to back; Hkv divides H); cu_seqlens: B+1
-    offsets, sequence b holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (the variable-length batches of the
-    survey's key-padding row, read as FlashAttention-style packing). Queries of sequence b see only the keys of
+    offsets, sequence b holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (batches of sequences of different
+    lengths, read as FlashAttention-style packing of the padded batches the key-padding mask of the
+    triton-transformer README's usage example describes). Queries of sequence b see only the keys of
     sequence b (and, when causal, only those at or before their own position in it). rows: flat ids t*H + h
     (token t, query head h), or None for all T*H in that order. Each sequence is handed to attention_rows as a
     [1, H, L, d] problem. Returns (o [n, d] float64, lse [n] float64).

@@ -1,7 +1,7 @@
 """Pins for the oracle of packed variable-length batches (oracle.attention_varlen).
 
-The survey's key-padding row also names variable-length batches with per-batch sequence lengths; the pages show
-only a boolean (batch, seq) mask in the triton-transformer README's usage example ("ex. BERT"). The reading
+Batches of sequences with different lengths: the pages show only a boolean (batch, seq) mask in the
+triton-transformer README's usage example ("ex. BERT"), i.e. padded batches. The reading
 pinned here is FlashAttention-style packing: the tokens of B sequences lie back to back ([T, H, d]), sequence b
 holds tokens cu[b] .. cu[b+1]-1, and its queries attend only to its own keys (causal: to those at or before their
 own position in the sequence). The pins: torch SDPA in fp64 on the whole packed problem with a block-diagonal
