@@ -292,7 +292,7 @@ def test_bad_rows_rejected():
         oracle.attention_rows(q, k, v, False, 0.125, rows=np.array([8]))
 
 
-# --- the page's blockwise recurrence (reading R6) -----------------------------------------------------------------
+# --- the page's blockwise recurrence, as printed and with the old sum kept -----------------------------------------
 
 def _page_blockwise(q, k, v, scale, block, keep_old_sum):
     """The recurrence of the unite.ai page's "Implementation Details" code, restated in numpy fp64 (the page's
